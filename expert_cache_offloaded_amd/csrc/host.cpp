@@ -1,0 +1,417 @@
+// Host branch of the hybrid decode: persistent worker pool + host expert FFN.
+//
+// [jjl357] "8.3 CPU 分支也被纳入捕获路径": a persistent C++ worker pool pinned to
+// cores runs SIMD expert kernels that dequantise inside the kernel instead of
+// materialising larger temporary weights.  [jjl357] "6.2": host-computed experts
+// stay in host DRAM and are run in place.  [wanger] "背景": the CPU reads the pinned
+// banks directly (no PCIe) and computes a GEMV.
+//
+// Work split: phase 1 = (expert, 16 intermediate rows) tasks computing
+// h = silu(W_gate x) * (W_up x) for every token routed to the expert; phase 2 =
+// (16 hidden rows) tasks summing w * (W_down h) over the experts in a fixed order,
+// so y does not depend on the number of threads.
+#include <immintrin.h>
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "../../include/mc.h"
+
+namespace mc {
+void set_error(const char* fmt, ...);
+void clear_error();
+}  // namespace mc
+
+// ------------------------------------------------------------------ worker pool
+
+struct mc_host_pool {
+  std::vector<std::thread> threads;
+  std::mutex mu, pf_mu;
+  std::condition_variable cv_work, cv_done;
+  // parallel-for state (one generation at a time; every worker acknowledges each)
+  const std::function<void(int)>* fn = nullptr;
+  std::atomic<int> next{0};
+  int n_tasks = 0;
+  int generation = 0;
+  int acked = 0;
+  bool stop = false;
+  // asynchronous job (hybrid branch)
+  std::thread driver;
+  std::function<void()> job;
+  bool job_pending = false, job_done = true, driver_stop = false;
+  std::condition_variable cv_job, cv_job_done;
+
+  void worker_loop() {
+    int seen = 0;
+    for (;;) {
+      const std::function<void(int)>* f;
+      int n;
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv_work.wait(lk, [&] { return stop || generation != seen; });
+        if (stop) return;
+        seen = generation;
+        f = fn;
+        n = n_tasks;
+      }
+      for (int i; (i = next.fetch_add(1)) < n;) (*f)(i);
+      {
+        std::lock_guard<std::mutex> lk(mu);
+        if (++acked == (int)threads.size()) cv_done.notify_all();
+      }
+    }
+  }
+
+  // Runs f(0..n-1) on the workers and the calling thread; returns when every task
+  // is done and every worker has left this generation.
+  void parallel_for(int n, const std::function<void(int)>& f) {
+    if (n <= 0) return;
+    if (threads.empty()) {
+      for (int i = 0; i < n; ++i) f(i);
+      return;
+    }
+    std::lock_guard<std::mutex> serial(pf_mu);
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      fn = &f;
+      n_tasks = n;
+      next.store(0);
+      acked = 0;
+      ++generation;
+    }
+    cv_work.notify_all();
+    for (int i; (i = next.fetch_add(1)) < n;) f(i);
+    std::unique_lock<std::mutex> lk(mu);
+    cv_done.wait(lk, [&] { return acked == (int)threads.size(); });
+    fn = nullptr;
+  }
+
+  void driver_loop() {
+    for (;;) {
+      std::function<void()> j;
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv_job.wait(lk, [&] { return driver_stop || job_pending; });
+        if (driver_stop) return;
+        j = std::move(job);
+        job_pending = false;
+      }
+      j();
+      {
+        std::lock_guard<std::mutex> lk(mu);
+        job_done = true;
+      }
+      cv_job_done.notify_all();
+    }
+  }
+
+  void submit(std::function<void()> j) {
+    {
+      std::unique_lock<std::mutex> lk(mu);
+      cv_job_done.wait(lk, [&] { return job_done; });
+      job = std::move(j);
+      job_pending = true;
+      job_done = false;
+    }
+    cv_job.notify_all();
+  }
+
+  void wait_job() {
+    std::unique_lock<std::mutex> lk(mu);
+    cv_job_done.wait(lk, [&] { return job_done; });
+  }
+};
+
+extern "C" mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* cpu_ids) {
+  mc::clear_error();
+  if (n_threads < 1 || n_threads > 1024) {
+    mc::set_error("mc_host_pool_create: n_threads=%d must be in [1, 1024]", n_threads);
+    return nullptr;
+  }
+  mc_host_pool* p = new (std::nothrow) mc_host_pool();
+  if (!p) {
+    mc::set_error("mc_host_pool_create: out of memory");
+    return nullptr;
+  }
+  // the calling thread takes part in parallel_for, so n_threads - 1 workers
+  for (int i = 0; i + 1 < n_threads; ++i) {
+    p->threads.emplace_back([p] { p->worker_loop(); });
+    if (cpu_ids) {
+      cpu_set_t set;
+      CPU_ZERO(&set);
+      CPU_SET(cpu_ids[i + 1], &set);
+      pthread_setaffinity_np(p->threads.back().native_handle(), sizeof set, &set);
+    }
+  }
+  p->driver = std::thread([p] { p->driver_loop(); });
+  if (cpu_ids) {
+    cpu_set_t set;
+    CPU_ZERO(&set);
+    CPU_SET(cpu_ids[0], &set);
+    pthread_setaffinity_np(p->driver.native_handle(), sizeof set, &set);
+  }
+  return p;
+}
+
+extern "C" void mc_host_pool_destroy(mc_host_pool* p) {
+  if (!p) return;
+  p->wait_job();
+  {
+    std::lock_guard<std::mutex> lk(p->mu);
+    p->stop = true;
+    p->driver_stop = true;
+  }
+  p->cv_work.notify_all();
+  p->cv_job.notify_all();
+  for (auto& t : p->threads) t.join();
+  p->driver.join();
+  delete p;
+}
+
+namespace mc {
+
+void host_pool_submit(mc_host_pool* p, std::function<void()> job) {
+  if (!p) {
+    job();
+    return;
+  }
+  p->submit(std::move(job));
+}
+
+void host_pool_wait(mc_host_pool* p) {
+  if (p) p->wait_job();
+}
+
+// ------------------------------------------------------------------ expert kernels
+
+static float g_e2m1[16];
+static bool init_table() {
+  for (int c = 0; c < 16; ++c) {
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    float mag = e == 0 ? 0.5f * m : ldexpf(1.0f + 0.5f * m, e - 1);
+    g_e2m1[c] = s ? -mag : mag;
+  }
+  return true;
+}
+static bool g_table_ok = init_table();
+
+static inline float e8m0(uint8_t X) { return ldexpf(1.0f, (int)X - 127); }
+static inline float bf16f(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// Activation vector prepared for one format: MXFP4 blocks of 32 are stored as
+// 16 even-index values followed by 16 odd-index values (matching the low/high
+// nibbles of the code bytes); bf16 rows keep natural order.
+static void prep_vec(const float* v, int n, int fmt, float* out) {
+  if (fmt == MC_MXFP4) {
+    for (int b = 0; b < n / 32; ++b)
+      for (int i = 0; i < 16; ++i) {
+        out[32 * b + i] = v[32 * b + 2 * i];
+        out[32 * b + 16 + i] = v[32 * b + 2 * i + 1];
+      }
+  } else {
+    memcpy(out, v, sizeof(float) * n);
+  }
+}
+
+static float dot_mx_scalar(const uint8_t* codes, const uint8_t* scales, const float* xp, int n) {
+  float acc = 0.0f;
+  for (int b = 0; b < n / 32; ++b) {
+    float part = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+      uint8_t byte = codes[16 * b + i];
+      part += g_e2m1[byte & 15] * xp[32 * b + i] + g_e2m1[byte >> 4] * xp[32 * b + 16 + i];
+    }
+    acc += part * e8m0(scales[b]);
+  }
+  return acc;
+}
+
+static float dot_bf_scalar(const uint16_t* wrow, const float* xp, int n) {
+  float acc = 0.0f;
+  for (int i = 0; i < n; ++i) acc += bf16f(wrow[i]) * xp[i];
+  return acc;
+}
+
+__attribute__((target("avx512f,avx512bw")))
+static float dot_mx_avx512(const uint8_t* codes, const uint8_t* scales, const float* xp, int n) {
+  const __m512 tab = _mm512_loadu_ps(g_e2m1);
+  const __m512i lo4 = _mm512_set1_epi32(15);
+  __m512 acc = _mm512_setzero_ps();
+  for (int b = 0; b < n / 32; ++b) {
+    __m512i bytes = _mm512_cvtepu8_epi32(_mm_loadu_si128((const __m128i*)(codes + 16 * b)));
+    __m512 ve = _mm512_permutexvar_ps(_mm512_and_si512(bytes, lo4), tab);
+    __m512 vo = _mm512_permutexvar_ps(_mm512_srli_epi32(bytes, 4), tab);
+    __m512 part = _mm512_mul_ps(ve, _mm512_loadu_ps(xp + 32 * b));
+    part = _mm512_fmadd_ps(vo, _mm512_loadu_ps(xp + 32 * b + 16), part);
+    acc = _mm512_fmadd_ps(part, _mm512_set1_ps(e8m0(scales[b])), acc);
+  }
+  return _mm512_reduce_add_ps(acc);
+}
+
+__attribute__((target("avx512f,avx512bw")))
+static float dot_bf_avx512(const uint16_t* wrow, const float* xp, int n) {
+  __m512 acc = _mm512_setzero_ps();
+  int i = 0;
+  for (; i + 16 <= n; i += 16) {
+    __m512i w16 = _mm512_cvtepu16_epi32(_mm256_loadu_si256((const __m256i*)(wrow + i)));
+    __m512 wf = _mm512_castsi512_ps(_mm512_slli_epi32(w16, 16));
+    acc = _mm512_fmadd_ps(wf, _mm512_loadu_ps(xp + i), acc);
+  }
+  float s = _mm512_reduce_add_ps(acc);
+  for (; i < n; ++i) s += bf16f(wrow[i]) * xp[i];
+  return s;
+}
+
+static bool g_avx512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+
+static inline float dot_row(int fmt, const uint8_t* row, const uint8_t* srow, const float* xp,
+                            int n) {
+  if (fmt == MC_MXFP4)
+    return g_avx512 ? dot_mx_avx512(row, srow, xp, n) : dot_mx_scalar(row, srow, xp, n);
+  const uint16_t* r = reinterpret_cast<const uint16_t*>(row);
+  return g_avx512 ? dot_bf_avx512(r, xp, n) : dot_bf_scalar(r, xp, n);
+}
+
+static void run_tasks(mc_host_pool* pool, int n, const std::function<void(int)>& f) {
+  if (pool)
+    pool->parallel_for(n, f);
+  else
+    for (int i = 0; i < n; ++i) f(i);
+}
+
+struct HostUnit {
+  int64_t entry;                 // host bank entry (flat id)
+  std::vector<int> toks;         // tokens routed to it
+  std::vector<float> gates;
+};
+
+int host_experts_run(mc_host_pool* pool, const uint16_t* x, const int32_t* ids, const float* w,
+                     int T, int k, int layer, int E, const mc_banks* host, float* y) {
+  const int H = host->H, I = host->I, fmt = host->fmt;
+  // units in first-occurrence order
+  std::vector<HostUnit> units;
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) {
+      int e = ids[(size_t)t * k + j];
+      if (e < 0 || e >= E) continue;
+      int64_t flat = (int64_t)layer * E + e;
+      if (flat >= host->n) continue;
+      HostUnit* u = nullptr;
+      for (auto& v : units)
+        if (v.entry == flat) u = &v;
+      if (!u) {
+        units.push_back(HostUnit{flat, {}, {}});
+        u = &units.back();
+      }
+      u->toks.push_back(t);
+      u->gates.push_back(w[(size_t)t * k + j]);
+    }
+  if (units.empty()) return MC_OK;
+
+  // prepared activations
+  std::vector<float> xp((size_t)T * H), xtmp(H);
+  for (int t = 0; t < T; ++t) {
+    for (int c = 0; c < H; ++c) xtmp[c] = bf16f(x[(size_t)t * H + c]);
+    prep_vec(xtmp.data(), H, fmt, xp.data() + (size_t)t * H);
+  }
+  // h per (unit, token-of-unit), prepared for the down contraction
+  std::vector<size_t> hoff(units.size() + 1, 0);
+  for (size_t u = 0; u < units.size(); ++u) hoff[u + 1] = hoff[u] + units[u].toks.size();
+  std::vector<float> h(hoff.back() * I), hp(hoff.back() * I);
+
+  const size_t gu_row = fmt == MC_MXFP4 ? H / 2 : (size_t)H * 2;
+  const size_t gu_per = 2 * (size_t)I * gu_row;
+  const size_t gus_per = 2 * (size_t)I * H / 32;
+  const size_t dn_row = fmt == MC_MXFP4 ? I / 2 : (size_t)I * 2;
+  const size_t dn_per = (size_t)H * dn_row;
+  const size_t dns_per = (size_t)H * I / 32;
+  const uint8_t* GU = static_cast<const uint8_t*>(host->gate_up);
+  const uint8_t* GUS = static_cast<const uint8_t*>(host->gate_up_scale);
+  const uint8_t* DN = static_cast<const uint8_t*>(host->down);
+  const uint8_t* DNS = static_cast<const uint8_t*>(host->down_scale);
+
+  constexpr int RB = 16;
+  const int nib = I / RB;
+  std::function<void(int)> phase1 = [&](int task) {
+    const size_t u = task / nib;
+    const int i0 = (task % nib) * RB;
+    const HostUnit& U = units[u];
+    const uint8_t* gu = GU + U.entry * gu_per;
+    const uint8_t* gus = fmt == MC_MXFP4 ? GUS + U.entry * gus_per : nullptr;
+    for (int i = i0; i < i0 + RB; ++i) {
+      const uint8_t* rg = gu + (size_t)i * gu_row;
+      const uint8_t* ru = gu + (size_t)(I + i) * gu_row;
+      const uint8_t* sg = gus ? gus + (size_t)i * (H / 32) : nullptr;
+      const uint8_t* su = gus ? gus + (size_t)(I + i) * (H / 32) : nullptr;
+      for (size_t n = 0; n < U.toks.size(); ++n) {
+        const float* xv = xp.data() + (size_t)U.toks[n] * H;
+        float g = dot_row(fmt, rg, sg, xv, H);
+        float up = dot_row(fmt, ru, su, xv, H);
+        h[(hoff[u] + n) * I + i] = g / (1.0f + expf(-g)) * up;
+      }
+    }
+  };
+  run_tasks(pool, (int)units.size() * nib, phase1);
+  for (size_t r = 0; r < hoff.back(); ++r) prep_vec(h.data() + r * I, I, fmt, hp.data() + r * I);
+
+  const int nrb = (H + RB - 1) / RB;
+  std::function<void(int)> phase2 = [&](int task) {
+    const int r0 = task * RB, r1 = std::min(H, r0 + RB);
+    for (size_t u = 0; u < units.size(); ++u) {
+      const HostUnit& U = units[u];
+      const uint8_t* dn = DN + U.entry * dn_per;
+      const uint8_t* dns = fmt == MC_MXFP4 ? DNS + U.entry * dns_per : nullptr;
+      for (int r = r0; r < r1; ++r) {
+        const uint8_t* row = dn + (size_t)r * dn_row;
+        const uint8_t* srow = dns ? dns + (size_t)r * (I / 32) : nullptr;
+        for (size_t n = 0; n < U.toks.size(); ++n) {
+          float v = dot_row(fmt, row, srow, hp.data() + (hoff[u] + n) * I, I);
+          y[(size_t)U.toks[n] * H + r] += U.gates[n] * v;
+        }
+      }
+    }
+  };
+  run_tasks(pool, nrb, phase2);
+  return MC_OK;
+}
+
+}  // namespace mc
+
+extern "C" int mc_host_experts(mc_host_pool* pool, const void* x_bf16, const int32_t* ids,
+                               const float* w, int32_t T, int32_t k, int32_t layer, int32_t E,
+                               const mc_banks* host, float* y) {
+  mc::clear_error();
+  if (!host || !(host->fmt == MC_BF16 || host->fmt == MC_MXFP4) || host->H <= 0 ||
+      host->I <= 0 || host->H % 64 || host->I % 64 || host->n <= 0 || !host->gate_up ||
+      !host->down || (host->fmt == MC_MXFP4 && (!host->gate_up_scale || !host->down_scale))) {
+    mc::set_error("mc_host_experts: invalid host banks");
+    return MC_EINVAL;
+  }
+  if (T < 0 || k < 1 || E < 1 || layer < 0) {
+    mc::set_error("mc_host_experts: T=%d k=%d E=%d layer=%d", T, k, E, layer);
+    return MC_EINVAL;
+  }
+  if (T == 0) return MC_OK;
+  if (!x_bf16 || !ids || !w || !y) {
+    mc::set_error("mc_host_experts: NULL pointer");
+    return MC_EINVAL;
+  }
+  return mc::host_experts_run(pool, static_cast<const uint16_t*>(x_bf16), ids, w, T, k, layer, E,
+                              host, y);
+}

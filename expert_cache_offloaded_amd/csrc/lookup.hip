@@ -1,0 +1,274 @@
+// slot_cache_lookup_evict: one layer call of the cross-layer LRU slot cache.
+//
+// [jjl357] "6.1 全局 LRU 专家缓存", "6.7 系统如何选择哪 q 个专家进入缓存" and
+// "8.2 把控制流表示成数据": a single GPU kernel dedups the routed experts, checks
+// residency, derives q, picks LRU victims and rewrites logical ids to a slot or a
+// host flag, so the whole step stays on the device (capturable, no host round trip).
+// [wanger] "3. ensure_experts_hybrid 内核": the integer (Q16) split rule.
+// [juhe] "生成阶段": slot_for_id / id_of_slot / usage tables.
+//
+// One workgroup of 1024 threads.  Unique experts of the call come from a presence
+// table over the layer's E experts (so they are already in ascending flat-id order);
+// ranks of hits/misses come from workgroup prefix sums.  Victims are taken in rounds:
+// each round finds the smallest stamp among the evictable slots not yet taken and
+// takes the slots carrying it in ascending slot order, which yields the victims in
+// (stamp, slot) order without sorting.  Every round takes at least one slot, so the
+// loop ends after at most q rounds.
+#include "mc_common.h"
+
+namespace mc {
+
+constexpr int kLkThreads = 1024;
+constexpr int kLkMaxE = 4096;
+constexpr int kLkMaxRoutes = 2048;
+
+__device__ __forceinline__ int64_t wave_min_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    int64_t w = __shfl_xor(v, o, 64);
+    v = w < v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Exclusive prefix sum of one int per thread over the workgroup; returns the
+// thread's offset and writes the total to *total (all threads).
+__device__ int block_excl_scan(int v, int* sh_wave, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh_wave[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < kLkThreads / 64 ? sh_wave[lane] : 0;
+    int z = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(z, o, 64);
+      if (lane >= o) z += y;
+    }
+    if (lane < kLkThreads / 64) sh_wave[lane] = z - w;   // exclusive wave offsets
+    if (lane == kLkThreads / 64 - 1) sh_wave[kLkThreads / 64] = z;
+  }
+  __syncthreads();
+  int off = sh_wave[wid] + x - v;
+  *total = sh_wave[kLkThreads / 64];
+  __syncthreads();
+  return off;
+}
+
+__device__ int64_t block_min_i64(int64_t v, int64_t* sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_min_i64(v);
+  if (lane == 0) sh[wid] = v;
+  __syncthreads();
+  if (wid == 0) {
+    int64_t w = lane < kLkThreads / 64 ? sh[lane] : INT64_MAX;
+    w = wave_min_i64(w);
+    if (lane == 0) sh[kLkThreads / 64] = w;
+  }
+  __syncthreads();
+  int64_t r = sh[kLkThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kLkThreads)
+lookup_kernel(int32_t L, int32_t E, int32_t S, int32_t* __restrict__ slot_of,
+              int32_t* __restrict__ id_of, int64_t* __restrict__ stamp, int64_t* __restrict__ clock_p,
+              int64_t* __restrict__ stats, int32_t layer, const int32_t* __restrict__ ids, int32_t T,
+              int32_t k, const int32_t* __restrict__ n_tok, uint32_t frac_q16, int32_t fixed_cap,
+              int32_t min_fill, int32_t* __restrict__ slots, int32_t* __restrict__ fill_flat,
+              int32_t* __restrict__ fill_slot, int32_t* __restrict__ n_fill,
+              int32_t* __restrict__ host_flat, int32_t* __restrict__ n_host, int32_t kcap) {
+  __shared__ uint8_t s_present[kLkMaxE];     // 1 if expert e is routed in this call
+  __shared__ int32_t s_slot_e[kLkMaxE];      // slot of expert e after the call, -1 = none
+  __shared__ int32_t s_victim[kLkMaxRoutes]; // victims in (stamp, slot) order
+  __shared__ int32_t s_miss[kLkMaxRoutes];   // misses, ascending flat id
+  __shared__ int s_scan[kLkThreads / 64 + 1];
+  __shared__ int64_t s_min[kLkThreads / 64 + 1];
+  __shared__ int s_err;
+
+  const int tid = threadIdx.x;
+  const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
+  const int nroutes = nt * k;
+  const int64_t clock = *clock_p + 1;
+
+  for (int e = tid; e < E; e += kLkThreads) {
+    s_present[e] = 0;
+    s_slot_e[e] = -1;
+  }
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+
+  // 1. presence of the valid routes
+  int my_err = 0;
+  for (int r = tid; r < nroutes; r += kLkThreads) {
+    int e = ids[r];
+    if (e == -1) continue;
+    if (e < 0 || e >= E) {
+      ++my_err;
+      continue;
+    }
+    s_present[e] = 1;
+  }
+  if (my_err) atomicAdd(&s_err, my_err);
+  __syncthreads();
+
+  // 2. hits are stamped; misses ranked in ascending expert order
+  //    each thread owns a contiguous run of experts so ranks follow e order
+  const int per = (E + kLkThreads - 1) / kLkThreads;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int my_hits = 0, my_miss = 0;
+  for (int e = e0; e < e1; ++e) {
+    if (!s_present[e]) continue;
+    int s = slot_of[(int64_t)layer * E + e];
+    if (s >= 0 && s < S) {
+      stamp[s] = clock;
+      s_slot_e[e] = s;
+      ++my_hits;
+    } else {
+      ++my_miss;
+    }
+  }
+  int n_hits, m;
+  int miss_off = block_excl_scan(my_miss, s_scan, &m);
+  block_excl_scan(my_hits, s_scan, &n_hits);
+  for (int e = e0, i = miss_off; e < e1; ++e)
+    if (s_present[e] && s_slot_e[e] < 0) s_miss[i++] = layer * E + e;
+  __threadfence_block();
+  __syncthreads();
+
+  // 3. split count (integer rule), capped by evictable slots and list capacity
+  int q;
+  if (m == 0) {
+    q = 0;
+  } else if (frac_q16 == 0) {
+    q = min(m, fixed_cap);
+  } else {
+    const int64_t f = frac_q16;
+    const int64_t lo = ((int64_t)m * f) >> 16;
+    const int64_t c_lo = max(lo * (65536 - f), ((int64_t)m - lo) * f);
+    const int64_t c_hi = max((lo + 1) * (65536 - f), ((int64_t)m - lo - 1) * f);
+    q = (int)min((int64_t)m, c_lo <= c_hi ? lo : lo + 1);
+  }
+  if (min_fill && m >= 1) q = max(q, 1);
+  q = min(q, S - n_hits);
+  q = min(q, kcap);
+
+  // 4. victims in (stamp, slot) order, in rounds of equal stamp
+  int taken = 0;
+  int64_t floor_stamp = -1;   // stamps <= floor_stamp were exhausted by earlier rounds
+  const int sper = (S + kLkThreads - 1) / kLkThreads;
+  const int s0 = tid * sper, s1 = min(S, s0 + sper);
+  while (taken < q) {
+    int64_t mine = INT64_MAX;
+    for (int s = s0; s < s1; ++s) {
+      int64_t st = stamp[s];
+      if (st > floor_stamp && st < clock && st < mine) mine = st;
+    }
+    const int64_t smin = block_min_i64(mine, s_min);
+    int cnt = 0;
+    for (int s = s0; s < s1; ++s) cnt += stamp[s] == smin;
+    int tot;
+    int off = block_excl_scan(cnt, s_scan, &tot);
+    const int need = q - taken;
+    for (int s = s0; s < s1 && off < need; ++s)
+      if (stamp[s] == smin) s_victim[taken + off++] = s;
+    taken += min(tot, need);
+    floor_stamp = smin;
+    __syncthreads();
+    if (tot == 0) break;   // no evictable slot left (only with inconsistent tables)
+  }
+  q = taken;
+
+  // 5. install the first q misses into the victims
+  int my_evict = 0;
+  for (int i = tid; i < q; i += kLkThreads) {
+    const int s = s_victim[i];
+    const int f = s_miss[i];
+    const int old = id_of[s];
+    if (old >= 0 && old < L * E) {
+      slot_of[old] = -1;
+      ++my_evict;
+    }
+    slot_of[f] = s;
+    id_of[s] = f;
+    stamp[s] = clock;
+    s_slot_e[f - layer * E] = s;
+    fill_flat[i] = f;
+    fill_slot[i] = s;
+  }
+  for (int i = q + tid; i < m; i += kLkThreads) host_flat[i - q] = s_miss[i];
+  int n_evict;
+  block_excl_scan(my_evict, s_scan, &n_evict);   // includes a barrier
+
+  // 6. rewrite routes to slots (-1 = host-computed, masked, invalid, beyond n_tok)
+  for (int r = tid; r < T * k; r += kLkThreads) {
+    int v = -1;
+    if (r < nroutes) {
+      int e = ids[r];
+      if (e >= 0 && e < E) v = s_slot_e[e];
+    }
+    slots[r] = v;
+  }
+
+  if (tid == 0) {
+    *clock_p = clock;
+    *n_fill = q;
+    *n_host = m - q;
+    stats[MC_STAT_HITS] += n_hits;
+    stats[MC_STAT_MISSES] += m;
+    stats[MC_STAT_FILLS] += q;
+    stats[MC_STAT_HOST] += m - q;
+    stats[MC_STAT_EVICT] += n_evict;
+    stats[MC_STAT_CALLS] += 1;
+    stats[MC_STAT_ERR] += s_err;
+  }
+}
+
+}  // namespace mc
+
+using namespace mc;
+
+extern "C" int slot_cache_lookup_evict(const mc_cache* c, int32_t layer, const int32_t* ids,
+                                       int32_t T, int32_t k, const int32_t* n_tok,
+                                       uint32_t frac_q16, int32_t fixed_cap, int32_t min_fill,
+                                       int32_t* slots, int32_t* fill_flat, int32_t* fill_slot,
+                                       int32_t* n_fill, int32_t* host_flat, int32_t* n_host,
+                                       int32_t kcap, hipStream_t s) {
+  clear_error();
+  MC_REQUIRE(c != nullptr, "slot_cache_lookup_evict: cache is NULL");
+  MC_REQUIRE(c->L > 0 && c->E > 0 && c->S > 0, "slot_cache_lookup_evict: L=%d E=%d S=%d",
+             c->L, c->E, c->S);
+  MC_REQUIRE(c->E <= kLkMaxE, "slot_cache_lookup_evict: E=%d exceeds %d", c->E, kLkMaxE);
+  MC_REQUIRE((int64_t)c->L * c->E < (1ll << 31), "slot_cache_lookup_evict: L*E too large");
+  MC_REQUIRE(c->slot_of && c->id_of && c->stamp && c->clock && c->stats,
+             "slot_cache_lookup_evict: NULL table pointer");
+  MC_REQUIRE(layer >= 0 && layer < c->L, "slot_cache_lookup_evict: layer=%d not in [0, %d)",
+             layer, c->L);
+  MC_REQUIRE(T >= 0 && k >= 1, "slot_cache_lookup_evict: T=%d k=%d", T, k);
+  MC_REQUIRE((int64_t)T * k <= kLkMaxRoutes, "slot_cache_lookup_evict: T*k=%lld exceeds %d",
+             (long long)T * k, kLkMaxRoutes);
+  MC_REQUIRE(frac_q16 <= 65536u, "slot_cache_lookup_evict: frac_q16=%u exceeds 65536", frac_q16);
+  MC_REQUIRE(fixed_cap >= 0, "slot_cache_lookup_evict: fixed_cap=%d must be >= 0", fixed_cap);
+  MC_REQUIRE(kcap >= T * k, "slot_cache_lookup_evict: kcap=%d < T*k=%d", kcap, T * k);
+  MC_REQUIRE(ids && slots && fill_flat && fill_slot && n_fill && host_flat && n_host,
+             "slot_cache_lookup_evict: NULL pointer");
+  hipLaunchKernelGGL(lookup_kernel, dim3(1), dim3(kLkThreads), 0, s, c->L, c->E, c->S, c->slot_of,
+                     c->id_of, c->stamp, c->clock, c->stats, layer, ids, T, k, n_tok, frac_q16,
+                     fixed_cap, min_fill, slots, fill_flat, fill_slot, n_fill, host_flat, n_host,
+                     kcap);
+  MC_LAUNCH_CHECK();
+  return MC_OK;
+}

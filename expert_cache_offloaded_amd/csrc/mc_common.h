@@ -1,0 +1,124 @@
+// Shared host/device helpers of the MoE slot-cache library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/mc.h"
+
+namespace mc {
+
+// ---------------------------------------------------------------- host side errors
+
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define MC_REQUIRE(cond, ...)            \
+  do {                                   \
+    if (!(cond)) {                       \
+      ::mc::set_error(__VA_ARGS__);      \
+      return MC_EINVAL;                  \
+    }                                    \
+  } while (0)
+
+#define MC_HIP(call)                                                        \
+  do {                                                                      \
+    hipError_t e_ = (call);                                                 \
+    if (e_ != hipSuccess) {                                                 \
+      ::mc::set_error("%s failed: %s", #call, hipGetErrorString(e_));       \
+      return MC_EHIP;                                                       \
+    }                                                                       \
+  } while (0)
+
+// Checks a launch (no synchronisation).
+#define MC_LAUNCH_CHECK()                                                   \
+  do {                                                                      \
+    hipError_t e_ = hipGetLastError();                                      \
+    if (e_ != hipSuccess) {                                                 \
+      ::mc::set_error("kernel launch failed: %s", hipGetErrorString(e_));   \
+      return MC_EHIP;                                                       \
+    }                                                                       \
+  } while (0)
+
+// Bytes of one expert entry in each bank.
+struct BankBytes {
+  size_t gate_up, gate_up_scale, down, down_scale;
+  size_t total() const { return gate_up + gate_up_scale + down + down_scale; }
+};
+
+inline BankBytes bank_bytes(int fmt, int H, int I) {
+  BankBytes b{};
+  if (fmt == MC_BF16) {
+    b.gate_up = (size_t)2 * I * H * 2;
+    b.down = (size_t)H * I * 2;
+  } else {
+    b.gate_up = (size_t)2 * I * H / 2;
+    b.gate_up_scale = (size_t)2 * I * H / 32;
+    b.down = (size_t)H * I / 2;
+    b.down_scale = (size_t)H * I / 32;
+  }
+  return b;
+}
+
+// Host validation of a bank descriptor; returns MC_OK or MC_EINVAL with a message.
+int check_banks(const mc_banks* b, const char* what, bool need_nonempty = true);
+
+// ---------------------------------------------------------------- device helpers
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// e8m0 exponent byte -> fp32 scale 2^(X-127) (X = 0 gives 2^-127, a subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t X) {
+  return X == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(X << 23);
+}
+
+// Two FP4 E2M1 values held in byte `sel` of `v`, scaled, as packed bf16 (exact for
+// the scales MXFP4 weights use).
+template <int SEL>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t v, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t v, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, SEL);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Sum over all 64 lanes of a wavefront; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace mc

@@ -1,0 +1,150 @@
+"""Device/host memory plumbing and the per-layer call sequence of the decode path.
+
+torch allocates every buffer (device tensors, pinned host tensors) and provides the
+stream; each step of the path is one call into ``libmc.so``:
+
+  moe_route -> slot_cache_lookup_evict -> [hybrid_split_merge(SPLIT)] -> mc_fill_slots
+            -> moe_experts_decode -> hybrid_split_merge(MERGE) | mc_finish_bf16
+
+which follows [jjl357] "6.8 CPU 与 GPU 并发执行的顺序" and [wanger] "代码全链路":
+the host branch is started before the fills and the GPU experts, and the two
+partials are merged at the end.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib as L
+
+_NP2T = {"uint8": torch.uint8, "uint16": torch.int16}
+
+
+def bank_shapes(H: int, I: int, fmt: str):
+    if fmt == "bf16":
+        return {"gate_up": ((2 * I, H), torch.int16), "down": ((H, I), torch.int16)}
+    return {"gate_up": ((2 * I, H // 2), torch.uint8), "gate_up_scale": ((2 * I, H // 32), torch.uint8),
+            "down": ((H, I // 2), torch.uint8), "down_scale": ((H, I // 32), torch.uint8)}
+
+
+def alloc_banks(n: int, H: int, I: int, fmt: str, device=None, pin: bool = False) -> Dict[str, torch.Tensor]:
+    out = {}
+    for name, (shp, dt) in bank_shapes(H, I, fmt).items():
+        if device is not None and device != "cpu":
+            out[name] = torch.empty((n,) + shp, dtype=dt, device=device)
+        else:
+            out[name] = torch.empty((n,) + shp, dtype=dt, pin_memory=pin)
+    return out
+
+
+class BankSet:
+    """Tensors of one bank set plus its C descriptor."""
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], H: int, I: int, fmt: str):
+        self.t, self.H, self.I, self.fmt = tensors, H, I, fmt
+        self.desc = L.make_banks(fmt, H, I, tensors)
+
+    @property
+    def n(self) -> int:
+        return self.t["gate_up"].shape[0]
+
+    def entry(self, i: int) -> "BankSet":
+        """A one-entry view (e.g. one layer's shared expert)."""
+        return BankSet({k: v[i:i + 1] for k, v in self.t.items()}, self.H, self.I, self.fmt)
+
+
+class CacheState:
+    """Device tables of the cross-layer LRU (caller-owned memory)."""
+
+    def __init__(self, L_: int, E: int, S: int, device="cuda"):
+        self.L, self.E, self.S = L_, E, S
+        self.t = {"slot_of": torch.empty(L_ * E, dtype=torch.int32, device=device),
+                  "id_of": torch.empty(S, dtype=torch.int32, device=device),
+                  "stamp": torch.empty(S, dtype=torch.int64, device=device),
+                  "clock": torch.empty(1, dtype=torch.int64, device=device),
+                  "stats": torch.empty(8, dtype=torch.int64, device=device)}
+        self.desc = L.make_cache(L_, E, S, self.t)
+
+    def reset(self, stream=None):
+        L.cache_reset(self.desc, stream)
+
+    def state(self) -> dict:
+        return {k: v.cpu().numpy() for k, v in self.t.items()}
+
+
+@dataclass
+class DecodeBuffers:
+    """Fixed-shape workspaces of one decode layer call (capacity T tokens x k routes)."""
+    T: int
+    k: int
+    H: int
+    I: int
+    device: str = "cuda"
+
+    def __post_init__(self):
+        d, T, k = self.device, self.T, self.k
+        i32 = dict(dtype=torch.int32, device=d)
+        self.ids = torch.empty((T, k), **i32)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=d)
+        self.slots = torch.empty((T, k), **i32)
+        self.fill_flat = torch.empty(T * k, **i32)
+        self.fill_slot = torch.empty(T * k, **i32)
+        self.n_fill = torch.zeros(1, **i32)
+        self.host_flat = torch.empty(T * k, **i32)
+        self.n_host = torch.zeros(1, **i32)
+        self.gpu_w = torch.empty((T, k), dtype=torch.float32, device=d)
+        self.host_ids = torch.empty((T, k), **i32)
+        self.y_acc = torch.empty((T, self.H), dtype=torch.float32, device=d)
+        self.y_host = torch.empty((T, self.H), dtype=torch.float32, device=d)
+        self.y = torch.empty((T, self.H), dtype=torch.int16, device=d)
+        self.ws = torch.empty(L.decode_ws_bytes(T, k, self.I) // 4 + 4, dtype=torch.float32, device=d)
+
+
+class DecodeLayer:
+    """Runs one decode layer call through the C ABI (offload or hybrid mode)."""
+
+    def __init__(self, cache: CacheState, host: BankSet, pool: BankSet, shared: Optional[BankSet],
+                 bufs: DecodeBuffers, frac_q16: int = 1 << 16, fixed_cap: int = 1, min_fill: int = 1,
+                 renorm: int = 1, hybrid: bool = False, host_pool: Optional[L.HostPool] = None):
+        self.cache, self.host, self.pool, self.shared, self.b = cache, host, pool, shared, bufs
+        self.frac_q16, self.fixed_cap, self.min_fill, self.renorm = frac_q16, fixed_cap, min_fill, renorm
+        self.hybrid = hybrid
+        self.host_pool = host_pool
+        if hybrid:
+            nb = L.hybrid_stage_bytes(bufs.T, bufs.k, bufs.H)
+            self.stage = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+        self._hy = {}
+
+    def __call__(self, layer: int, logits: torch.Tensor, x: torch.Tensor, n_tok=None, stream=None):
+        """logits fp32 [T, E], x bf16 bits [T, H] (device) -> self.b.y (bf16 bits)."""
+        b = self.b
+        L.moe_route(logits, b.k, self.renorm, b.ids, b.w, stream)
+        L.slot_cache_lookup_evict(self.cache.desc, layer, b.ids, n_tok, self.frac_q16, self.fixed_cap,
+                                  self.min_fill, b.slots, b.fill_flat, b.fill_slot, b.n_fill,
+                                  b.host_flat, b.n_host, stream)
+        if self.hybrid:
+            key = (layer, x.data_ptr(), None if n_tok is None else n_tok.data_ptr())
+            hy = self._hy.get(key)
+            if hy is None:
+                hy = L.make_hybrid(x, b.ids, b.slots, b.w, layer, self.cache.E, n_tok, self.host.desc,
+                                   self.host_pool, self.stage, b.gpu_w, b.host_ids, b.y_acc, b.y_host, b.y)
+                self._hy[key] = hy
+            L.hybrid_split_merge(hy, L.MC_SPLIT_SUBMIT, stream)
+            w_gpu = b.gpu_w
+        else:
+            w_gpu = b.w
+        L.fill_slots(self.host.desc, self.pool.desc, b.fill_flat, b.fill_slot, b.n_fill, stream)
+        if stream is None:
+            b.y_acc.zero_()
+        else:
+            with torch.cuda.stream(stream):
+                b.y_acc.zero_()
+        sh = self.shared.entry(layer).desc if self.shared is not None else None
+        L.moe_experts_decode(x, b.slots, w_gpu, n_tok, self.pool.desc, sh, b.ws, b.y_acc, stream)
+        if self.hybrid:
+            L.hybrid_split_merge(hy, L.MC_MERGE, stream)
+        else:
+            L.finish_bf16(b.y_acc, n_tok, b.y, stream)
+        return b.y

@@ -1,0 +1,285 @@
+/*
+ * mc.h — C ABI of the MI355X (gfx950) routed-MoE layer over a cross-layer LRU
+ * expert slot cache ("mc" = MoE cache).
+ *
+ * The operations follow the FreeToken pages:
+ *   [jjl357] "FreeToken: Efficient Edge-Native MoE Serving with Bandwidth-Adaptive
+ *            Execution" (jjl357.github.io blog)
+ *   [qiita]  "FreeTokenってなんだ？ ─ 8GBノートPCで35Bを動かす判断基準" (Qiita)
+ *   [wanger] "FreeToken hybrid MoE 后端：带宽比如何决定专家「搬」还是「算」"
+ *   [juhe]   juhe.plus explainer of FreeToken on an 8 GB RTX 4060 Laptop
+ *
+ * Conventions for every call
+ *   - Ownership: the caller allocates and frees every buffer (device memory,
+ *     pinned host memory).  The library never frees caller memory and never
+ *     allocates device memory inside a call.  The only library-owned object is
+ *     mc_host_pool (CPU worker threads).
+ *   - Asynchrony: calls enqueue work on the given HIP stream and return; results
+ *     are visible to the host after the stream is synchronised.  Counts written
+ *     by the device (n_fill, n_host, ...) are device int32s.
+ *   - Valid counts: where a call takes `const int32_t* n_tok`, NULL means all T
+ *     rows are valid; otherwise it is a DEVICE pointer to the number of valid
+ *     rows (0 <= *n_tok <= T), read by the kernels, so a fixed-shape call can be
+ *     captured once in a hipGraph and replayed for any batch size up to T
+ *     ([jjl357] "8.2 把控制流表示成数据": fixed-size buffers plus device-resident
+ *     valid counts).
+ *   - Errors: arguments are validated on the host before anything is enqueued;
+ *     a bad argument returns MC_EINVAL, a failing HIP call MC_EHIP, with a
+ *     message from mc_last_error().  Bad device data (an expert id outside
+ *     [-1, E), a slot outside [-1, S)) is never dereferenced: the route is
+ *     treated as absent and the cache's stats[MC_STAT_ERR] counter is raised.
+ *     No call exits the process or lets an exception cross the ABI.
+ *   - Threading: calls are reentrant; one mc_cache must be used from one stream
+ *     at a time (calls on one cache are ordered by that stream).
+ */
+#ifndef MC_H
+#define MC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MC_ABI_VERSION 1
+
+typedef enum {
+  MC_OK = 0,
+  MC_EINVAL = -1,        /* invalid argument (nothing was enqueued)           */
+  MC_ENOMEM = -2,        /* a caller-provided workspace/staging is too small  */
+  MC_EHIP = -3,          /* a HIP runtime call failed                         */
+  MC_EUNSUPPORTED = -4,  /* shape or format this build does not handle        */
+  MC_EDEVICE = -5        /* device-side error counter was found non-zero      */
+} mc_status;
+
+typedef enum { MC_BF16 = 0, MC_MXFP4 = 1 } mc_wfmt;
+
+/*
+ * One set of expert banks: n experts, indexed by slot (device pool) or by flat id
+ * l*E + e (host pool).  A flat id / slot indexes the same entry of every bank, so
+ * one entry across all banks is one complete expert ([jjl357] "8.4 FTW 权重布局").
+ *   MC_BF16 : gate_up  bf16 [n][2I][H];   down bf16 [n][H][I];   *_scale unused
+ *   MC_MXFP4: gate_up  u8   [n][2I][H/2]  e2m1 codes
+ *             gate_up_scale u8 [n][2I][H/32] e8m0
+ *             down     u8   [n][H][I/2]   e2m1 codes
+ *             down_scale    u8 [n][H][I/32] e8m0
+ * gate_up rows [0, I) are the gate projection, rows [I, 2I) the up projection;
+ * byte j of a code row holds element 2j in its low nibble and 2j+1 in its high
+ * nibble; one e8m0 scale per 32 consecutive elements along the contraction axis
+ * (OCP MX: value = 2^(X-127) * e2m1).  Pointers are device pointers for a device
+ * pool, pinned host pointers for a host pool.  Bank bases must be 16-byte aligned.
+ */
+typedef struct {
+  int32_t fmt;            /* mc_wfmt */
+  int32_t H, I;           /* hidden size, expert intermediate size */
+  int32_t reserved;
+  int64_t n;              /* number of experts (slots or flat ids) */
+  void *gate_up, *gate_up_scale;
+  void *down, *down_scale;
+} mc_banks;
+
+/*
+ * Cross-layer LRU state, all device memory owned by the caller
+ * ([juhe] "生成阶段": slot_for_id / id_of_slot / usage; [jjl357] "3. FreeToken Overview":
+ * one pool of slots shared by every layer, a slot = one whole (layer, expert)).
+ */
+typedef struct {
+  int32_t L, E, S;        /* layers, experts per layer, slots */
+  int32_t reserved;
+  int32_t *slot_of;       /* [L*E]  slot holding flat id, -1 = not resident */
+  int32_t *id_of;         /* [S]    flat id held by slot, -1 = empty         */
+  int64_t *stamp;         /* [S]    clock of last access, 0 = never used     */
+  int64_t *clock;         /* [1]    +1 per lookup call                       */
+  int64_t *stats;         /* [8]    see MC_STAT_*                            */
+} mc_cache;
+
+enum { MC_STAT_HITS = 0, MC_STAT_MISSES = 1, MC_STAT_FILLS = 2, MC_STAT_HOST = 3,
+       MC_STAT_EVICT = 4, MC_STAT_CALLS = 5, MC_STAT_ERR = 6 };
+
+/* ------------------------------------------------------------------------- */
+/* Library                                                                   */
+/* ------------------------------------------------------------------------- */
+
+int mc_abi_version(void);
+/* Message of the last failing call on this thread ("" if none). */
+const char* mc_last_error(void);
+
+/*
+ * Empty cache: slot_of = -1, id_of = -1, stamp = 0, clock = 0, stats = 0 (enqueued
+ * as fill kernels on s, so it may be captured).
+ */
+int mc_cache_reset(const mc_cache* c, hipStream_t s);
+
+/*
+ * Q16 fetched fraction of the misses ([jjl357] "6.5 q* 的推导"; [wanger] "实测版本").
+ * If p_ov > 0, f = p_ov / (p_ov + c_ov) from bandwidths measured while the host
+ * branch and the link run concurrently; otherwise f = b_p / b_h, and f = 1 when
+ * b_h <= b_p (no residual host bandwidth, [jjl357] "6.4").  Returns
+ * floor(f * 65536 + 1/2) clamped to [1, 65536]; 0 when there is no usable
+ * measurement (p_ov <= 0 and b_p <= 0) — the fixed-cap mode of
+ * slot_cache_lookup_evict ([wanger] "1. 启动时": no profile -> fixed fetch cap).
+ */
+uint32_t mc_fetch_fraction_q16(double b_p, double b_h, double p_ov, double c_ov);
+
+/* ------------------------------------------------------------------------- */
+/* Hot path                                                                  */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Top-k routing ([jjl357] "1.1 Dense LLM 与 MoE LLM 的区别").
+ *   logits   device fp32 [T][E]
+ *   topk_ids device int32 [T][k] out: experts by logit descending, equal logits
+ *            to the lower id (comparisons on the raw fp32 values)
+ *   topk_w   device fp32 [T][k] out: renorm=1: softmax over the k selected
+ *            logits; renorm=0: the selected experts' softmax probabilities over
+ *            all E logits.
+ * 1 <= k <= min(E, 32), 1 <= E <= 1024.  T = 0 enqueues nothing.
+ */
+int moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renorm,
+              int32_t* topk_ids, float* topk_w, hipStream_t s);
+
+/*
+ * One layer call of the cross-layer LRU ([jjl357] "6.1", "6.7", "8.2";
+ * [wanger] "3. ensure_experts_hybrid 内核").  One kernel, one workgroup:
+ *   1. clock += 1; U = sorted unique flat ids layer*E + e of the valid routes
+ *      (rows t < *n_tok; id -1 = masked route; ids outside [-1, E) count in
+ *      stats[ERR] and are ignored).
+ *   2. hits: resident members of U, stamped with the clock.  Misses M (ascending),
+ *      m = |M|.
+ *   3. q: frac_q16 = 0 -> min(m, fixed_cap); otherwise lo = (m*frac_q16) >> 16 and
+ *      q = lo or lo+1, whichever has the smaller max(F*(65536-frac_q16),
+ *      (m-F)*frac_q16) (ties to lo), then min(q, m); min_fill != 0 and m >= 1
+ *      -> q >= 1.  Then q is capped by the slots not hit in this call and by kcap.
+ *   4. victims: the q slots not hit in this call with the smallest (stamp, slot).
+ *      The first q misses are paired in order with the victims: the old
+ *      occupant (if any) is evicted, the miss is installed and stamped.
+ *   5. the remaining m - q misses are host-computed: no insert, no stamp.
+ *   6. slots[t][j] = slot of the route's expert, or -1 (host-computed, masked,
+ *      invalid, or t >= *n_tok).
+ *   ids       device int32 [T][k] expert-in-layer ids
+ *   fill_flat, fill_slot  device int32 [kcap] out: (flat id, slot) of each fill
+ *   n_fill    device int32 [1] out: q
+ *   host_flat device int32 [kcap] out: flat ids of the host-computed misses, ascending
+ *   n_host    device int32 [1] out: m - q
+ * frac_q16 in [0, 65536] (65536 = fetch every miss), fixed_cap >= 0,
+ * kcap >= T*k, 0 <= layer < L, T*k <= 4096.
+ */
+int slot_cache_lookup_evict(const mc_cache* c, int32_t layer, const int32_t* ids, int32_t T,
+                            int32_t k, const int32_t* n_tok, uint32_t frac_q16, int32_t fixed_cap,
+                            int32_t min_fill, int32_t* slots, int32_t* fill_flat,
+                            int32_t* fill_slot, int32_t* n_fill, int32_t* host_flat,
+                            int32_t* n_host, int32_t kcap, hipStream_t s);
+
+/*
+ * Fill fetch ([jjl357] "6.7" step 3 and "6.8": one fused batch copy of the chosen
+ * misses into their victim slots).  Copies every bank of host entry fill_flat[i]
+ * into pool entry fill_slot[i] for i < *n_fill, as a kernel that reads the pinned
+ * host banks over the host link (no host synchronisation, capturable).
+ *   host  pinned host banks indexed by flat id (host->n = L*E), same fmt/H/I as pool
+ *   pool  device slot banks (pool->n = S)
+ *   fill_flat, fill_slot, n_fill: as written by slot_cache_lookup_evict (device)
+ * Entries with a flat id outside [0, host->n) or a slot outside [0, pool->n) are
+ * skipped.  kcap = capacity of the lists.
+ */
+int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
+                  const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap, hipStream_t s);
+
+/*
+ * Workspace bytes of moe_experts_decode for up to T tokens x k routes.
+ */
+size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I);
+
+/*
+ * Slot-indirected SwiGLU experts and gated combine on the GPU
+ * ([jjl357] "1.1", "6.7" step 5; [wanger] "代码全链路": GPU routes of the hybrid
+ * split carry gate 0 for host routes).
+ *   y_acc[t][:] += sum_j w[t][j] * Expert(pool[slots[t][j]])(x[t])
+ *                  (+ Expert(shared[0])(x[t]) with weight 1 if shared != NULL)
+ * for t < *n_tok, over routes with slots[t][j] >= 0; each distinct slot's weights
+ * are read once for all tokens that route to it ([jjl357] "6.1": dedup).
+ * Expert(x) = W_down (silu(W_gate x) * (W_up x)), fp32 accumulation; x bf16 [T][H];
+ * y_acc fp32 [T][H] (accumulated into, not overwritten).
+ *   pool     device slot banks; shared: NULL or a device bank whose entry 0 is the
+ *            layer's shared expert (same fmt, H, I).
+ *   ws       device workspace of moe_experts_decode_ws_bytes(T, k, I) bytes.
+ * Needs H % 64 == 0, I % 64 == 0 (MXFP4 blocks of 32 along both contractions),
+ * T*k <= 1024.
+ */
+int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w, int32_t T,
+                       int32_t k, const int32_t* n_tok, const mc_banks* pool,
+                       const mc_banks* shared, void* ws, size_t ws_bytes, float* y_acc,
+                       hipStream_t s);
+
+/* ------------------------------------------------------------------------- */
+/* Hybrid split / merge and the host branch                                  */
+/* ------------------------------------------------------------------------- */
+
+/* Persistent CPU worker pool ([jjl357] "8.3": persistent C++ workers pinned to cores). */
+typedef struct mc_host_pool mc_host_pool;
+/* n_threads >= 1; cpu_ids: NULL = no pinning, else n_threads core ids. NULL on failure. */
+mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* cpu_ids);
+void mc_host_pool_destroy(mc_host_pool* p);
+
+/*
+ * Host expert FFN, synchronous (used by the hybrid branch and by tests):
+ *   y[t][:] += sum_j w[t][j] * Expert(host[layer*E + flat_ids... ]) — precisely, for
+ *   every (t, j) with ids[t][j] >= 0: y[t] += w[t][j] * Expert(host entry
+ *   layer*E + ids[t][j])(x[t]).  Dequantisation happens inside the dot products
+ *   ([jjl357] "8.3": SIMD kernels dequantise in-kernel).  All pointers are host
+ *   memory: x bf16 [T][H], ids int32 [T][k], w fp32 [T][k], y fp32 [T][H].
+ *   pool may be NULL (runs on the calling thread).
+ */
+int mc_host_experts(mc_host_pool* pool, const void* x_bf16, const int32_t* ids, const float* w,
+                    int32_t T, int32_t k, int32_t layer, int32_t E, const mc_banks* host,
+                    float* y);
+
+/* Pinned staging bytes of one hybrid layer call (header + x, ids, w, y_host). */
+size_t mc_hybrid_stage_bytes(int32_t T, int32_t k, int32_t H);
+
+typedef struct {
+  const void* x_bf16;        /* device bf16 [T][H]                                   */
+  const int32_t* ids_raw;    /* device int32 [T][k]: router ids (expert-in-layer)    */
+  const int32_t* slots;      /* device int32 [T][k]: slot_cache_lookup_evict output  */
+  const float* w;            /* device fp32 [T][k]: router gates                     */
+  int32_t T, k, layer, E;
+  const int32_t* n_tok;      /* device valid count or NULL                           */
+  const mc_banks* host;      /* pinned host banks by flat id                         */
+  mc_host_pool* pool;        /* CPU workers                                          */
+  void* pinned_stage;        /* caller-owned pinned host memory, mc_hybrid_stage_bytes */
+  size_t stage_bytes;
+  float* gpu_w;              /* device fp32 [T][k] out: w where slot >= 0, else 0   */
+  int32_t* host_ids;         /* device int32 [T][k] out: raw id where slot < 0, else -1 */
+  float* y_acc;              /* device fp32 [T][H]: GPU partial (moe_experts_decode) */
+  float* y_host;             /* device fp32 [T][H] out: host partial, copied back    */
+  void* y_bf16;              /* device bf16 [T][H] out: bf16(y_acc + y_host)         */
+} mc_hybrid;
+
+enum { MC_SPLIT_SUBMIT = 0, MC_MERGE = 1 };
+
+/*
+ * Exact split and merge of one decode layer ([jjl357] "6.2", "6.8", "6.9";
+ * [wanger] "代码全链路"; [juhe] "为什么可以直接相加").
+ * MC_SPLIT_SUBMIT: kernel writes gpu_w and host_ids (complementary masks: every
+ *   valid route is on exactly one side), copies x / host_ids / w to the pinned
+ *   stage and enqueues the host branch on the worker pool through a host function
+ *   that returns at once, so the GPU continues with fills and moe_experts_decode.
+ * MC_MERGE: waits (host function) for the host branch, copies its fp32 partial to
+ *   y_host, and writes y_bf16 = bf16_rne(y_acc + y_host) — one rounding.
+ * Every SPLIT_SUBMIT must be followed by a MERGE on the same stream before the
+ * stage is reused.
+ */
+int hybrid_split_merge(const mc_hybrid* h, int32_t phase, hipStream_t s);
+
+/*
+ * Final bf16 output of a layer with no host branch: y_bf16 = bf16_rne(y_acc) for
+ * rows t < *n_tok (rows beyond are set to 0).
+ */
+int mc_finish_bf16(const float* y_acc, int32_t T, int32_t H, const int32_t* n_tok, void* y_bf16,
+                   hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MC_H */

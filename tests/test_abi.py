@@ -1,0 +1,95 @@
+"""The C ABI library loads and exports what include/mc.h declares; host-side
+argument validation (no GPU work is enqueued by these calls)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from oracle import fetch_fraction_q16 as oracle_q16
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "mc.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", src))
+    skip = {"if", "for", "while", "return", "sizeof", "defined"}
+    return sorted(n for n in names if n not in skip and (n.startswith("mc_") or n.startswith("moe_")
+                                                       or n in ("slot_cache_lookup_evict", "hybrid_split_merge")))
+
+
+def test_header_declares_the_hot_path():
+    names = _declared()
+    for n in ("moe_route", "slot_cache_lookup_evict", "moe_experts_decode", "hybrid_split_merge",
+              "mc_fill_slots"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from expert_cache_offloaded_amd import _lib
+    lib = _lib.lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    # and the binding covers every declared entry point
+    assert set(_declared()) <= set(_lib.declared_symbols())
+
+
+def test_abi_version():
+    from expert_cache_offloaded_amd import abi_version
+    assert abi_version() == 1
+
+
+@pytest.mark.parametrize("bp,bh,pov,cov", [(11.8, 47.5, 0, 0), (52.7, 77.3, 0, 0), (49.0, 53.8, 0, 0),
+                                           (1.0, 4.0, 0, 0), (50.0, 40.0, 0, 0), (0, 0, 0, 0),
+                                           (0, 0, 30.0, 10.0), (0, 0, 12.5, 0.0), (1e-9, 1.0, 0, 0)])
+def test_fetch_fraction_matches_oracle(bp, bh, pov, cov):
+    from expert_cache_offloaded_amd import fetch_fraction_q16
+    assert fetch_fraction_q16(bp, bh, pov, cov) == oracle_q16(bp, bh, pov, cov)
+
+
+def test_validation_errors_do_not_need_a_gpu():
+    from expert_cache_offloaded_amd import _lib as L
+    lib = L.lib()
+    ids = (C.c_int32 * 8)()
+    w = (C.c_float * 8)()
+    lg = (C.c_float * 64)()
+    # k = 0, k > E, E too large, renorm out of range
+    assert lib.moe_route(lg, 4, 16, 0, 1, ids, w, None) == L.MC_EINVAL
+    assert lib.moe_route(lg, 4, 2, 3, 1, ids, w, None) == L.MC_EINVAL
+    assert lib.moe_route(lg, 1, 4096, 2, 1, ids, w, None) == L.MC_EINVAL
+    assert lib.moe_route(lg, 4, 16, 2, 7, ids, w, None) == L.MC_EINVAL
+    assert "renorm" in L.last_error()
+    # empty batch: nothing to do
+    assert lib.moe_route(lg, 0, 16, 2, 1, ids, w, None) == L.MC_OK
+    # cache checks
+    c = L.Cache()
+    c.L, c.E, c.S = 2, 8, 4
+    assert lib.slot_cache_lookup_evict(C.byref(c), 0, ids, 4, 2, None, 65536, 1, 1, ids, ids, ids, ids,
+                                       ids, ids, 8, None) == L.MC_EINVAL        # NULL tables
+    buf = (C.c_int64 * 64)()
+    c.slot_of = c.id_of = c.stamp = c.clock = c.stats = C.cast(buf, C.c_void_p)
+    assert lib.slot_cache_lookup_evict(C.byref(c), 2, ids, 4, 2, None, 65536, 1, 1, ids, ids, ids, ids,
+                                       ids, ids, 8, None) == L.MC_EINVAL        # layer out of range
+    assert lib.slot_cache_lookup_evict(C.byref(c), 0, ids, 4, 2, None, 65537, 1, 1, ids, ids, ids, ids,
+                                       ids, ids, 8, None) == L.MC_EINVAL        # frac > 1
+    assert lib.slot_cache_lookup_evict(C.byref(c), 0, ids, 4, 2, None, 65536, 1, 1, ids, ids, ids, ids,
+                                       ids, ids, 7, None) == L.MC_EINVAL        # kcap < T*k
+    assert "kcap" in L.last_error()
+    # bank checks
+    b = L.Banks()
+    b.fmt, b.H, b.I, b.n = L.MC_MXFP4, 100, 64, 4
+    assert lib.moe_experts_decode(ids, ids, w, 1, 2, None, C.byref(b), None, ids, 0, w, None) == L.MC_EINVAL
+    assert "multiples of 64" in L.last_error()
+    b.H = 64
+    assert lib.moe_experts_decode(ids, ids, w, 1, 2, None, C.byref(b), None, ids, 0, w, None) == L.MC_EINVAL
+    assert lib.mc_host_pool_create(0, None) is None
+
+
+def test_host_pool_lifecycle():
+    from expert_cache_offloaded_amd import HostPool
+    for n in (1, 2, 5):
+        p = HostPool(n)
+        p.close()

@@ -1,0 +1,228 @@
+"""GPU parity: fills, moe_experts_decode, hybrid split/merge and whole decode steps."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import LruOracle, decode_layer, hybrid_partials
+from gpu_helpers import (assert_bf16_close, device_banks, empty_device_banks, pinned_banks, rel_l2,
+                         t_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def _desc(cfg, t):
+    from expert_cache_offloaded_amd import make_banks
+    return make_banks(cfg.fmt, cfg.H, cfg.I, t)
+
+
+def _resident_case(cfg, T, n_slots, host_frac, seed, shared=False, layer=1, nt=None):
+    """Routes of one layer call with their experts placed at random slots of a device pool.
+
+    A fraction of the routes is marked host-side (slot -1).  Unused slots hold other
+    experts so a wrong slot read cannot go unnoticed.
+    """
+    r = np.random.default_rng(seed)
+    ids = np.stack([r.choice(cfg.E, cfg.k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = r.random((T, cfg.k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    flats = sorted({layer * cfg.E + int(e) for e in ids.ravel()})
+    assert len(flats) <= n_slots
+    slot_perm = r.permutation(n_slots)
+    slot_of = {f: int(slot_perm[i]) for i, f in enumerate(flats)}
+    fillers = [f for f in range(cfg.n_flat) if f not in slot_of][: n_slots - len(flats)]
+    entry_flat = [None] * n_slots
+    for f, s in slot_of.items():
+        entry_flat[s] = f
+    for s in range(n_slots):
+        if entry_flat[s] is None:
+            entry_flat[s] = fillers.pop()
+    banks = synth.host_pool(cfg, entry_flat)               # entry s = expert entry_flat[s]
+    slots = np.array([[slot_of[layer * cfg.E + int(e)] for e in row] for row in ids], dtype=np.int32)
+    slots[r.random(slots.shape) < host_frac] = -1
+    x = synth.activations(cfg, seed, T=T)
+    sh = synth.shared_pool(cfg) if shared else None
+    index_of = {f: i for i, f in enumerate(entry_flat)}.__getitem__
+    y_gpu_ref, _, _, _ = hybrid_partials(x, ids, slots, w, banks, layer, cfg.E, cfg.fmt, cfg.H, cfg.I,
+                                         n_tok=nt, index_of=index_of)
+    if sh is not None:
+        from oracle import bf16_to_f64, expert_ffn, expert_matrices
+        wg, wu, wd = expert_matrices(sh, layer, cfg.fmt, cfg.H, cfg.I)
+        n = T if nt is None else nt
+        y_gpu_ref[:n] += expert_ffn(wg, wu, wd, bf16_to_f64(x[:n]))
+    return dict(ids=ids, w=w, slots=slots, x=x, banks=banks, shared=sh, ref=y_gpu_ref, layer=layer)
+
+
+def _run_decode(cfg, case, nt=None):
+    from expert_cache_offloaded_amd import decode_ws_bytes, finish_bf16, moe_experts_decode
+    T = case["ids"].shape[0]
+    pool_t = device_banks(case["banks"])
+    pool = _desc(cfg, pool_t)
+    sh = None
+    if case["shared"] is not None:
+        sh_t = {k: t_of(v[case["layer"]:case["layer"] + 1]).cuda() for k, v in case["shared"].items()}
+        sh = _desc(cfg, sh_t)
+    x = t_of(case["x"]).cuda()
+    slots = torch.from_numpy(case["slots"]).cuda()
+    w = torch.from_numpy(case["w"]).cuda()
+    ws = torch.empty(decode_ws_bytes(T, cfg.k, cfg.I) // 4, dtype=torch.float32, device="cuda")
+    y = torch.zeros((T, cfg.H), dtype=torch.float32, device="cuda")
+    ntt = None
+    if nt is not None:
+        ntt = torch.tensor([nt], dtype=torch.int32, device="cuda")
+    moe_experts_decode(x, slots, w, ntt, pool, sh, ws, y)
+    yb = torch.empty((T, cfg.H), dtype=torch.int16, device="cuda")
+    finish_bf16(y, ntt, yb)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), yb
+
+
+CASES = [
+    # name, config, T, slots, host fraction, shared
+    ("tiny-bf16", "tiny", 4, 8, 0.25, False),
+    ("qwen-mxfp4-bs1", "qwen_decode", 1, 24, 0.0, True),
+    ("qwen-mxfp4-bs1-split", "qwen_decode", 1, 24, 0.4, True),
+    ("zipf-mxfp4-bs4", "zipf_decode", 4, 40, 0.1, False),
+    ("zipf-mxfp4-bs16", "zipf_decode", 16, 130, 0.1, False),
+    ("dsv4-mxfp4-bs1", "dsv4_hybrid", 1, 8, 0.3, False),
+]
+
+
+@pytest.mark.parametrize("name,cname,T,n_slots,hf,shared", CASES)
+def test_decode_matches_oracle(name, cname, T, n_slots, hf, shared):
+    cfg = synth.CONFIGS[cname].with_(L=2)
+    case = _resident_case(cfg, T, n_slots, hf, seed=zlib.crc32(name.encode()) % 1000, shared=shared)
+    y, yb = _run_decode(cfg, case)
+    assert rel_l2(y, case["ref"]) <= 1e-4, name              # fp32 partial (diagnostic bar)
+    assert_bf16_close(yb, case["ref"], name)                  # bf16 output bar
+
+
+def test_decode_valid_count_and_empty():
+    cfg = synth.CONFIGS["zipf_decode"].with_(L=2)
+    for nt in (0, 5, 16):
+        case = _resident_case(cfg, 16, 130, 0.0, seed=7, nt=nt)
+        y, yb = _run_decode(cfg, case, nt=nt)
+        assert np.all(y[nt:] == 0)
+        if nt:
+            assert rel_l2(y[:nt], case["ref"][:nt]) <= 1e-4
+            assert_bf16_close(yb[:nt], case["ref"][:nt])
+        assert torch.all(yb[nt:] == 0)
+
+
+def test_fill_copies_every_bank():
+    from expert_cache_offloaded_amd import fill_slots
+    for cname in ("tiny", "qwen_decode"):
+        cfg = synth.CONFIGS[cname].with_(L=1, E=24) if cname == "qwen_decode" else synth.CONFIGS[cname]
+        host_np = synth.host_pool(cfg)
+        host_t = pinned_banks(cfg, host_np)
+        host = _desc(cfg, host_t)
+        S = 6
+        pool_t = empty_device_banks(cfg, S)
+        for v in pool_t.values():
+            v.fill_(0)
+        pool = _desc(cfg, pool_t)
+        flats = [3, 0, cfg.n_flat - 1, 5]
+        slots = [4, 1, 0, 5]
+        n = 3                                   # the 4th entry is beyond n_fill and must not move
+        ff = torch.tensor(flats, dtype=torch.int32, device="cuda")
+        fs = torch.tensor(slots, dtype=torch.int32, device="cuda")
+        nf = torch.tensor([n], dtype=torch.int32, device="cuda")
+        fill_slots(host, pool, ff, fs, nf)
+        torch.cuda.synchronize()
+        for name, arr in pool_t.items():
+            got = arr.cpu()
+            for i in range(4):
+                want = t_of(host_np[name][flats[i]]) if i < n else torch.zeros_like(got[slots[i]])
+                assert torch.equal(got[slots[i]], want), (cname, name, i)
+            for s in (2, 3):
+                assert torch.all(got[s] == 0)
+
+
+def _step_oracle(cfg, o, layer, ids, w, x, banks, frac, shared=None):
+    res = o.lookup(layer, ids, frac, 1, 1)
+    y = decode_layer(x, ids, w, banks, layer, cfg.E, cfg.fmt, cfg.H, cfg.I, shared=shared)
+    return res, y
+
+
+@pytest.mark.parametrize("frac", [1 << 16, 1 << 15])
+def test_tiny_trace_end_to_end(frac):
+    """The tiny config through route -> lookup -> split -> fill -> experts -> merge, every step
+    (4 slots for up to 8 unique experts: overflow misses run on the host branch)."""
+    from expert_cache_offloaded_amd import HostPool
+    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer
+    from oracle import route
+    cfg = synth.CONFIGS["tiny"]
+    tr = synth.trace(cfg)
+    host_np = synth.host_pool(cfg)
+    host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(empty_device_banks(cfg, cfg.S), cfg.H, cfg.I, cfg.fmt)
+    cs = CacheState(cfg.L, cfg.E, cfg.S)
+    cs.reset()
+    hp = HostPool(2)
+    dl = DecodeLayer(cs, host, pool, None, DecodeBuffers(cfg.T, cfg.k, cfg.H, cfg.I), frac_q16=frac,
+                     hybrid=True, host_pool=hp)
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    x_dev = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda")
+    for s in range(cfg.steps):
+        lg = synth.step_logits(cfg, tr[s], s)[0]
+        x = synth.activations(cfg, s)
+        x_dev.copy_(t_of(x))
+        y = dl(0, torch.from_numpy(lg).cuda(), x_dev)
+        torch.cuda.synchronize()
+        ids, w = route(lg, cfg.k)
+        res, yref = _step_oracle(cfg, o, 0, ids, w, x, host_np, frac)
+        assert np.array_equal(dl.b.slots.cpu().numpy(), res["slots"]), s
+        assert_bf16_close(y, yref, "step %d" % s)
+    st = cs.state()
+    assert np.array_equal(st["stats"], o.stats) and np.array_equal(st["slot_of"], o.slot_of)
+    # every slot equals its host bank (a fill never corrupts a resident expert)
+    for sl in range(cfg.S):
+        f = int(st["id_of"][sl])
+        if f >= 0:
+            for name, arr in pool.t.items():
+                assert torch.equal(arr[sl].cpu(), t_of(host_np[name][f]))
+    hp.close()
+
+
+@pytest.mark.parametrize("ratio,p", [(2.0, 0.5), (3.0, 0.9)])
+def test_dsv4_shaped_hybrid_steps(ratio, p):
+    """DeepSeek-V4-Flash expert shapes (H 4096, I 2048, MXFP4, top-6) on a reduced pool of
+    E=16 experts x 3 layers, split by q* with B_H/B_P = ratio; y against the unsplit layer."""
+    from expert_cache_offloaded_amd import HostPool, fetch_fraction_q16
+    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer
+    from oracle import route
+    cfg = synth.CONFIGS["dsv4_hybrid"].with_(L=3, E=16, S=10, steps=2, p=p)
+    tr = synth.trace(cfg)
+    host_np = synth.host_pool(cfg)
+    host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(empty_device_banks(cfg, cfg.S), cfg.H, cfg.I, cfg.fmt)
+    cs = CacheState(cfg.L, cfg.E, cfg.S)
+    cs.reset()
+    frac = fetch_fraction_q16(1.0, ratio)
+    hp = HostPool(4)
+    dl = DecodeLayer(cs, host, pool, None, DecodeBuffers(1, cfg.k, cfg.H, cfg.I), frac_q16=frac,
+                     hybrid=True, host_pool=hp)
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    x_dev = torch.empty((1, cfg.H), dtype=torch.int16, device="cuda")
+    for s in range(cfg.steps):
+        lgs = synth.step_logits(cfg, tr[s], s)
+        for l in range(cfg.L):
+            x = synth.activations(cfg, s, l)
+            x_dev.copy_(t_of(x))
+            y = dl(l, torch.from_numpy(lgs[l]).cuda(), x_dev)
+            torch.cuda.synchronize()
+            ids, w = route(lgs[l], cfg.k)
+            res = o.lookup(l, ids, frac, 1, 1)
+            assert np.array_equal(dl.b.slots.cpu().numpy(), res["slots"])
+            n_host = int(dl.b.n_host.item())
+            assert n_host == len(res["host"])
+            # the two partials (their sum is the unsplit layer, pinned in the oracle tests)
+            yg, yh, _, _ = hybrid_partials(x, ids, res["slots"], w, host_np, l, cfg.E, cfg.fmt, cfg.H, cfg.I)
+            assert_bf16_close(y, yg + yh, "step %d layer %d" % (s, l))
+            assert rel_l2(dl.b.y_acc.cpu().numpy(), yg) <= 1e-4
+            if n_host:
+                assert rel_l2(dl.b.y_host.cpu().numpy(), yh) <= 1e-4
+    assert o.stats[3] > 0          # some misses did run on the host
+    hp.close()

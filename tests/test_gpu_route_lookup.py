@@ -1,0 +1,160 @@
+"""GPU parity: moe_route and slot_cache_lookup_evict against the oracle (bit-exact ints)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import LruOracle, route
+
+pytestmark = pytest.mark.gpu
+
+
+def _route_gpu(lg, k, renorm):
+    from expert_cache_offloaded_amd import moe_route
+    T = lg.shape[0]
+    d = torch.from_numpy(np.ascontiguousarray(lg, dtype=np.float32)).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe_route(d, k, renorm, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_route_trace_logits(renorm):
+    for name in ("tiny", "qwen_decode", "zipf_decode"):
+        cfg = synth.CONFIGS[name].with_(steps=3, T=4 if name != "qwen_decode" else 1)
+        tr = synth.trace(cfg)
+        for s in range(cfg.steps):
+            lg = synth.step_logits(cfg, tr[s], s).reshape(-1, cfg.E)
+            ids, w = _route_gpu(lg, cfg.k, renorm)
+            rid, rw = route(lg, cfg.k, renorm)
+            assert np.array_equal(ids, rid), name
+            assert np.max(np.abs(w - rw) / np.maximum(rw, 1e-30)) < (2e-6 if renorm else 1e-5)
+
+
+def test_route_prefill_and_edges():
+    cfg = synth.CONFIGS["prefill"]
+    lg = synth.uniform_logits(cfg)
+    for renorm in (0, 1):
+        ids, w = _route_gpu(lg, cfg.k, renorm)
+        rid, rw = route(lg, cfg.k, renorm)
+        assert np.array_equal(ids, rid)
+        assert np.max(np.abs(w - rw)) < 2e-6
+    r = np.random.default_rng(9)
+    # ties, a single expert, the largest E, k = 32, a ragged T
+    cases = [np.zeros((3, 16), np.float32),
+             np.round(r.standard_normal((37, 64)) * 2).astype(np.float32),
+             r.standard_normal((5, 1)).astype(np.float32),
+             r.standard_normal((7, 1024)).astype(np.float32)]
+    for lg, k in zip(cases, (4, 8, 1, 32)):
+        ids, w = _route_gpu(lg, k, 1)
+        rid, rw = route(lg, k, 1)
+        assert np.array_equal(ids, rid)
+        assert np.max(np.abs(w - rw)) < 2e-6
+
+
+class GpuLookup:
+    def __init__(self, L_, E, S, T, k):
+        from expert_cache_offloaded_amd.runtime import CacheState
+        self.cs = CacheState(L_, E, S)
+        self.cs.reset()
+        self.T, self.k = T, k
+        i32 = dict(dtype=torch.int32, device="cuda")
+        self.ids = torch.empty((T, k), **i32)
+        self.slots = torch.empty((T, k), **i32)
+        self.ff = torch.empty(T * k, **i32)
+        self.fs = torch.empty(T * k, **i32)
+        self.nf = torch.empty(1, **i32)
+        self.hf = torch.empty(T * k, **i32)
+        self.nh = torch.empty(1, **i32)
+        self.ntok = torch.empty(1, **i32)
+
+    def __call__(self, layer, ids, frac, cap=1, min_fill=1, n_tok=None):
+        from expert_cache_offloaded_amd import slot_cache_lookup_evict
+        self.ids.copy_(torch.from_numpy(ids))
+        nt = None
+        if n_tok is not None:
+            self.ntok.fill_(n_tok)
+            nt = self.ntok
+        slot_cache_lookup_evict(self.cs.desc, layer, self.ids, nt, frac, cap, min_fill, self.slots,
+                                self.ff, self.fs, self.nf, self.hf, self.nh)
+        torch.cuda.synchronize()
+        nf, nh = int(self.nf.item()), int(self.nh.item())
+        return {"slots": self.slots.cpu().numpy(),
+                "fills": list(zip(self.ff[:nf].cpu().tolist(), self.fs[:nf].cpu().tolist())),
+                "host": self.hf[:nh].cpu().tolist()}
+
+
+def _compare_state(g, o):
+    st = g.cs.state()
+    assert np.array_equal(st["slot_of"], o.slot_of)
+    assert np.array_equal(st["id_of"], o.id_of)
+    assert np.array_equal(st["stamp"], o.stamp)
+    assert int(st["clock"][0]) == o.clock
+    assert np.array_equal(st["stats"], o.stats)
+
+
+@pytest.mark.parametrize("frac,cap", [(1 << 16, 1), (1 << 15, 1), (0, 1), (21845, 1), (1, 1)])
+def test_lookup_tiny_trace(frac, cap):
+    cfg = synth.CONFIGS["tiny"]
+    tr = synth.trace(cfg)
+    g = GpuLookup(cfg.L, cfg.E, cfg.S, cfg.T, cfg.k)
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    for s in range(cfg.steps):
+        ids = tr[s, 0]
+        a = g(0, ids, frac, cap)
+        b = o.lookup(0, ids, frac, cap, 1)
+        assert np.array_equal(a["slots"], b["slots"]), s
+        assert a["fills"] == b["fills"], s
+        assert a["host"] == b["host"], s
+        _compare_state(g, o)
+
+
+def test_lookup_qwen_shaped_trace():
+    cfg = synth.CONFIGS["qwen_decode"].with_(steps=40)
+    tr = synth.trace(cfg)
+    g = GpuLookup(cfg.L, cfg.E, cfg.S, 1, cfg.k)
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    n = 0
+    for s in range(cfg.steps):
+        for l in range(cfg.L):
+            a = g(l, tr[s, l], 1 << 16)
+            b = o.lookup(l, tr[s, l], 1 << 16)
+            assert np.array_equal(a["slots"], b["slots"])
+            assert a["fills"] == b["fills"] and a["host"] == b["host"]
+            n += 1
+            if n % 64 == 0:
+                _compare_state(g, o)
+    _compare_state(g, o)
+    assert o.stats[4] > 0          # the pool wrapped: evictions happened
+
+
+@pytest.mark.parametrize("S", [256, 1024])
+def test_lookup_zipf_batched_valid_count(S):
+    cfg = synth.CONFIGS["zipf_decode"].with_(L=6, steps=12, T=16, S=S)
+    tr = synth.trace(cfg)
+    g = GpuLookup(cfg.L, cfg.E, cfg.S, cfg.T, cfg.k)
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    r = np.random.default_rng(1)
+    for s in range(cfg.steps):
+        for l in range(cfg.L):
+            nt = int(r.integers(0, cfg.T + 1))
+            a = g(l, tr[s, l], 1 << 16, n_tok=nt)
+            b = o.lookup(l, tr[s, l], 1 << 16, n_tok=nt)
+            assert np.array_equal(a["slots"], b["slots"])
+            assert a["fills"] == b["fills"] and a["host"] == b["host"]
+        _compare_state(g, o)
+
+
+def test_lookup_invalid_ids_and_masks():
+    g = GpuLookup(2, 8, 3, 3, 2)
+    o = LruOracle(2, 8, 3)
+    ids = np.array([[0, -1], [9, 3], [-7, 5]], dtype=np.int32)     # -1 masked, 9 and -7 invalid
+    for layer in (1, 0, 1):
+        a = g(layer, ids, 1 << 16)
+        b = o.lookup(layer, ids, 1 << 16)
+        assert np.array_equal(a["slots"], b["slots"])
+        assert a["fills"] == b["fills"] and a["host"] == b["host"]
+        _compare_state(g, o)
+    assert o.stats[6] == 6
