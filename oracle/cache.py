@@ -101,7 +101,13 @@ def fetch_fraction(b_p: float, b_h: float, p_ov: float = 0.0, c_ov: float = 0.0)
 
 
 def fetch_fraction_q16(b_p: float, b_h: float, p_ov: float = 0.0, c_ov: float = 0.0) -> int:
-    """Q16 form of ``fetch_fraction``: round half up, clamped to [1, 65536]."""
+    """Q16 form of ``fetch_fraction``: round half up, clamped to [1, 65536].
+
+    With no usable measurement (p_ov <= 0 and B_P <= 0) it returns 0, the fixed-cap
+    mode ([wanger] "1. 启动时": no profile -> a fixed fetch cap).
+    """
+    if p_ov <= 0 and b_p <= 0:
+        return 0
     f = fetch_fraction(b_p, b_h, p_ov, c_ov)
     v = (f * Q16 + Fraction(1, 2)).__floor__()
     return int(min(max(v, 1), Q16))
