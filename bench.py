@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE layer over the cross-layer LRU slot cache on one MI355X.
+
+Workload (default): Qwen3.6-35B-A3B-shaped decode — 40 MoE layers, 256 routed experts
+top-8 plus one shared expert, hidden 2048, expert intermediate 512, MXFP4 experts,
+bf16 activations, batch 1, cross-layer LRU pool of 600 of the 10240 (layer, expert)
+slots, routing locality p = 0.8, seeded synthetic weights / trace / activations.
+
+A step is one decode token through all 40 layers: per layer moe_route ->
+slot_cache_lookup_evict -> mc_fill_slots (misses from pinned host memory over the
+host link) -> moe_experts_decode -> mc_finish_bf16, all captured in one hipGraph.
+Inputs (router logits, activations, the pinned host expert pool) are resident
+before the timed region starts; the fills are part of the path.
+
+Printed: one JSON line (value = decode tokens/s).  ``roofline`` is for the expert
+GEMV (moe_experts_decode), timed with HIP events on its own stream over graph
+replays of the same calls the steps make; ``cpu_baseline`` times the CPU oracle on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE-layer decode tok/s (bs=1) + prefill tok/s at 8k; HBM GB/s & MFMA % peak"
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--cpu-tokens", type=int, default=1, help="decode tokens in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=5)
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def build_host_pool(cfg, torch):
+    """Pinned host expert pool indexed by flat id (the host truth)."""
+    import synth
+    from expert_cache_offloaded_amd.runtime import alloc_banks
+    banks = alloc_banks(cfg.n_flat, cfg.H, cfg.I, cfg.fmt, pin=True)
+    views = {k: v.numpy() for k, v in banks.items()}
+    t0 = time.time()
+
+    def one(f):
+        for k, a in synth.expert_weights(cfg, f).items():
+            views[k][f] = a if a.dtype != np.uint16 else a.view(np.int16)
+        if f % 2048 == 0:
+            log("host pool %d/%d experts (%.0f s)" % (f, cfg.n_flat, time.time() - t0))
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        list(ex.map(one, range(cfg.n_flat)))
+    log("host pool ready (%.0f s)" % (time.time() - t0))
+    return banks, views
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures a single GPU: the method runs on one GPU (its expert pool, slot "
+              "cache and host link); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from expert_cache_offloaded_amd import _lib as L
+    from expert_cache_offloaded_amd.runtime import (BankSet, CacheState, DecodeBuffers, DecodeLayer,
+                                                   alloc_banks)
+
+    L.lib()   # fails loudly if the library is not built
+    cfg = synth.CONFIGS["qwen_decode"]
+    W, K = args.warmup, args.steps
+    n_steps = W + K
+    dev = "cuda"
+
+    # ------------------------------------------------------------------ inputs
+    log("trace / logits / activations for %d steps" % n_steps)
+    tr = synth.trace(cfg, steps=n_steps)
+    logits = np.stack([synth.step_logits(cfg, tr[s], s) for s in range(n_steps)])     # [S, L, 1, E]
+    xs = np.stack([np.stack([synth.activations(cfg, s, l) for l in range(cfg.L)]) for s in range(n_steps)])
+    logits_all = torch.from_numpy(logits).to(dev)
+    x_all = torch.from_numpy(xs.view(np.int16)).to(dev)
+    log("host pool: %d experts x %d B pinned" % (cfg.n_flat, synth.expert_bytes(cfg.H, cfg.I, cfg.fmt)))
+    host_t, host_np = build_host_pool(cfg, torch)
+    host = BankSet(host_t, cfg.H, cfg.I, cfg.fmt)
+    sh_np = synth.shared_pool(cfg)
+    shared = BankSet({k: torch.from_numpy(v if v.dtype != np.uint16 else v.view(np.int16)).to(dev)
+                      for k, v in sh_np.items()}, cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(alloc_banks(cfg.S, cfg.H, cfg.I, cfg.fmt, device=dev), cfg.H, cfg.I, cfg.fmt)
+    cache = CacheState(cfg.L, cfg.E, cfg.S)
+    cache.reset()
+    layers = [DecodeLayer(cache, host, pool, shared, DecodeBuffers(1, cfg.k, cfg.H, cfg.I),
+                          frac_q16=1 << 16, renorm=cfg.renorm) for _ in range(cfg.L)]
+    logits_buf = torch.empty_like(logits_all[0])
+    x_buf = torch.empty_like(x_all[0])
+
+    def step():
+        for l in range(cfg.L):
+            layers[l](l, logits_buf[l], x_buf[l])
+
+    # ------------------------------------------------------------------ warmup + capture
+    log("warmup (%d steps) and graph capture" % W)
+    logits_buf.copy_(logits_all[0])
+    x_buf.copy_(x_all[0])
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for s in range(1, W):
+        logits_buf.copy_(logits_all[s])
+        x_buf.copy_(x_all[s])
+        g.replay()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ timed region
+    stats0 = cache.t["stats"].cpu().numpy().copy()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(W, n_steps):
+        logits_buf.copy_(logits_all[s])
+        x_buf.copy_(x_all[s])
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    stats1 = cache.t["stats"].cpu().numpy().copy()
+    d = stats1 - stats0
+    ms_per_step = ms_total / K
+    tok_s = 1000.0 / ms_per_step
+    S_e = synth.expert_bytes(cfg.H, cfg.I, cfg.fmt)
+    miss_rate = float(d[1]) / max(1.0, float(d[0] + d[1]))
+    link_gbs = float(d[2]) * S_e / (ms_total * 1e-3) / 1e9
+    log("decode: %.3f ms/token, %.1f tok/s, miss rate %.3f, %.1f fills/token, link %.1f GB/s"
+        % (ms_per_step, tok_s, miss_rate, d[2] / K, link_gbs))
+
+    # ------------------------------------------------------------------ expert GEMV timing
+    # the same moe_experts_decode calls as the last step (all routes resident), replayed
+    # back to back in a graph; HIP events on the replay stream.
+    reps = args.kernel_reps
+    ys = [torch.zeros((1, cfg.H), dtype=torch.float32, device=dev) for _ in range(cfg.L)]
+    gk = torch.cuda.CUDAGraph()
+    sh_descs = [shared.entry(l).desc for l in range(cfg.L)]
+    with torch.cuda.graph(gk):
+        for _ in range(reps):
+            for l in range(cfg.L):
+                b = layers[l].b
+                L.moe_experts_decode(x_buf[l], b.slots, b.w, None, pool.desc, sh_descs[l], b.ws, ys[l],
+                                     accumulate=1)
+    gk.replay()
+    torch.cuda.synchronize()
+    times = []
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gk.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    us_per_call = 1000.0 * float(np.median(times)) / (reps * cfg.L)
+    units = []
+    for l in range(cfg.L):
+        sl = layers[l].b.slots.cpu().numpy().ravel()
+        units.append(len(set(int(v) for v in sl if v >= 0)) + 1)       # + shared expert
+    bytes_per_call = float(np.mean(units)) * S_e
+    achieved = bytes_per_call / (us_per_call * 1e-6) / 1e9
+    log("expert GEMV: %.2f us/call, %.2f MB/call, %.0f GB/s" % (us_per_call, bytes_per_call / 1e6, achieved))
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "qwen3.6-35b-a3b-shaped decode: 40 MoE layers, E=256 top-8 + 1 shared, "
+                               "H=2048, I=512, MXFP4 experts, bf16 activations, bs=1, LRU pool 600 of "
+                               "10240 slots, locality p=0.8",
+                   "global_batch": 1, "layers": cfg.L, "slots": cfg.S, "locality": cfg.p},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moe_experts_decode", "bytes_per_launch": int(bytes_per_call),
+                     "us_per_launch": round(us_per_call, 3)},
+        "decode": {"miss_rate": round(miss_rate, 4), "fills_per_token": round(float(d[2]) / K, 2),
+                   "host_routes": int(d[3]), "link_gbs": round(link_gbs, 2),
+                   "expert_gemv_us_per_token": round(us_per_call * cfg.L, 2),
+                   "wall_s": round(wall, 3)},
+    }
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, tr, logits, xs, host_np, sh_np, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, tr, logits, xs, host_np, sh_np, n_tokens):
+    """The oracle (as it stands) on the host cores: route + LRU + split + per-token expert sum."""
+    from oracle import LruOracle, decode_layer, route
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    host = {k: (v.view(np.uint16) if v.dtype == np.int16 else v) for k, v in host_np.items()}
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    log("cpu baseline: oracle on %d token(s) x %d layers" % (n_tokens, cfg.L))
+    t0 = time.perf_counter()
+    for s in range(n_tokens):
+        for l in range(cfg.L):
+            ids, w = route(logits[s, l], cfg.k, cfg.renorm)
+            o.lookup(l, ids, 1 << 16)
+            decode_layer(xs[s, l], ids, w, host, l, cfg.E, cfg.fmt, cfg.H, cfg.I, shared=sh_np)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": "%d decode token(s) x %d layers of the same workload (route, LRU lookup, split, "
+                      "unsplit per-token expert sum in float64)" % (n_tokens, cfg.L),
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -61,7 +61,7 @@ _SIGS = {
     "mc_fill_slots": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, _P]),
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
-                                     _P, C.c_size_t, _P, _P]),
+                                     _P, C.c_size_t, _P, _I32, _P, _P]),
     "mc_host_pool_create": (_P, [_I32, _P]),
     "mc_host_pool_destroy": (None, [_P]),
     "mc_host_experts": (C.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, C.POINTER(Banks), _P]),
@@ -179,12 +179,13 @@ def decode_ws_bytes(T: int, k: int, I: int) -> int:
 
 
 def moe_experts_decode(x, slots, w, n_tok, pool: Banks, shared: Optional[Banks], ws, y_acc,
-                       stream=None) -> None:
+                       accumulate: int = 1, y_bf16=None, stream=None) -> None:
     T, k = slots.shape
     _check("moe_experts_decode", lib().moe_experts_decode(
         _ptr(x), _ptr(slots), _ptr(w), T, k, _ptr(n_tok), C.byref(pool),
         C.byref(shared) if shared is not None else None, _ptr(ws), ws.numel() * ws.element_size(),
-        _ptr(y_acc), _stream(stream)))
+        _ptr(y_acc), accumulate, _ptr(y_bf16), _stream(stream)))
+
 
 
 def finish_bf16(y_acc, n_tok, y_bf16, stream=None) -> None:

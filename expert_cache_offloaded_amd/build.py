@@ -33,7 +33,8 @@ def _compile(src: str) -> str:
     if src.endswith(".hip"):
         cmd = [HIPCC, "-x", "hip"] + COMMON + DEVICE + ["-c", src, "-o", obj]
     else:
-        cmd = [HIPCC] + COMMON + ["-pthread", "-c", src, "-o", obj]
+        cmd = [HIPCC, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"] + COMMON + [
+            "-pthread", "-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), r.stdout))

@@ -6,28 +6,32 @@
 // with slot -1 (or gate 0) and are skipped.
 //
 // Decode is a GEMV that streams ~0.53 B of MXFP4 weight per multiply-add, so it is
-// bound by HBM bandwidth.  Two kernels:
-//   A. gate_up + SwiGLU.  Workgroup = (unit, 16 intermediate rows); a unit is one
-//      distinct slot of the call (first-occurrence order) or the shared expert.  Each
-//      wave owns 4 gate rows and the 4 matching up rows; lane l reads the 16-byte
-//      chunks l, l+64, ... of every row (one coalesced 1 KiB row slice per load
-//      instruction), keeps them in registers and reuses them for every token that
-//      routes to the unit.  Dot products run on packed bf16 (MXFP4 -> bf16 is exact)
-//      with fp32 accumulation; h = silu(g) * u is written in fp32 per route.
-//   B. down + combine.  Workgroup = 8 hidden rows for every route of every token, so
-//      each output element is produced by exactly one lane group and written once
-//      (deterministic, no atomics).  A token's route vectors h (fp32) are staged in
-//      LDS; lanes split a row's contraction into 16-byte chunks and reduce across
-//      the row's lanes at the end.
+// bound by HBM bandwidth; at batch 1 a layer moves only ~15 MB, so what matters is
+// having every weight load of a wave in flight at once (no branch or conversion
+// between a load and the next one).  Two kernels, no cross-workgroup waiting:
+//   gate_up: workgroup = (unit, 16 intermediate rows); a unit is one distinct slot of
+//      the call (first-occurrence order) or the shared expert.  Each wave owns 4 gate
+//      rows and the 4 matching up rows; lane l reads the 16-byte chunks l, l+64, ...
+//      of every row (one coalesced 1 KiB row slice per load instruction), keeps them
+//      in registers and reuses them for every token that routes to the unit.  Dot
+//      products run on packed bf16 (MXFP4 -> bf16 is exact) with fp32 accumulation;
+//      h = silu(g) * u is written in fp32 per route.
+//   down: workgroup = 8 hidden rows for every route of a token.  The token's h
+//      vectors are staged in LDS; each wave takes every fourth route, loads all of
+//      its rows first, then computes; the waves' partial sums meet in LDS and are
+//      added in a fixed order, so every output element is written once (no atomics,
+//      run-to-run identical).  The same pass writes the bf16 output when asked.
 #include "mc_common.h"
 
 namespace mc {
 
-constexpr int kA_Threads = 256;
-constexpr int kA_RowsI = 16;                 // intermediate rows per workgroup
+constexpr int kThreads = 256;
+constexpr int kA_RowsI = 16;                 // gate_up: intermediate rows per workgroup
 constexpr int kA_WaveRows = kA_RowsI / 4;    // per wave: 4 gate + 4 up rows
-constexpr int kB_Rows = 8;                   // hidden rows per workgroup (one wave)
+constexpr int kB_Rows = 8;                   // down: hidden rows per workgroup
+constexpr int kB_RoutesPerWave = 3;          // down: routes a wave holds in registers at once
 constexpr int kMaxRoutes = 1024;
+constexpr int kMaxTok = 64;
 constexpr int kB_LdsBytes = 64 * 1024;
 
 // ---------------------------------------------------------------- chunk dots
@@ -107,27 +111,32 @@ struct DecodeArgs {
   const uint8_t* sh_dns;
   float* h_route;             // [T*k][I]
   float* h_shared;            // [T][I]
-  float* y;                   // [T][H] accumulated
+  float* y;                   // [T][H]
+  uint16_t* y_bf16;           // [T][H] or null
+  int32_t accumulate;
+  int32_t has_shared;
 };
 
-// ---------------------------------------------------------------- kernel A
+__device__ __forceinline__ int valid_tokens(const DecodeArgs& a) {
+  return a.n_tok ? min(max(*a.n_tok, 0), a.T) : a.T;
+}
 
-// Unit table of the call, computed by every workgroup (at most kMaxRoutes routes):
-// s_first[u] = first route of the u-th distinct valid slot.
+__device__ __forceinline__ int pool_slot(const DecodeArgs& a, int r) {
+  const int s = a.slots[r];
+  return (s >= 0 && s < a.n_pool) ? s : -1;
+}
+
+// Unit table of the call (every gate_up workgroup builds it): s_slot[r] = slot of
+// route r or -1; s_first[u] = first route of the u-th distinct slot, in route order.
 __device__ int build_units(const DecodeArgs& a, int nr, int32_t* s_slot, int32_t* s_first,
                            int* s_cnt) {
   const int tid = threadIdx.x;
-  for (int r = tid; r < nr; r += blockDim.x) {
-    int s = a.slots[r];
-    s_slot[r] = (s >= 0 && s < a.n_pool) ? s : -1;
-  }
-  if (tid == 0) *s_cnt = 0;
+  for (int r = tid; r < nr; r += blockDim.x) s_slot[r] = pool_slot(a, r);
   __syncthreads();
-  // first occurrences, ranked in route order by a serial pass of wave 0 with ballots
   if (tid < 64) {
     int count = 0;
     for (int base = 0; base < nr; base += 64) {
-      int r = base + tid;
+      const int r = base + tid;
       bool first = false;
       if (r < nr && s_slot[r] >= 0) {
         first = true;
@@ -137,7 +146,7 @@ __device__ int build_units(const DecodeArgs& a, int nr, int32_t* s_slot, int32_t
             break;
           }
       }
-      uint64_t m = __ballot(first);
+      const uint64_t m = __ballot(first);
       if (first) s_first[count + __popcll(m & ((1ull << tid) - 1ull))] = r;
       count += __popcll(m);
     }
@@ -147,101 +156,101 @@ __device__ int build_units(const DecodeArgs& a, int nr, int32_t* s_slot, int32_t
   return *s_cnt;
 }
 
+// ---------------------------------------------------------------- gate_up kernel
+
 template <int FMT, int CPL>
-__global__ void __launch_bounds__(kA_Threads)
-gate_up_kernel(DecodeArgs a, int has_shared) {
+__global__ void __launch_bounds__(kThreads)
+gate_up_kernel(DecodeArgs a) {
   __shared__ int32_t s_slot[kMaxRoutes];
   __shared__ int32_t s_first[kMaxRoutes];
   __shared__ int s_cnt;
-  const int nt = a.n_tok ? min(max(*a.n_tok, 0), a.T) : a.T;
+  const int nt = valid_tokens(a);
   const int nr = nt * a.k;
   const int n_units = build_units(a, nr, s_slot, s_first, &s_cnt);
   const int u = blockIdx.x;
-  const bool shared_unit = has_shared && u == n_units;
-  if (u > n_units || (u == n_units && !shared_unit)) return;
-  if (shared_unit && nt == 0) return;
+  const bool shared_unit = a.has_shared && u == n_units;
+  if (u > n_units || (u == n_units && !shared_unit) || (shared_unit && nt == 0)) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
   const int i0 = blockIdx.y * kA_RowsI + wave * kA_WaveRows;   // first intermediate row
-  constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;              // elements per 16-B chunk
-  const int n_chunks = H / ELEMS;                              // chunks per row
+  constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;             // elements per 16-B chunk
+  const int n_chunks = H / ELEMS;
+  const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)H / 2 : (size_t)H * 2;
 
   const uint8_t* gu;
-  const uint8_t* gus;
+  const uint8_t* gus = nullptr;
   int slot = -1;
   if (shared_unit) {
     gu = a.sh_gu;
     gus = a.sh_gus;
   } else {
     slot = s_slot[s_first[u]];
-    const size_t per = FMT == MC_MXFP4 ? (size_t)2 * I * H / 2 : (size_t)2 * I * H * 2;
-    gu = a.gu + (size_t)slot * per;
-    gus = FMT == MC_MXFP4 ? a.gus + (size_t)slot * ((size_t)2 * I * H / 32) : nullptr;
+    gu = a.gu + (size_t)slot * (2 * (size_t)I * row_bytes);
+    if (FMT == MC_MXFP4) gus = a.gus + (size_t)slot * ((size_t)2 * I * H / 32);
   }
-  const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)H / 2 : (size_t)H * 2;
 
-  // weights of the wave's 8 rows: rows 0..3 gate i0.., rows 4..7 up I+i0..
+  // all loads of the wave's 8 rows first (chunk index clamped; out-of-row lanes are
+  // zeroed after the loads), scale bytes kept raw until every load is issued
+  int cq[CPL];
+  bool okq[CPL];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const int c = lane + 64 * q;
+    okq[q] = c < n_chunks;
+    cq[q] = okq[q] ? c : n_chunks - 1;
+  }
   uint4 wv[2 * kA_WaveRows][CPL];
-  float sc[2 * kA_WaveRows][CPL];
+  uint32_t sb[2 * kA_WaveRows][CPL];
 #pragma unroll
   for (int r = 0; r < 2 * kA_WaveRows; ++r) {
     const int row = r < kA_WaveRows ? i0 + r : I + i0 + (r - kA_WaveRows);
     const uint4* rp = reinterpret_cast<const uint4*>(gu + (size_t)row * row_bytes);
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      const int c = lane + 64 * q;
-      if (c < n_chunks) {
-        wv[r][q] = rp[c];
-        if (FMT == MC_MXFP4) sc[r][q] = e8m0_to_f32(gus[(size_t)row * (H / 32) + c]);
-      } else {
-        wv[r][q] = make_uint4(0, 0, 0, 0);
-        sc[r][q] = 0.0f;
-      }
+      wv[r][q] = rp[cq[q]];
+      if (FMT == MC_MXFP4) sb[r][q] = gus[(size_t)row * (H / 32) + cq[q]];
     }
   }
 
-  // tokens of this unit
   int r_next = shared_unit ? 0 : s_first[u];
   while (true) {
     int t, route;
     if (shared_unit) {
       if (r_next >= nt) break;
-      t = r_next;
+      t = r_next++;
       route = -1;
-      ++r_next;
     } else {
       while (r_next < nr && s_slot[r_next] != slot) ++r_next;
       if (r_next >= nr) break;
-      route = r_next;
+      route = r_next++;
       t = route / a.k;
-      ++r_next;
     }
     const uint32_t* xrow = reinterpret_cast<const uint32_t*>(a.x + (size_t)t * H);
-    float acc[2 * kA_WaveRows];
-#pragma unroll
-    for (int r = 0; r < 2 * kA_WaveRows; ++r) acc[r] = 0.0f;
+    uint32_t xp[CPL][ELEMS / 2];
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      const int c = lane + 64 * q;
-      if (c < n_chunks) {
-        uint32_t xp[ELEMS / 2];
-        const uint4* xs = reinterpret_cast<const uint4*>(xrow + (size_t)c * (ELEMS / 2));
+      const uint4* xs = reinterpret_cast<const uint4*>(xrow + (size_t)cq[q] * (ELEMS / 2));
 #pragma unroll
-        for (int v = 0; v < ELEMS / 8; ++v) {
-          uint4 xx = xs[v];
-          xp[4 * v + 0] = xx.x;
-          xp[4 * v + 1] = xx.y;
-          xp[4 * v + 2] = xx.z;
-          xp[4 * v + 3] = xx.w;
-        }
+      for (int v = 0; v < ELEMS / 8; ++v) {
+        const uint4 xx = xs[v];
+        xp[q][4 * v + 0] = xx.x;
+        xp[q][4 * v + 1] = xx.y;
+        xp[q][4 * v + 2] = xx.z;
+        xp[q][4 * v + 3] = xx.w;
+      }
+    }
+    float acc[2 * kA_WaveRows];
 #pragma unroll
-        for (int r = 0; r < 2 * kA_WaveRows; ++r) {
-          if (FMT == MC_MXFP4)
-            acc[r] = dot_chunk_mx(wv[r][q], sc[r][q], xp, acc[r]);
-          else
-            acc[r] = dot_chunk_bf(wv[r][q], xp, acc[r]);
-        }
+    for (int r = 0; r < 2 * kA_WaveRows; ++r) {
+      acc[r] = 0.0f;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const uint4 wq = okq[q] ? wv[r][q] : make_uint4(0, 0, 0, 0);
+        if (FMT == MC_MXFP4)
+          acc[r] = dot_chunk_mx(wq, e8m0_to_f32(sb[r][q]), xp[q], acc[r]);
+        else
+          acc[r] = dot_chunk_bf(wq, xp[q], acc[r]);
       }
     }
 #pragma unroll
@@ -260,108 +269,156 @@ gate_up_kernel(DecodeArgs a, int has_shared) {
   }
 }
 
-// ---------------------------------------------------------------- kernel B
+// ---------------------------------------------------------------- down kernel
 
 template <int FMT, int LPR, int CPLB>
-__global__ void __launch_bounds__(64)
-down_kernel(DecodeArgs a, int has_shared) {
-  extern __shared__ float s_h[];      // [(k + 1)][I] route vectors of one token
-  const int nt = a.n_tok ? min(max(*a.n_tok, 0), a.T) : a.T;
-  const int lane = threadIdx.x;
-  const int H = a.H, I = a.I, k = a.k;
+__global__ void __launch_bounds__(kThreads)
+down_kernel(DecodeArgs a) {
+  extern __shared__ float s_h[];                 // [k + 1][I]: one token's route vectors
+  __shared__ float s_part[4][kB_Rows];
+  __shared__ int32_t s_rslot[kMaxRoutes];        // slot of each route (-1 = none)
+  __shared__ float s_rgate[kMaxRoutes];
+  const int nt = valid_tokens(a);
+  for (int r = threadIdx.x; r < nt * a.k; r += kThreads) {
+    s_rslot[r] = pool_slot(a, r);
+    s_rgate[r] = a.w[r];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, k = a.k, T = a.T;
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;
-  constexpr int RPP = 64 / LPR;                      // rows per pass
+  constexpr int RPP = 64 / LPR;                              // rows per pass of a wave
   constexpr int PASSES = kB_Rows >= RPP ? kB_Rows / RPP : 1;
   const int n_chunks = I / ELEMS;
   const int row_sub = lane / LPR, c_lane = lane % LPR;
   const int r0 = blockIdx.x * kB_Rows;
+  const bool lane_rows = RPP <= kB_Rows || row_sub < kB_Rows;
   const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)I / 2 : (size_t)I * 2;
-  const size_t per = FMT == MC_MXFP4 ? (size_t)H * I / 2 : (size_t)H * I * 2;
+  const size_t per = (size_t)H * row_bytes;
   const size_t per_s = (size_t)H * I / 32;
-  const int nvec = k + (has_shared ? 1 : 0);
+  const int nvec = k + a.has_shared;                         // routes (+ shared) of a token
+
+  int cq[CPLB];
+  bool okq[CPLB];
+#pragma unroll
+  for (int q = 0; q < CPLB; ++q) {
+    const int c = c_lane + LPR * q;
+    okq[q] = c < n_chunks && lane_rows;
+    cq[q] = c < n_chunks ? c : n_chunks - 1;
+  }
+  int rowp[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) rowp[p] = min(r0 + row_sub + RPP * p, H - 1);
+
+  constexpr int kGroup = 4 * kB_RoutesPerWave;             // routes covered by one round
+  const int n_groups = (nvec + kGroup - 1) / kGroup;
+
+  uint4 wv[kB_RoutesPerWave][PASSES][CPLB];
+  uint32_t sb[kB_RoutesPerWave][PASSES][CPLB];
+  float gate[kB_RoutesPerWave];
+  // the wave's routes v0, v0+4, v0+8 of token t: gates and all row loads
+  auto load_group = [&](int t, int v0) {
+#pragma unroll
+    for (int j = 0; j < kB_RoutesPerWave; ++j) {
+      const int v = v0 + 4 * j;
+      const uint8_t* dn = a.dn;            // any readable address when there is nothing to read
+      const uint8_t* dns = a.dns;
+      gate[j] = 0.0f;
+      if (v < k) {
+        const int s = s_rslot[t * k + v];
+        if (s >= 0) {
+          dn = a.dn + (size_t)s * per;
+          if (FMT == MC_MXFP4) dns = a.dns + (size_t)s * per_s;
+          gate[j] = s_rgate[t * k + v];
+        }
+      } else if (v == k && a.has_shared) {
+        dn = a.sh_dn;
+        dns = a.sh_dns;
+        gate[j] = 1.0f;
+      }
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+        for (int q = 0; q < CPLB; ++q) {
+          wv[j][p][q] = reinterpret_cast<const uint4*>(dn + (size_t)rowp[p] * row_bytes)[cq[q]];
+          if (FMT == MC_MXFP4) sb[j][p][q] = dns[(size_t)rowp[p] * (I / 32) + cq[q]];
+        }
+    }
+  };
 
   for (int t = 0; t < nt; ++t) {
-    // stage h of this token's routes (and the shared expert) in LDS
-    __syncthreads();
-    for (int v = 0; v < nvec; ++v) {
+    if (t > 0) __syncthreads();              // previous token is done with s_h and s_part
+    // h of this token straight into LDS (global_load_lds, 1 KiB per wave instruction),
+    // then the first route group's rows: both sets of loads are in flight together
+    const int n4 = nvec * I / 4;
+    for (int ch = wave; ch * 64 < n4; ch += 4) {
+      int i4 = ch * 64 + lane;
+      if (i4 >= n4) i4 = n4 - 1;                       // tail lanes re-read a valid vector
+      const int v = (i4 * 4) / I, e = (i4 * 4) % I;
       const float* src = v < k ? a.h_route + ((size_t)t * k + v) * I : a.h_shared + (size_t)t * I;
-      bool valid = true;
-      if (v < k) {
-        int s = a.slots[(size_t)t * k + v];
-        valid = s >= 0 && s < a.n_pool;
-      }
-      if (!valid) continue;
-      for (int i = lane * 4; i < I; i += 64 * 4)
-        *reinterpret_cast<float4*>(s_h + (size_t)v * I + i) =
-            *reinterpret_cast<const float4*>(src + i);
+      __builtin_amdgcn_global_load_lds(src + e, (__attribute__((address_space(3))) void*)(s_h + ch * 256),
+                                       16, 0, 0);
     }
+    if (n_groups > 0) load_group(t, wave);
+    __builtin_amdgcn_s_waitcnt(0);                     // the LDS copies have landed
     __syncthreads();
 
     float acc[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) acc[p] = 0.0f;
-
-    for (int v = 0; v < nvec; ++v) {
-      const uint8_t* dn;
-      const uint8_t* dns;
-      float gate;
-      if (v < k) {
-        const int s = a.slots[(size_t)t * k + v];
-        if (s < 0 || s >= a.n_pool) continue;
-        gate = a.w[(size_t)t * k + v];
-        dn = a.dn + (size_t)s * per;
-        dns = FMT == MC_MXFP4 ? a.dns + (size_t)s * per_s : nullptr;
-      } else {
-        gate = 1.0f;
-        dn = a.sh_dn;
-        dns = a.sh_dns;
-      }
-      // issue all weight loads of this route first
-      uint4 wv[PASSES][CPLB];
-      float sc[PASSES][CPLB];
+    for (int g = 0; g < n_groups; ++g) {
+      const int v0 = wave + g * kGroup;
+      if (g > 0) load_group(t, v0);
 #pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        const int row = r0 + row_sub + RPP * p;
+      for (int j = 0; j < kB_RoutesPerWave; ++j) {
+        const int v = v0 + 4 * j;
+        if (v >= nvec || gate[j] == 0.0f) continue;
 #pragma unroll
         for (int q = 0; q < CPLB; ++q) {
-          const int c = c_lane + LPR * q;
-          if (row < H && c < n_chunks && (RPP <= kB_Rows || row_sub < kB_Rows)) {
-            wv[p][q] = reinterpret_cast<const uint4*>(dn + (size_t)row * row_bytes)[c];
-            if (FMT == MC_MXFP4) sc[p][q] = e8m0_to_f32(dns[(size_t)row * (I / 32) + c]);
-          } else {
-            wv[p][q] = make_uint4(0, 0, 0, 0);
-            sc[p][q] = 0.0f;
+          float hv[ELEMS];
+          const float4* hs = reinterpret_cast<const float4*>(s_h + (size_t)v * I + (size_t)cq[q] * ELEMS);
+#pragma unroll
+          for (int e = 0; e < ELEMS / 4; ++e) {
+            const float4 f = hs[e];
+            hv[4 * e + 0] = f.x;
+            hv[4 * e + 1] = f.y;
+            hv[4 * e + 2] = f.z;
+            hv[4 * e + 3] = f.w;
           }
-        }
-      }
 #pragma unroll
-      for (int q = 0; q < CPLB; ++q) {
-        const int c = c_lane + LPR * q;
-        if (c >= n_chunks) continue;
-        float hv[ELEMS];
-        const float4* hs = reinterpret_cast<const float4*>(s_h + (size_t)v * I + (size_t)c * ELEMS);
-#pragma unroll
-        for (int e = 0; e < ELEMS / 4; ++e) {
-          float4 f = hs[e];
-          hv[4 * e + 0] = f.x;
-          hv[4 * e + 1] = f.y;
-          hv[4 * e + 2] = f.z;
-          hv[4 * e + 3] = f.w;
-        }
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-          float part = FMT == MC_MXFP4 ? dot_chunk_mx_f32(wv[p][q], sc[p][q], hv, 0.0f)
-                                       : dot_chunk_bf_f32(wv[p][q], hv, 0.0f);
-          acc[p] = fmaf(gate, part, acc[p]);
+          for (int p = 0; p < PASSES; ++p) {
+            const uint4 wq = okq[q] ? wv[j][p][q] : make_uint4(0, 0, 0, 0);
+            const float part = FMT == MC_MXFP4
+                                   ? dot_chunk_mx_f32(wq, e8m0_to_f32(sb[j][p][q]), hv, 0.0f)
+                                   : dot_chunk_bf_f32(wq, hv, 0.0f);
+            acc[p] = fmaf(gate[j], part, acc[p]);
+          }
         }
       }
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      float sum = group_sum(acc[p], LPR);
-      const int row = r0 + row_sub + RPP * p;
-      if (c_lane == 0 && row < H && (RPP <= kB_Rows || row_sub < kB_Rows))
-        a.y[(size_t)t * H + row] += sum;
+      const float sum = group_sum(acc[p], LPR);
+      const int rl = row_sub + RPP * p;
+      if (c_lane == 0 && lane_rows && rl < kB_Rows) s_part[wave][rl] = sum;
+    }
+    __syncthreads();
+    if (threadIdx.x < kB_Rows) {
+      const int row = r0 + threadIdx.x;
+      float v = ((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
+                s_part[3][threadIdx.x];
+      float* yp = a.y + (size_t)t * H + row;
+      if (a.accumulate) v += *yp;
+      *yp = v;
+      if (a.y_bf16) a.y_bf16[(size_t)t * H + row] = f32_to_bf16_rne(v);
+    }
+  }
+  // rows of tokens beyond the valid count
+  if (!a.accumulate || a.y_bf16) {
+    for (int i = threadIdx.x; i < (T - nt) * kB_Rows; i += kThreads) {
+      const int t = nt + i / kB_Rows, row = r0 + i % kB_Rows;
+      if (!a.accumulate) a.y[(size_t)t * H + row] = 0.0f;
+      if (a.y_bf16) a.y_bf16[(size_t)t * H + row] = 0;
     }
   }
 }
@@ -369,35 +426,28 @@ down_kernel(DecodeArgs a, int has_shared) {
 // ---------------------------------------------------------------- dispatch
 
 template <int FMT>
-static void launch_gate_up(const DecodeArgs& a, int has_shared, int cpl, dim3 grid, hipStream_t s) {
+static void launch_gate_up(const DecodeArgs& a, int cpl, dim3 grid, hipStream_t s) {
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((gate_up_kernel<FMT, 1>), grid, dim3(kA_Threads), 0, s, a, has_shared); break;
-    case 2: hipLaunchKernelGGL((gate_up_kernel<FMT, 2>), grid, dim3(kA_Threads), 0, s, a, has_shared); break;
-    case 4: hipLaunchKernelGGL((gate_up_kernel<FMT, 4>), grid, dim3(kA_Threads), 0, s, a, has_shared); break;
-    default: hipLaunchKernelGGL((gate_up_kernel<FMT, 8>), grid, dim3(kA_Threads), 0, s, a, has_shared); break;
+    case 1: hipLaunchKernelGGL((gate_up_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gate_up_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((gate_up_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a); break;
   }
 }
 
 template <int FMT, int LPR>
-static void launch_down_l(const DecodeArgs& a, int has_shared, int cplb, dim3 grid, size_t lds,
-                          hipStream_t s) {
-  switch (cplb) {
-    case 1: hipLaunchKernelGGL((down_kernel<FMT, LPR, 1>), grid, dim3(64), lds, s, a, has_shared); break;
-    case 2: hipLaunchKernelGGL((down_kernel<FMT, LPR, 2>), grid, dim3(64), lds, s, a, has_shared); break;
-    default: hipLaunchKernelGGL((down_kernel<FMT, LPR, 4>), grid, dim3(64), lds, s, a, has_shared); break;
-  }
+static void launch_down_l(const DecodeArgs& a, int cplb, dim3 grid, size_t lds, hipStream_t s) {
+  if (cplb == 1)
+    hipLaunchKernelGGL((down_kernel<FMT, LPR, 1>), grid, dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((down_kernel<FMT, LPR, 2>), grid, dim3(kThreads), lds, s, a);
 }
 
 template <int FMT>
-static void launch_down(const DecodeArgs& a, int has_shared, int lpr, int cplb, dim3 grid,
-                        size_t lds, hipStream_t s) {
+static void launch_down(const DecodeArgs& a, int lpr, int cplb, dim3 grid, size_t lds, hipStream_t s) {
   switch (lpr) {
-    case 2: launch_down_l<FMT, 2>(a, has_shared, cplb, grid, lds, s); break;
-    case 4: launch_down_l<FMT, 4>(a, has_shared, cplb, grid, lds, s); break;
-    case 8: launch_down_l<FMT, 8>(a, has_shared, cplb, grid, lds, s); break;
-    case 16: launch_down_l<FMT, 16>(a, has_shared, cplb, grid, lds, s); break;
-    case 32: launch_down_l<FMT, 32>(a, has_shared, cplb, grid, lds, s); break;
-    default: launch_down_l<FMT, 64>(a, has_shared, cplb, grid, lds, s); break;
+    case 4: launch_down_l<FMT, 4>(a, cplb, grid, lds, s); break;
+    case 16: launch_down_l<FMT, 16>(a, cplb, grid, lds, s); break;
+    default: launch_down_l<FMT, 64>(a, cplb, grid, lds, s); break;
   }
 }
 
@@ -419,7 +469,8 @@ extern "C" size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I) {
 extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w,
                                   int32_t T, int32_t k, const int32_t* n_tok,
                                   const mc_banks* pool, const mc_banks* shared, void* ws,
-                                  size_t ws_bytes, float* y_acc, hipStream_t s) {
+                                  size_t ws_bytes, float* y_acc, int32_t accumulate, void* y_bf16,
+                                  hipStream_t s) {
   clear_error();
   int rc;
   if ((rc = check_banks(pool, "moe_experts_decode pool")) != MC_OK) return rc;
@@ -429,8 +480,10 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
                "moe_experts_decode: shared expert differs from the pool in format or shape");
   }
   MC_REQUIRE(T >= 0 && k >= 1, "moe_experts_decode: T=%d k=%d", T, k);
+  MC_REQUIRE(T <= kMaxTok, "moe_experts_decode: T=%d exceeds %d", T, kMaxTok);
   MC_REQUIRE((int64_t)T * k <= kMaxRoutes, "moe_experts_decode: T*k=%lld exceeds %d",
              (long long)T * k, kMaxRoutes);
+  MC_REQUIRE(accumulate == 0 || accumulate == 1, "moe_experts_decode: accumulate=%d", accumulate);
   if (T == 0) return MC_OK;
   MC_REQUIRE(x_bf16 && slots && w && y_acc && ws, "moe_experts_decode: NULL pointer");
   MC_REQUIRE(ws_bytes >= moe_experts_decode_ws_bytes(T, k, pool->I),
@@ -439,25 +492,24 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
   MC_REQUIRE((uintptr_t)x_bf16 % 16 == 0 && (uintptr_t)ws % 16 == 0,
              "moe_experts_decode: x and ws must be 16-byte aligned");
   const int H = pool->H, I = pool->I, fmt = pool->fmt;
-  const int nvec = k + (shared ? 1 : 0);
-  const size_t lds = (size_t)nvec * I * sizeof(float);
-  if (lds > (size_t)kB_LdsBytes) {
-    set_error("moe_experts_decode: (k+1)*I*4 = %zu bytes of staged activations exceed %d", lds,
-              kB_LdsBytes);
-    return MC_EUNSUPPORTED;
-  }
   const int elems = fmt == MC_MXFP4 ? 32 : 8;
   const int cpl = pow2_at_least((H / elems + 63) / 64);
-  if (cpl > 8) {
+  if (cpl > 4) {
     set_error("moe_experts_decode: H=%d too large", H);
     return MC_EUNSUPPORTED;
   }
   const int chunks_b = I / elems;
-  int lpr = chunks_b >= 64 ? 64 : pow2_at_least(chunks_b);
-  if (lpr < 2) lpr = 2;
+  const int lpr = chunks_b <= 4 ? 4 : (chunks_b <= 16 ? 16 : 64);
   const int cplb = pow2_at_least((chunks_b + lpr - 1) / lpr);
-  if (cplb > 4) {
+  if (cplb > 2) {
     set_error("moe_experts_decode: I=%d too large", I);
+    return MC_EUNSUPPORTED;
+  }
+  const int has_shared = shared ? 1 : 0;
+  const size_t lds = ((size_t)(k + has_shared) * I * sizeof(float) + 1023) & ~(size_t)1023;
+  if (lds > (size_t)kB_LdsBytes) {
+    set_error("moe_experts_decode: (k+1)*I*4 = %zu bytes of staged activations exceed %d", lds,
+              kB_LdsBytes);
     return MC_EUNSUPPORTED;
   }
 
@@ -484,19 +536,21 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
   a.h_route = static_cast<float*>(ws);
   a.h_shared = a.h_route + (size_t)T * k * I;
   a.y = y_acc;
-  const int has_shared = shared ? 1 : 0;
+  a.y_bf16 = static_cast<uint16_t*>(y_bf16);
+  a.accumulate = accumulate;
+  a.has_shared = has_shared;
 
   dim3 grid_a(T * k + has_shared, I / kA_RowsI);
   if (fmt == MC_MXFP4)
-    launch_gate_up<MC_MXFP4>(a, has_shared, cpl, grid_a, s);
+    launch_gate_up<MC_MXFP4>(a, cpl, grid_a, s);
   else
-    launch_gate_up<MC_BF16>(a, has_shared, cpl, grid_a, s);
+    launch_gate_up<MC_BF16>(a, cpl, grid_a, s);
   MC_LAUNCH_CHECK();
   dim3 grid_b((H + kB_Rows - 1) / kB_Rows);
   if (fmt == MC_MXFP4)
-    launch_down<MC_MXFP4>(a, has_shared, lpr, cplb, grid_b, lds, s);
+    launch_down<MC_MXFP4>(a, lpr, cplb, grid_b, lds, s);
   else
-    launch_down<MC_BF16>(a, has_shared, lpr, cplb, grid_b, lds, s);
+    launch_down<MC_BF16>(a, lpr, cplb, grid_b, lds, s);
   MC_LAUNCH_CHECK();
   return MC_OK;
 }

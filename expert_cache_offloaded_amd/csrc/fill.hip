@@ -10,6 +10,8 @@
 // Grid: (list entry, chunk of the expert's bytes).  Every entry copies all banks
 // of one expert (one flat id across gate_up / scales / down, [jjl357] "8.4").
 // Workgroups whose entry is beyond *n_fill exit at once.
+#include <mutex>
+
 #include "mc_common.h"
 
 namespace mc {
@@ -59,10 +61,26 @@ fill_kernel(FillSegs g, const int32_t* __restrict__ fill_flat, const int32_t* __
   }
 }
 
+// Device-visible address of pinned host memory.  Translations are remembered so a
+// call made while a stream is being captured needs no runtime query once the same
+// banks were used before.
+static std::mutex g_view_mu;
+static const void* g_view_host[64];
+static const uint8_t* g_view_dev[64];
+static int g_view_n = 0, g_view_next = 0;
+
 static int device_view(const void* host, const uint8_t** out, const char* what) {
   if (host == nullptr) {
     *out = nullptr;
     return MC_OK;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_view_mu);
+    for (int i = 0; i < g_view_n; ++i)
+      if (g_view_host[i] == host) {
+        *out = g_view_dev[i];
+        return MC_OK;
+      }
   }
   void* d = nullptr;
   hipError_t e = hipHostGetDevicePointer(&d, const_cast<void*>(host), 0);
@@ -72,6 +90,11 @@ static int device_view(const void* host, const uint8_t** out, const char* what) 
     return MC_EINVAL;
   }
   *out = static_cast<const uint8_t*>(d);
+  std::lock_guard<std::mutex> lk(g_view_mu);
+  g_view_host[g_view_next] = host;
+  g_view_dev[g_view_next] = *out;
+  g_view_next = (g_view_next + 1) % 64;
+  if (g_view_n < 64) ++g_view_n;
   return MC_OK;
 }
 

@@ -26,7 +26,7 @@
 #include <thread>
 #include <vector>
 
-#include "../../include/mc.h"
+#include "mc.h"
 
 namespace mc {
 void set_error(const char* fmt, ...);

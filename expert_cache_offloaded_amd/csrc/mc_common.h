@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <stddef.h>
 
-#include "../../include/mc.h"
+#include "mc.h"
 
 namespace mc {
 

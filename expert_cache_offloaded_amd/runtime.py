@@ -116,6 +116,7 @@ class DecodeLayer:
             nb = L.hybrid_stage_bytes(bufs.T, bufs.k, bufs.H)
             self.stage = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
         self._hy = {}
+        self._sh = {}
 
     def __call__(self, layer: int, logits: torch.Tensor, x: torch.Tensor, n_tok=None, stream=None):
         """logits fp32 [T, E], x bf16 bits [T, H] (device) -> self.b.y (bf16 bits)."""
@@ -136,15 +137,21 @@ class DecodeLayer:
         else:
             w_gpu = b.w
         L.fill_slots(self.host.desc, self.pool.desc, b.fill_flat, b.fill_slot, b.n_fill, stream)
-        if stream is None:
-            b.y_acc.zero_()
-        else:
-            with torch.cuda.stream(stream):
-                b.y_acc.zero_()
-        sh = self.shared.entry(layer).desc if self.shared is not None else None
-        L.moe_experts_decode(x, b.slots, w_gpu, n_tok, self.pool.desc, sh, b.ws, b.y_acc, stream)
+        sh = self._shared_desc(layer)
         if self.hybrid:
+            # GPU partial in fp32; the merge adds the host partial and rounds once
+            L.moe_experts_decode(x, b.slots, w_gpu, n_tok, self.pool.desc, sh, b.ws, b.y_acc,
+                                 accumulate=0, y_bf16=None, stream=stream)
             L.hybrid_split_merge(hy, L.MC_MERGE, stream)
         else:
-            L.finish_bf16(b.y_acc, n_tok, b.y, stream)
+            L.moe_experts_decode(x, b.slots, w_gpu, n_tok, self.pool.desc, sh, b.ws, b.y_acc,
+                                 accumulate=0, y_bf16=b.y, stream=stream)
         return b.y
+
+    def _shared_desc(self, layer):
+        if self.shared is None:
+            return None
+        d = self._sh.get(layer)
+        if d is None:
+            d = self._sh[layer] = self.shared.entry(layer)
+        return d.desc

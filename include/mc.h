@@ -195,22 +195,27 @@ size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I);
  * Slot-indirected SwiGLU experts and gated combine on the GPU
  * ([jjl357] "1.1", "6.7" step 5; [wanger] "代码全链路": GPU routes of the hybrid
  * split carry gate 0 for host routes).
- *   y_acc[t][:] += sum_j w[t][j] * Expert(pool[slots[t][j]])(x[t])
- *                  (+ Expert(shared[0])(x[t]) with weight 1 if shared != NULL)
+ *   y_acc[t][:] (+)= sum_j w[t][j] * Expert(pool[slots[t][j]])(x[t])
+ *                    (+ Expert(shared[0])(x[t]) with weight 1 if shared != NULL)
  * for t < *n_tok, over routes with slots[t][j] >= 0; each distinct slot's weights
  * are read once for all tokens that route to it ([jjl357] "6.1": dedup).
- * Expert(x) = W_down (silu(W_gate x) * (W_up x)), fp32 accumulation; x bf16 [T][H];
- * y_acc fp32 [T][H] (accumulated into, not overwritten).
- *   pool     device slot banks; shared: NULL or a device bank whose entry 0 is the
- *            layer's shared expert (same fmt, H, I).
- *   ws       device workspace of moe_experts_decode_ws_bytes(T, k, I) bytes.
- * Needs H % 64 == 0, I % 64 == 0 (MXFP4 blocks of 32 along both contractions),
- * T*k <= 1024.
+ * Expert(x) = W_down (silu(W_gate x) * (W_up x)), fp32 accumulation; x bf16 [T][H].
+ *   y_acc      fp32 [T][H]: accumulate = 1 adds to it, accumulate = 0 overwrites it
+ *              (rows t >= *n_tok are then set to 0).
+ *   y_bf16     NULL, or bf16 [T][H] written with bf16_rne(y_acc) (rows t >= *n_tok = 0),
+ *              so a layer with no host branch needs no separate rounding pass.
+ *   pool       device slot banks; shared: NULL or a device bank whose entry 0 is the
+ *              layer's shared expert (same fmt, H, I).
+ *   ws         device workspace of moe_experts_decode_ws_bytes(T, k, I) bytes (the
+ *              gate_up results h), 16-byte aligned; one workspace per call in flight.
+ * Two kernel launches (gate_up + SwiGLU, then down + combine).  Needs H % 64 == 0,
+ * I % 64 == 0, T <= 64, T*k <= 1024, (k + 1) * I * 4 <= 64 KiB.
  */
 int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w, int32_t T,
                        int32_t k, const int32_t* n_tok, const mc_banks* pool,
                        const mc_banks* shared, void* ws, size_t ws_bytes, float* y_acc,
-                       hipStream_t s);
+                       int32_t accumulate, void* y_bf16, hipStream_t s);
+
 
 /* ------------------------------------------------------------------------- */
 /* Hybrid split / merge and the host branch                                  */

@@ -67,15 +67,22 @@ def _run_decode(cfg, case, nt=None):
     x = t_of(case["x"]).cuda()
     slots = torch.from_numpy(case["slots"]).cuda()
     w = torch.from_numpy(case["w"]).cuda()
-    ws = torch.empty(decode_ws_bytes(T, cfg.k, cfg.I) // 4, dtype=torch.float32, device="cuda")
-    y = torch.zeros((T, cfg.H), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(decode_ws_bytes(T, cfg.k, cfg.I) // 4, dtype=torch.float32, device="cuda")
+    y = torch.full((T, cfg.H), 7.0, dtype=torch.float32, device="cuda")    # overwritten
     ntt = None
     if nt is not None:
         ntt = torch.tensor([nt], dtype=torch.int32, device="cuda")
-    moe_experts_decode(x, slots, w, ntt, pool, sh, ws, y)
     yb = torch.empty((T, cfg.H), dtype=torch.int16, device="cuda")
-    finish_bf16(y, ntt, yb)
+    moe_experts_decode(x, slots, w, ntt, pool, sh, ws, y, accumulate=0, y_bf16=yb)
+    # a second call accumulating on top doubles the result; the separate rounding pass
+    # gives the same bf16 bits as the fused one
+    y2 = y.clone()
+    moe_experts_decode(x, slots, w, ntt, pool, sh, ws, y2, accumulate=1)
+    yb2 = torch.empty_like(yb)
+    finish_bf16(y, ntt, yb2)
     torch.cuda.synchronize()
+    assert torch.equal(yb, yb2)
+    assert torch.allclose(y2, 2 * y, rtol=1e-6, atol=1e-6)
     return y.cpu().numpy(), yb
 
 
