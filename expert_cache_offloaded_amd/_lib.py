@@ -39,6 +39,11 @@ class Cache(C.Structure):
                 ("clock", C.c_void_p), ("stats", C.c_void_p)]
 
 
+class Prefetch(C.Structure):
+    _fields_ = [("host_src", C.POINTER(Banks)), ("first_flat", C.c_int64), ("dst", C.POINTER(Banks)),
+                ("copy", C.c_void_p), ("dst_free", C.c_void_p), ("done", C.c_void_p)]
+
+
 class Hybrid(C.Structure):
     _fields_ = [("x_bf16", C.c_void_p), ("ids_raw", C.c_void_p), ("slots", C.c_void_p),
                 ("w", C.c_void_p), ("T", C.c_int32), ("k", C.c_int32), ("layer", C.c_int32),
@@ -62,6 +67,10 @@ _SIGS = {
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
                                      _P, C.c_size_t, _P, _I32, _P, _P]),
+    "mc_prefill_sort_routes": (C.c_int, [_P, _I32, _I32, _P, _I32, _P, C.c_size_t, _P, _P, _P, _P]),
+    "moe_experts_prefill_ws_bytes": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_experts_prefill": (C.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, C.POINTER(Banks), _P, C.c_size_t,
+                                      _P, _P, C.POINTER(Prefetch)]),
     "mc_host_pool_create": (_P, [_I32, _P]),
     "mc_host_pool_destroy": (None, [_P]),
     "mc_host_experts": (C.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, C.POINTER(Banks), _P]),
@@ -192,6 +201,39 @@ def finish_bf16(y_acc, n_tok, y_bf16, stream=None) -> None:
     T, H = y_acc.shape
     _check("mc_finish_bf16", lib().mc_finish_bf16(_ptr(y_acc), T, H, _ptr(n_tok), _ptr(y_bf16),
                                                   _stream(stream)))
+
+
+def prefill_sort_routes(ids, n_tok, E: int, ws, counts, offsets, perm, stream=None) -> None:
+    T, k = ids.shape
+    _check("mc_prefill_sort_routes", lib().mc_prefill_sort_routes(
+        _ptr(ids), T, k, _ptr(n_tok), E, _ptr(ws), ws.numel() * ws.element_size(), _ptr(counts),
+        _ptr(offsets), _ptr(perm), _stream(stream)))
+
+
+def prefill_ws_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
+    return int(lib().moe_experts_prefill_ws_bytes(T, k, E, H, I))
+
+
+def make_prefetch(host: Banks, first_flat: int, dst: Banks, copy_stream) -> Prefetch:
+    """Prefetch descriptor; ordering with the compute stream is left to the caller's
+    stream/event waits (dst_free and done are NULL)."""
+    p = Prefetch()
+    p.host_src = C.pointer(host)
+    p.first_flat = first_flat
+    p.dst = C.pointer(dst)
+    p.copy = copy_stream.cuda_stream
+    p.dst_free = None
+    p.done = None
+    p._keep = (host, dst)
+    return p
+
+
+def moe_experts_prefill(x, ids, w, n_tok, E: int, layer_buf: Banks, ws, y, nxt: Optional[Prefetch] = None,
+                        stream=None) -> None:
+    T, k = ids.shape
+    _check("moe_experts_prefill", lib().moe_experts_prefill(
+        _ptr(x), _ptr(ids), _ptr(w), T, k, _ptr(n_tok), E, C.byref(layer_buf), _ptr(ws),
+        ws.numel() * ws.element_size(), _ptr(y), _stream(stream), C.byref(nxt) if nxt is not None else None))
 
 
 class HostPool:

@@ -1,0 +1,612 @@
+// moe_experts_prefill: token-sorted grouped expert GEMM over one layer's resident
+// experts, plus the whole-layer prefetch of the next layer.
+//
+// [jjl357] "4.1"-"4.3": in prefill the routed experts of thousands of tokens cover
+// almost the whole layer, so the next layer's complete expert pool is copied into a
+// second layer-sized buffer while this layer computes (T_layer ~ max(T_compute,
+// T_PCIe)); the two buffers come from the slot pool.  [jjl357] "6.8" / [wanger]
+// "代码全链路": experts run as grouped GPU execution.
+//
+// Steps (all on the compute stream, fixed grids, no host synchronisation):
+//   1. count:   one workgroup per expert counts its routes (ballots; 4 wave quarters).
+//   2. plan:    one workgroup: row offsets per expert (exclusive scan) and the M-tile
+//               table (64-row tiles per expert).
+//   3. scatter: one workgroup per expert writes its routes' indices r = t*k + j in
+//               (t, j) order — a stable counting sort — into perm.
+//   4. gate_up: grouped GEMM, tile = (expert, 64 sorted rows, 128 intermediate
+//               columns).  Four waves share the gathered activation tile in LDS;
+//               each wave owns 32 gate and the matching 32 up columns and reads its
+//               MXFP4 weights straight from memory into MFMA operand registers,
+//               dequantising to bf16 (exact).  K is visited in 128-element steps;
+//               the MFMA's K order is permuted so a lane consumes one whole 32-element
+//               MX block (16 B + 1 scale byte) per row per step.  bf16 MFMA 16x16x32,
+//               fp32 accumulation; epilogue h = silu(g) * u, stored as fp16.
+//   5. down:    grouped GEMM of h (fp16, rows contiguous per expert) against W_down
+//               dequantised to fp16 (exact for block exponents in [-23, 13]), fp16
+//               MFMA 16x16x32; epilogue writes w_r * Y into the route's own row of a
+//               [T*k][H] fp32 buffer (no atomics).
+//   6. combine: y[t] = bf16_rne(sum_j Yr[t*k + j]) in route order — one rounding.
+// Tiles are enumerated expert-major, then column block, then row tile, and the
+// block id is remapped so consecutive tiles run on the same XCD (its L2 holds the
+// expert's weights and activation rows while they are reused).
+#include "mc_common.h"
+
+namespace mc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kP_BM = 64;          // rows per tile
+constexpr int kP_KS = 128;         // K per pipeline step
+constexpr int kP_Threads = 256;
+constexpr int kP_GU_Cols = 128;    // intermediate columns per gate_up tile (32 per wave)
+constexpr int kP_DN_Cols = 256;    // output columns per down tile (64 per wave)
+constexpr int kP_LdsRow = kP_KS + 8;   // padded LDS row (elements)
+constexpr int kP_MaxE = 1024;
+
+struct PrefillWs {
+  int32_t* counts;      // [E]
+  int32_t* counts4;     // [E][4] per-wave counts
+  int32_t* offsets;     // [E+1]
+  int32_t* mtile_off;   // [E+1]
+  int32_t* perm;        // [T*k]
+  _Float16* h;          // [T*k][I]
+  float* yr;            // [T*k][H]
+};
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static size_t ws_layout(int T, int k, int E, int H, int I, PrefillWs* w, uint8_t* base) {
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return base ? base + at : nullptr;
+  };
+  const size_t nr = (size_t)T * k;
+  uint8_t* p;
+  p = take((size_t)E * 4);
+  if (w) w->counts = (int32_t*)p;
+  p = take((size_t)E * 16);
+  if (w) w->counts4 = (int32_t*)p;
+  p = take((size_t)(E + 1) * 4);
+  if (w) w->offsets = (int32_t*)p;
+  p = take((size_t)(E + 1) * 4);
+  if (w) w->mtile_off = (int32_t*)p;
+  p = take(nr * 4);
+  if (w) w->perm = (int32_t*)p;
+  p = take(nr * (size_t)I * 2);
+  if (w) w->h = (_Float16*)p;
+  p = take(nr * (size_t)H * 4);
+  if (w) w->yr = (float*)p;
+  return o;
+}
+
+// ---------------------------------------------------------------- sort
+
+__device__ __forceinline__ int route_count(const int32_t* n_tok, int T, int k) {
+  const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
+  return nt * k;
+}
+
+// 1. per-expert route counts, per wave quarter (ballot + popcount, no atomics)
+__global__ void __launch_bounds__(256)
+sort_count_kernel(const int32_t* __restrict__ ids, int T, int k, const int32_t* __restrict__ n_tok,
+                  int E, int32_t* __restrict__ counts, int32_t* __restrict__ counts4) {
+  const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nr = route_count(n_tok, T, k);
+  const int q = (nr + 3) / 4, r0 = wave * q, r1 = min(nr, r0 + q);
+  int c = 0;
+  for (int base = r0; base < r1; base += 64) {
+    const int r = base + lane;
+    const bool hit = r < r1 && ids[r] == e;
+    c += __popcll(__ballot(hit));
+  }
+  __shared__ int s_c[4];
+  if (lane == 0) {
+    s_c[wave] = c;
+    counts4[e * 4 + wave] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) counts[e] = s_c[0] + s_c[1] + s_c[2] + s_c[3];
+}
+
+// 2. offsets and the M-tile table (one workgroup, E <= 1024)
+__global__ void __launch_bounds__(1024)
+sort_plan_kernel(int E, const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                 int32_t* __restrict__ mtile_off) {
+  __shared__ int s_a[kP_MaxE], s_b[kP_MaxE];
+  const int tid = threadIdx.x;
+  const int c = tid < E ? counts[tid] : 0;
+  s_a[tid] = c;
+  s_b[tid] = (c + kP_BM - 1) / kP_BM;
+  __syncthreads();
+  // Hillis-Steele inclusive scans
+  for (int o = 1; o < kP_MaxE; o <<= 1) {
+    int va = tid >= o ? s_a[tid - o] : 0;
+    int vb = tid >= o ? s_b[tid - o] : 0;
+    __syncthreads();
+    s_a[tid] += va;
+    s_b[tid] += vb;
+    __syncthreads();
+  }
+  if (tid < E) {
+    offsets[tid + 1] = s_a[tid];
+    mtile_off[tid + 1] = s_b[tid];
+  }
+  if (tid == 0) {
+    offsets[0] = 0;
+    mtile_off[0] = 0;
+  }
+}
+
+// 3. stable scatter: routes of expert e in (t, j) order
+__global__ void __launch_bounds__(256)
+sort_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, const int32_t* __restrict__ n_tok,
+                    int E, const int32_t* __restrict__ counts4, const int32_t* __restrict__ offsets,
+                    int32_t* __restrict__ perm) {
+  const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nr = route_count(n_tok, T, k);
+  const int q = (nr + 3) / 4, r0 = wave * q, r1 = min(nr, r0 + q);
+  int pos = offsets[e];
+  for (int w = 0; w < wave; ++w) pos += counts4[e * 4 + w];
+  for (int base = r0; base < r1; base += 64) {
+    const int r = base + lane;
+    const bool hit = r < r1 && ids[r] == e;
+    const uint64_t m = __ballot(hit);
+    if (hit) perm[pos + __popcll(m & ((1ull << lane) - 1ull))] = r;
+    pos += __popcll(m);
+  }
+}
+
+// ---------------------------------------------------------------- GEMM helpers
+
+struct PrefillArgs {
+  const uint16_t* x;          // [T][H] bf16
+  const float* w;             // [T*k]
+  int32_t T, k, E, H, I;
+  const uint8_t* gu;          // layer buffer banks (entry e = expert e)
+  const uint8_t* gus;
+  const uint8_t* dn;
+  const uint8_t* dns;
+  PrefillWs ws;
+  int32_t n_nb;               // column blocks per expert
+};
+
+// Tile of logical id L: expert, row range, column block.  Returns false if L is past
+// the last tile of this call.
+__device__ __forceinline__ bool find_tile(const PrefillArgs& a, int L, int* e_out, int* row0,
+                                          int* nrows, int* nb) {
+  const int32_t* mo = a.ws.mtile_off;
+  const int total = mo[a.E] * a.n_nb;
+  if (L >= total) return false;
+  int lo = 0, hi = a.E;                         // largest e with mo[e] * n_nb <= L
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mo[mid] * a.n_nb <= L) lo = mid;
+    else hi = mid;
+  }
+  const int e = lo;
+  const int m_e = mo[e + 1] - mo[e];
+  const int Lp = L - mo[e] * a.n_nb;
+  *nb = Lp / m_e;
+  const int mt = Lp % m_e;
+  const int start = a.ws.offsets[e] + mt * kP_BM;
+  *row0 = start;
+  *nrows = min(kP_BM, a.ws.offsets[e + 1] - start);
+  *e_out = e;
+  return true;
+}
+
+// Consecutive logical tiles on the same XCD: hardware block b runs on XCD b % 8.
+__device__ __forceinline__ int xcd_remap(int b, int G) {
+  const int per = G >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
+// 8 consecutive MXFP4 elements (one dword of codes) -> bf16x8 / f16x8, scaled.
+__device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t v, float s) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ f16x8_t fp4x8_f16(uint32_t v, float s) {
+  const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 0);
+  const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 1);
+  const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 2);
+  const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 3);
+  f16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// ---------------------------------------------------------------- gate_up GEMM
+
+__global__ void __launch_bounds__(kP_Threads)
+prefill_gate_up_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kP_BM][kP_LdsRow];
+  int e, row0, nrows, nb;
+  if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, I = a.I;
+  const int c0 = nb * kP_GU_Cols + wave * 32;              // first intermediate column of the wave
+
+  // activation rows: thread loads 4 x 16 B per step; chunk = tid + 256 q -> (row, 16-B piece)
+  const uint16_t* arow[4];
+  int a_r[4], a_c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int chunk = tid + kP_Threads * q;
+    a_r[q] = chunk >> 4;
+    a_c[q] = chunk & 15;
+    const int rr = min(a_r[q], nrows - 1);
+    const int route = a.ws.perm[row0 + rr];
+    arow[q] = a.x + (size_t)(route / a.k) * H;
+  }
+  // weight rows of the lane's 4 column tiles (2 gate, 2 up)
+  const size_t row_b = (size_t)H / 2, row_s = (size_t)H / 32;
+  const uint8_t* wbase = a.gu + (size_t)e * (2 * (size_t)I * row_b);
+  const uint8_t* sbase = a.gus + (size_t)e * (2 * (size_t)I * row_s);
+  const uint8_t* brow[4];
+  const uint8_t* bsc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = (nt & 1) * 16 + (lane & 15);
+    const int wr = (nt < 2 ? 0 : I) + c0 + col;
+    brow[nt] = wbase + (size_t)wr * row_b;
+    bsc[nt] = sbase + (size_t)wr * row_s;
+  }
+  const int kq = lane >> 4;                                 // which MX block of the step
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = H / kP_KS;
+  uint4 av[4];
+  uint4 bv[4];
+  uint32_t bs[4];
+  auto load_step = [&](int s) {
+    const int k0 = s * kP_KS;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      av[q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + a_c[q] * 8);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int kb = (k0 >> 5) + kq;
+      bv[nt] = *reinterpret_cast<const uint4*>(brow[nt] + (size_t)kb * 16);
+      bs[nt] = bsc[nt][kb];
+    }
+  };
+  load_step(0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[0][a_r[q]][a_c[q] * 8]) = av[q];
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    uint4 bcur[4];
+    float scur[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      bcur[nt] = bv[nt];
+      scur[nt] = e8m0_to_f32(bs[nt]);
+    }
+    if (s + 1 < nsteps) load_step(s + 1);
+    // 4 MFMA K-steps of 8 elements per lane: lane group kq owns MX block kq of the step
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t bop[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_bf16(u4_get(bcur[nt], ks), scur[nt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8_t aop =
+            *reinterpret_cast<const bf16x8_t*>(&sA[cur][mt * 16 + (lane & 15)][kq * 32 + ks * 8]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+    if (s + 1 < nsteps) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[cur ^ 1][a_r[q]][a_c[q] * 8]) = av[q];
+    }
+    __syncthreads();
+  }
+
+  // epilogue: h = silu(g) * u -> fp16, rows of this tile
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = mt * 16 + (lane >> 4) * 4 + j;
+      if (r >= nrows) continue;
+      _Float16* hrow = a.ws.h + (size_t)(row0 + r) * I;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float g = acc[mt][nt][j], u = acc[mt][nt + 2][j];
+        hrow[c0 + nt * 16 + (lane & 15)] = (_Float16)(silu(g) * u);
+      }
+    }
+}
+
+// ---------------------------------------------------------------- down GEMM
+
+__global__ void __launch_bounds__(kP_Threads)
+prefill_down_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kP_BM][kP_LdsRow];
+  int e, row0, nrows, nb;
+  if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, I = a.I;
+  const int c0 = nb * kP_DN_Cols + wave * 64;              // first output column of the wave
+
+  const _Float16* arow[4];
+  int a_r[4], a_c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int chunk = tid + kP_Threads * q;
+    a_r[q] = chunk >> 4;
+    a_c[q] = chunk & 15;
+    const int rr = min(a_r[q], nrows - 1);
+    arow[q] = a.ws.h + (size_t)(row0 + rr) * I;
+  }
+  const size_t row_b = (size_t)I / 2, row_s = (size_t)I / 32;
+  const uint8_t* wbase = a.dn + (size_t)e * ((size_t)H * row_b);
+  const uint8_t* sbase = a.dns + (size_t)e * ((size_t)H * row_s);
+  const uint8_t* brow[4];
+  const uint8_t* bsc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int wr = c0 + nt * 16 + (lane & 15);
+    brow[nt] = wbase + (size_t)wr * row_b;
+    bsc[nt] = sbase + (size_t)wr * row_s;
+  }
+  const int kq = lane >> 4;
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = I / kP_KS;
+  uint4 av[4];
+  uint4 bv[4];
+  uint32_t bs[4];
+  auto load_step = [&](int s) {
+    const int k0 = s * kP_KS;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      av[q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + a_c[q] * 8);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int kb = (k0 >> 5) + kq;
+      bv[nt] = *reinterpret_cast<const uint4*>(brow[nt] + (size_t)kb * 16);
+      bs[nt] = bsc[nt][kb];
+    }
+  };
+  load_step(0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[0][a_r[q]][a_c[q] * 8]) = av[q];
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    uint4 bcur[4];
+    float scur[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      bcur[nt] = bv[nt];
+      scur[nt] = e8m0_to_f32(bs[nt]);
+    }
+    if (s + 1 < nsteps) load_step(s + 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      f16x8_t bop[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_f16(u4_get(bcur[nt], ks), scur[nt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f16x8_t aop =
+            *reinterpret_cast<const f16x8_t*>(&sA[cur][mt * 16 + (lane & 15)][kq * 32 + ks * 8]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+    if (s + 1 < nsteps) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[cur ^ 1][a_r[q]][a_c[q] * 8]) = av[q];
+    }
+    __syncthreads();
+  }
+
+  // epilogue: the route's own output row, scaled by its gate
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = mt * 16 + (lane >> 4) * 4 + j;
+      if (r >= nrows) continue;
+      const int route = a.ws.perm[row0 + r];
+      const float g = a.w[route];
+      float* yrow = a.ws.yr + (size_t)route * H;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) yrow[c0 + nt * 16 + (lane & 15)] = g * acc[mt][nt][j];
+    }
+}
+
+// ---------------------------------------------------------------- combine
+
+// y[t][c] = bf16_rne(sum over valid routes j of Yr[t*k + j][c]), j ascending
+__global__ void __launch_bounds__(256)
+prefill_combine_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int H,
+                       const int32_t* __restrict__ n_tok, const float* __restrict__ yr,
+                       uint16_t* __restrict__ y) {
+  const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
+  const int64_t n4 = (int64_t)T * H / 4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i * 4 / H), c = (int)(i * 4 % H);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < nt) {
+      for (int j = 0; j < k; ++j) {
+        const int id = ids[t * k + j];
+        if (id < 0 || id >= E) continue;
+        const float4 v = *reinterpret_cast<const float4*>(yr + ((size_t)t * k + j) * H + c);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+      }
+    }
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16_rne(s.x) | ((uint32_t)f32_to_bf16_rne(s.y) << 16);
+    o.y = (uint32_t)f32_to_bf16_rne(s.z) | ((uint32_t)f32_to_bf16_rne(s.w) << 16);
+    *reinterpret_cast<uint2*>(y + (size_t)t * H + c) = o;
+  }
+}
+
+static int sort_launch(const int32_t* ids, int T, int k, const int32_t* n_tok, int E,
+                       const PrefillWs& w, hipStream_t s) {
+  hipLaunchKernelGGL(sort_count_kernel, dim3(E), dim3(256), 0, s, ids, T, k, n_tok, E, w.counts,
+                     w.counts4);
+  hipLaunchKernelGGL(sort_plan_kernel, dim3(1), dim3(1024), 0, s, E, w.counts, w.offsets,
+                     w.mtile_off);
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3(E), dim3(256), 0, s, ids, T, k, n_tok, E, w.counts4,
+                     w.offsets, w.perm);
+  MC_LAUNCH_CHECK();
+  return MC_OK;
+}
+
+}  // namespace mc
+
+using namespace mc;
+
+extern "C" size_t moe_experts_prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+  if (T < 0 || k < 0 || E < 0 || H < 0 || I < 0) return 0;
+  return ws_layout(T, k, E, H, I, nullptr, nullptr);
+}
+
+extern "C" int mc_prefill_sort_routes(const int32_t* ids, int32_t T, int32_t k,
+                                      const int32_t* n_tok, int32_t E, void* ws, size_t ws_bytes,
+                                      int32_t* counts, int32_t* offsets, int32_t* perm,
+                                      hipStream_t s) {
+  clear_error();
+  MC_REQUIRE(T >= 0 && k >= 1 && E >= 1 && E <= kP_MaxE, "mc_prefill_sort_routes: T=%d k=%d E=%d",
+             T, k, E);
+  MC_REQUIRE(ids && ws && counts && offsets && (perm || T == 0), "mc_prefill_sort_routes: NULL pointer");
+  MC_REQUIRE(ws_bytes >= (size_t)E * 16 + (size_t)(E + 1) * 4,
+             "mc_prefill_sort_routes: workspace too small");
+  PrefillWs w{};
+  w.counts = counts;
+  w.offsets = offsets;
+  w.perm = perm;
+  w.counts4 = static_cast<int32_t*>(ws);
+  w.mtile_off = static_cast<int32_t*>(ws) + (size_t)E * 4;
+  return sort_launch(ids, T, k, n_tok, E, w, s);
+}
+
+extern "C" int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const float* w,
+                                   int32_t T, int32_t k, const int32_t* n_tok, int32_t E,
+                                   const mc_banks* layer_buf, void* ws, size_t ws_bytes,
+                                   void* y_bf16, hipStream_t s, const mc_prefetch* next) {
+  clear_error();
+  int rc;
+  if ((rc = check_banks(layer_buf, "moe_experts_prefill layer_buf")) != MC_OK) return rc;
+  MC_REQUIRE(layer_buf->fmt == MC_MXFP4, "moe_experts_prefill: MXFP4 experts only");
+  MC_REQUIRE(T >= 0 && k >= 1 && E >= 1 && E <= kP_MaxE && k <= E,
+             "moe_experts_prefill: T=%d k=%d E=%d", T, k, E);
+  MC_REQUIRE(layer_buf->n >= E, "moe_experts_prefill: layer buffer holds %lld < E=%d experts",
+             (long long)layer_buf->n, E);
+  const int H = layer_buf->H, I = layer_buf->I;
+  MC_REQUIRE(H % kP_DN_Cols == 0 && I % kP_GU_Cols == 0 && H % kP_KS == 0 && I % kP_KS == 0,
+             "moe_experts_prefill: H=%d must be a multiple of %d and I=%d of %d", H, kP_DN_Cols, I,
+             kP_GU_Cols);
+  MC_REQUIRE(ws_bytes >= moe_experts_prefill_ws_bytes(T, k, E, H, I),
+             "moe_experts_prefill: workspace %zu < %zu bytes", ws_bytes,
+             moe_experts_prefill_ws_bytes(T, k, E, H, I));
+  MC_REQUIRE(((uintptr_t)x_bf16 | (uintptr_t)ws | (uintptr_t)y_bf16) % 16 == 0,
+             "moe_experts_prefill: x, ws and y must be 16-byte aligned");
+
+  // prefetch of the next layer's whole pool on the copy stream (double buffer)
+  if (next) {
+    MC_REQUIRE(next->host_src && next->dst && next->copy, "moe_experts_prefill: bad prefetch");
+    if ((rc = check_banks(next->host_src, "prefetch host_src")) != MC_OK) return rc;
+    if ((rc = check_banks(next->dst, "prefetch dst")) != MC_OK) return rc;
+    MC_REQUIRE(next->host_src->fmt == next->dst->fmt && next->host_src->H == next->dst->H &&
+                   next->host_src->I == next->dst->I,
+               "moe_experts_prefill: prefetch source and destination differ");
+    MC_REQUIRE(next->first_flat >= 0 && next->first_flat + E <= next->host_src->n && next->dst->n >= E,
+               "moe_experts_prefill: prefetch range out of bounds");
+    if (next->dst_free) MC_HIP(hipStreamWaitEvent(next->copy, next->dst_free, 0));
+    BankBytes bb = bank_bytes(next->dst->fmt, next->dst->H, next->dst->I);
+    const size_t nbytes[4] = {bb.gate_up, bb.gate_up_scale, bb.down, bb.down_scale};
+    const void* src[4] = {next->host_src->gate_up, next->host_src->gate_up_scale,
+                          next->host_src->down, next->host_src->down_scale};
+    void* dst[4] = {next->dst->gate_up, next->dst->gate_up_scale, next->dst->down,
+                    next->dst->down_scale};
+    for (int b = 0; b < 4; ++b) {
+      if (nbytes[b] == 0) continue;
+      MC_HIP(hipMemcpyAsync(dst[b], static_cast<const uint8_t*>(src[b]) + nbytes[b] * next->first_flat,
+                            nbytes[b] * (size_t)E, hipMemcpyHostToDevice, next->copy));
+    }
+    if (next->done) MC_HIP(hipEventRecord(next->done, next->copy));
+  }
+  if (T == 0) return MC_OK;
+  MC_REQUIRE(x_bf16 && ids && w && ws && y_bf16, "moe_experts_prefill: NULL pointer");
+
+  PrefillWs pw{};
+  ws_layout(T, k, E, H, I, &pw, static_cast<uint8_t*>(ws));
+  if ((rc = sort_launch(ids, T, k, n_tok, E, pw, s)) != MC_OK) return rc;
+
+  PrefillArgs a{};
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.w = w;
+  a.T = T;
+  a.k = k;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.gu = static_cast<const uint8_t*>(layer_buf->gate_up);
+  a.gus = static_cast<const uint8_t*>(layer_buf->gate_up_scale);
+  a.dn = static_cast<const uint8_t*>(layer_buf->down);
+  a.dns = static_cast<const uint8_t*>(layer_buf->down_scale);
+  a.ws = pw;
+  // tile count bound: sum_e ceil(n_e / BM) <= T*k / BM + E
+  const int max_mt = (T * k) / kP_BM + E;
+  a.n_nb = I / kP_GU_Cols;
+  int g = max_mt * a.n_nb;
+  g = (g + 7) & ~7;
+  hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g), dim3(kP_Threads), 0, s, a);
+  MC_LAUNCH_CHECK();
+  a.n_nb = H / kP_DN_Cols;
+  g = max_mt * a.n_nb;
+  g = (g + 7) & ~7;
+  hipLaunchKernelGGL(prefill_down_kernel, dim3(g), dim3(kP_Threads), 0, s, a);
+  MC_LAUNCH_CHECK();
+  const int64_t n4 = (int64_t)T * H / 4;
+  int64_t gc = (n4 + 255) / 256;
+  if (gc > 8192) gc = 8192;
+  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)gc), dim3(256), 0, s, ids, T, k, E, H,
+                     n_tok, pw.yr, static_cast<uint16_t*>(y_bf16));
+  MC_LAUNCH_CHECK();
+  return MC_OK;
+}

@@ -218,6 +218,62 @@ int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w,
 
 
 /* ------------------------------------------------------------------------- */
+/* Prefill                                                                   */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Stable grouping of a prefill chunk's routes by expert (the token sort in front of
+ * the grouped GEMM; [jjl357] "6.8": grouped GPU execution).  Route r = t*k + j for
+ * t < *n_tok (NULL = T) with 0 <= ids[r] < E:
+ *   counts  [E]    routes per expert
+ *   offsets [E+1]  exclusive prefix sum of counts
+ *   perm    [T*k]  perm[offsets[e] .. offsets[e+1]) = the routes of expert e in
+ *                  ascending r (the other entries are left untouched)
+ * ws: device scratch of at least E*16 + (E+1)*4 bytes.  All device memory.
+ * E <= 1024.
+ */
+int mc_prefill_sort_routes(const int32_t* ids, int32_t T, int32_t k, const int32_t* n_tok,
+                           int32_t E, void* ws, size_t ws_bytes, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, hipStream_t s);
+
+/*
+ * Whole-layer prefetch of the next layer's experts ([jjl357] "4.2 双缓冲时间线":
+ * buffer B is filled over the host link while buffer A computes).  On stream `copy`:
+ * wait for dst_free (may be NULL), copy host entries [first_flat, first_flat + E) of
+ * every bank into dst entries [0, E) with hipMemcpyAsync (SDMA), record done (may be
+ * NULL).  The caller makes the compute stream wait on `done` before using dst and
+ * records dst_free after the last kernel that reads dst's previous contents.
+ */
+typedef struct {
+  const mc_banks* host_src;  /* pinned host banks by flat id */
+  int64_t first_flat;        /* flat id of expert 0 of the next layer (= layer * E) */
+  const mc_banks* dst;       /* device layer buffer, >= E entries */
+  hipStream_t copy;
+  hipEvent_t dst_free;
+  hipEvent_t done;
+} mc_prefetch;
+
+size_t moe_experts_prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I);
+
+/*
+ * Prefill MoE layer over a resident layer buffer (entry e = expert e of the layer):
+ *   y[t] = bf16_rne( sum_j w[t][j] * Expert_{ids[t][j]}(x[t]) )   for t < *n_tok (else 0)
+ * computed as a stable token sort by expert, a grouped gate_up GEMM with the SwiGLU
+ * epilogue (bf16 MFMA; MXFP4 -> bf16 is exact), a grouped down GEMM (fp16 h and
+ * MXFP4 -> fp16 weights, exact for block exponents X-127 in [-23, 13]; fp16 MFMA),
+ * fp32 accumulation, and a fixed-order sum of each token's k gated route outputs.
+ * If next != NULL the next layer's prefetch (see mc_prefetch) is enqueued first on
+ * its own stream, so it overlaps this layer's compute.
+ *   x bf16 [T][H], ids int32 [T][k] (expert-in-layer; invalid ids contribute nothing),
+ *   w fp32 [T][k], y bf16 [T][H]; ws of moe_experts_prefill_ws_bytes(T, k, E, H, I).
+ * MXFP4 only; H % 256 == 0, I % 128 == 0, E <= 1024.
+ */
+int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const float* w, int32_t T,
+                        int32_t k, const int32_t* n_tok, int32_t E, const mc_banks* layer_buf,
+                        void* ws, size_t ws_bytes, void* y_bf16, hipStream_t s,
+                        const mc_prefetch* next);
+
+/* ------------------------------------------------------------------------- */
 /* Hybrid split / merge and the host branch                                  */
 /* ------------------------------------------------------------------------- */
 
