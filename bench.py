@@ -39,6 +39,8 @@ def _parse():
     ap.add_argument("--cpu-tokens", type=int, default=1, help="decode tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=5)
     return ap.parse_args()
 
 
@@ -51,6 +53,12 @@ def build_host_pool(cfg, torch):
     import synth
     from expert_cache_offloaded_amd.runtime import alloc_banks
     banks = alloc_banks(cfg.n_flat, cfg.H, cfg.I, cfg.fmt, pin=True)
+    fill_host_pool(cfg, banks)
+    return banks, {k: v.numpy() for k, v in banks.items()}
+
+
+def fill_host_pool(cfg, banks):
+    import synth
     views = {k: v.numpy() for k, v in banks.items()}
     t0 = time.time()
 
@@ -64,7 +72,6 @@ def build_host_pool(cfg, torch):
     with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
         list(ex.map(one, range(cfg.n_flat)))
     log("host pool ready (%.0f s)" % (time.time() - t0))
-    return banks, views
 
 
 def main():
@@ -213,7 +220,124 @@ def main():
     # ------------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, tr, logits, xs, host_np, sh_np, args.cpu_tokens)
+
+    # ------------------------------------------------------------------ prefill
+    if not args.no_prefill:
+        del host_t, host_np, host, layers, pool, cache, shared
+        torch.cuda.empty_cache()
+        pre, roof = bench_prefill(args, torch, L, synth)
+        out["prefill"] = pre
+        out["roofline_prefill"] = roof
     print(json.dumps(out), flush=True)
+
+
+def bench_prefill(args, torch, L, synth):
+    """8192-token prefill over 4 DeepSeek-V4-Flash-shaped MoE layers (E=256 top-6, H=4096,
+    I=2048, MXFP4, uniform routing): grouped-GEMM throughput on a resident layer, and the
+    whole-layer double buffer streaming each next layer's 256 experts host -> HBM."""
+    from expert_cache_offloaded_amd.runtime import alloc_banks
+    cfg = synth.CONFIGS["prefill"]
+    T, E, k, H, I = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I
+    dev = "cuda"
+    log("prefill: pinned pool of %d layers x %d experts" % (cfg.L, E))
+    host_t = alloc_banks(cfg.n_flat, H, I, cfg.fmt, pin=True)
+    fill_host_pool(cfg, host_t)
+    host = L.make_banks(cfg.fmt, H, I, host_t)
+    bufs_t = [alloc_banks(E, H, I, cfg.fmt, device=dev) for _ in range(2)]
+    bufs = [L.make_banks(cfg.fmt, H, I, b) for b in bufs_t]
+    x = torch.from_numpy(synth.activations(cfg, 0).view(np.int16)).to(dev)
+    logits = [torch.from_numpy(synth.uniform_logits(cfg, layer=l)).to(dev) for l in range(cfg.L)]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.prefill_ws_bytes(T, k, E, H, I), dtype=torch.uint8, device=dev)
+    ys = [torch.empty((T, H), dtype=torch.int16, device=dev) for _ in range(cfg.L)]
+    layer_bytes = synth.expert_bytes(H, I, cfg.fmt) * E
+    flops = 6.0 * H * I * T * k
+
+    def copy_layer(l, b, stream):
+        with torch.cuda.stream(stream):
+            for name in bufs_t[b]:
+                bufs_t[b][name].copy_(host_t[name][l * E:(l + 1) * E], non_blocking=True)
+
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+
+    # resident layer: route + sort + grouped GEMMs + combine, graph replays timed with events
+    copy_layer(0, 0, comp)
+    torch.cuda.synchronize()
+
+    def layer_compute(l, b, nxt=None):
+        L.moe_route(logits[l], k, 1, ids, w)
+        L.moe_experts_prefill(x, ids, w, None, E, bufs[b], ws, ys[l], nxt)
+
+    layer_compute(0, 0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer_compute(0, 0)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(args.prefill_reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        g.replay()
+        e1.record(comp)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    t_comp = float(np.median(ts))
+    log("prefill compute (resident layer): %.3f ms, %.0f tok/s, %.0f TFLOP/s"
+        % (t_comp, T / t_comp * 1e3, flops / t_comp * 1e-9))
+
+    # serialized: copy a layer, then compute it
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for l in range(cfg.L):
+        copy_layer(l, 0, comp)
+        layer_compute(l, 0)
+    torch.cuda.synchronize()
+    t_serial = (time.perf_counter() - t0) * 1e3 / cfg.L
+
+    # double buffer: layer l computes from buffer l % 2 while l+1 streams into the other
+    done = [torch.cuda.Event() for _ in range(2)]
+    free = [torch.cuda.Event() for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    copy_layer(0, 0, copy)
+    done[0].record(copy)
+    for l in range(cfg.L):
+        b = l % 2
+        comp.wait_event(done[b])
+        nxt = None
+        if l + 1 < cfg.L:
+            copy.wait_event(free[1 - b])
+            nxt = L.make_prefetch(host, (l + 1) * E, bufs[1 - b], copy)
+        layer_compute(l, b, nxt)
+        if nxt is not None:
+            done[1 - b].record(copy)
+        free[b].record(comp)
+    torch.cuda.synchronize()
+    t_pipe_total = (time.perf_counter() - t0) * 1e3
+    t_pipe = t_pipe_total / cfg.L
+    t_link = t_serial - t_comp
+    link_gbs = layer_bytes / (t_link * 1e-3) / 1e9
+    ideal = (t_comp + t_link) / max(t_comp, t_link)
+    log("prefill serialized %.1f ms/layer, double-buffered %.1f ms/layer (overlap %.3f of ideal %.3f)"
+        % (t_serial, t_pipe, t_serial / t_pipe, ideal))
+    pre = {"workload": "8192-token prefill, 4 MoE layers, E=256 top-6 uniform routing, H=4096, I=2048, "
+                       "MXFP4 experts, double-buffered 256-expert layer pool",
+           "tokens": T, "layers": cfg.L,
+           "compute_ms_per_layer": round(t_comp, 4), "compute_tok_s": round(T / t_comp * 1e3, 1),
+           "serial_ms_per_layer": round(t_serial, 3), "pipelined_ms_per_layer": round(t_pipe, 3),
+           "pipelined_tok_s": round(T / t_pipe * 1e3, 1), "layer_pool_bytes": int(layer_bytes),
+           "link_gbs": round(link_gbs, 2), "overlap_speedup": round(t_serial / t_pipe, 3),
+           "overlap_ideal": round(ideal, 3)}
+    tflops = flops / t_comp * 1e-9
+    roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+            "frac": round(tflops / 2500.0, 4), "traffic": None,
+            "kernel": "moe_experts_prefill (route + sort + gate_up + down + combine)",
+            "flop_per_launch": flops, "ms_per_launch": round(t_comp, 4)}
+    return pre, roof
 
 
 def cpu_baseline(cfg, tr, logits, xs, host_np, sh_np, n_tokens):
