@@ -37,6 +37,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kP_BM = 64;          // rows per tile
 constexpr int kP_KS = 128;         // K per pipeline step
@@ -229,47 +230,79 @@ __device__ __forceinline__ f16x8_t fp4x8_f16(uint32_t v, float s) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
 
-// ---------------------------------------------------------------- gate_up GEMM
+// ---------------------------------------------------------------- grouped GEMM
+//
+// One kernel template for both GEMMs.  Block = 4 waves = 64 sorted rows x 4 x 64 weight
+// rows; K in steps of 128.  Pipeline: the activation tile of step s+2 and the weight
+// operands of step s+2 are loaded into registers while step s computes; the tile of
+// step s+1 (loaded one step earlier) is then written to the other half of an LDS
+// double buffer.  The LDS tile is XOR-swizzled (16-byte chunk c of row r lives at
+// c ^ (r & 15)) so the 16 rows an MFMA operand read touches fall in different banks.
+// For the real shapes the K loop is fully unrolled so every register ring index is
+// static and the compiler's wait counts stay exact.
 
+constexpr int kP_StageBytes = kP_BM * kP_KS * 2;     // 16 KiB per activation tile
+
+struct GemmStage {
+  u32x4_t b[4];       // one MX block (16 B) per column tile
+  uint32_t s[4];      // its scale byte
+};
+
+template <int MODE, int NSTEPS>   // MODE 0: gate_up (bf16, SwiGLU), 1: down (fp16, gated rows)
 __global__ void __launch_bounds__(kP_Threads)
-prefill_gate_up_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kP_BM][kP_LdsRow];
+prefill_gemm_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kP_StageBytes];
   int e, row0, nrows, nb;
   if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, I = a.I;
-  const int c0 = nb * kP_GU_Cols + wave * 32;              // first intermediate column of the wave
+  const int K = MODE == 0 ? H : I;
+  const int nsteps = NSTEPS > 0 ? NSTEPS : K / kP_KS;
 
-  // activation rows: thread loads 4 x 16 B per step; chunk = tid + 256 q -> (row, 16-B piece)
-  const uint16_t* arow[4];
-  int a_r[4], a_c[4];
+  // the 4 activation chunks this thread moves per step: slot i of the tile holds
+  // row i / 16, logical chunk (i % 16) ^ (row % 16)
+  const uint16_t* aptr[4];
+  int aslot[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int chunk = tid + kP_Threads * q;
-    a_r[q] = chunk >> 4;
-    a_c[q] = chunk & 15;
-    const int rr = min(a_r[q], nrows - 1);
-    const int route = a.ws.perm[row0 + rr];
-    arow[q] = a.x + (size_t)(route / a.k) * H;
+    const int i = tid + kP_Threads * q;
+    const int r = i >> 4;
+    const int c = (i & 15) ^ (r & 15);
+    const int rr = min(r, nrows - 1);
+    const uint16_t* rowp;
+    if (MODE == 0) rowp = a.x + (size_t)(a.ws.perm[row0 + rr] / a.k) * H;
+    else rowp = reinterpret_cast<const uint16_t*>(a.ws.h) + (size_t)(row0 + rr) * I;
+    aptr[q] = rowp + c * 8;
+    aslot[q] = i * 16;
   }
-  // weight rows of the lane's 4 column tiles (2 gate, 2 up)
-  const size_t row_b = (size_t)H / 2, row_s = (size_t)H / 32;
-  const uint8_t* wbase = a.gu + (size_t)e * (2 * (size_t)I * row_b);
-  const uint8_t* sbase = a.gus + (size_t)e * (2 * (size_t)I * row_s);
+  // weight rows of the lane's 4 column tiles
   const uint8_t* brow[4];
   const uint8_t* bsc[4];
+  int c0;
+  {
+    const size_t row_b = (size_t)K / 2, row_s = (size_t)K / 32;
+    const uint8_t* wbase;
+    const uint8_t* sbase;
+    if (MODE == 0) {
+      wbase = a.gu + (size_t)e * (2 * (size_t)I * row_b);
+      sbase = a.gus + (size_t)e * (2 * (size_t)I * row_s);
+      c0 = nb * kP_GU_Cols + wave * 32;
+    } else {
+      wbase = a.dn + (size_t)e * ((size_t)H * row_b);
+      sbase = a.dns + (size_t)e * ((size_t)H * row_s);
+      c0 = nb * kP_DN_Cols + wave * 64;
+    }
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int col = (nt & 1) * 16 + (lane & 15);
-    const int wr = (nt < 2 ? 0 : I) + c0 + col;
-    brow[nt] = wbase + (size_t)wr * row_b;
-    bsc[nt] = sbase + (size_t)wr * row_s;
+    for (int nt = 0; nt < 4; ++nt) {
+      int wr;
+      if (MODE == 0) wr = (nt < 2 ? 0 : I) + c0 + (nt & 1) * 16 + (lane & 15);
+      else wr = c0 + nt * 16 + (lane & 15);
+      brow[nt] = wbase + (size_t)wr * row_b;
+      bsc[nt] = sbase + (size_t)wr * row_s;
+    }
   }
-  const int kq = lane >> 4;                                 // which MX block of the step
+  const int kq = lane >> 4;                             // MX block of the step this lane owns
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -277,180 +310,119 @@ prefill_gate_up_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = H / kP_KS;
-  uint4 av[4];
-  uint4 bv[4];
-  uint32_t bs[4];
-  auto load_step = [&](int s) {
+  // register rings: three weight stages, two activation tiles (named, so that every
+  // index is static and nothing is placed in scratch memory)
+  GemmStage st0, st1, st2;
+  u32x4_t ar0[4], ar1[4];
+  auto issue = [&](int s, GemmStage& g, u32x4_t* ar) {
     const int k0 = s * kP_KS;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      av[q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + a_c[q] * 8);
+    for (int q = 0; q < 4; ++q) ar[q] = *reinterpret_cast<const u32x4_t*>(aptr[q] + k0);
+    const int kb = (k0 >> 5) + kq;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int kb = (k0 >> 5) + kq;
-      bv[nt] = *reinterpret_cast<const uint4*>(brow[nt] + (size_t)kb * 16);
-      bs[nt] = bsc[nt][kb];
+      g.b[nt] = *reinterpret_cast<const u32x4_t*>(brow[nt] + (size_t)kb * 16);
+      g.s[nt] = bsc[nt][kb];
     }
   };
-  load_step(0);
+  auto store_a = [&](const u32x4_t* ar, int buf) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[0][a_r[q]][a_c[q] * 8]) = av[q];
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    uint4 bcur[4];
-    float scur[4];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(&sA[buf][aslot[q]]) = ar[q];
+  };
+  auto compute = [&](const GemmStage& g, int buf) {
+    float sc[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      bcur[nt] = bv[nt];
-      scur[nt] = e8m0_to_f32(bs[nt]);
-    }
-    if (s + 1 < nsteps) load_step(s + 1);
-    // 4 MFMA K-steps of 8 elements per lane: lane group kq owns MX block kq of the step
+    for (int nt = 0; nt < 4; ++nt) sc[nt] = e8m0_to_f32(g.s[nt]);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t bop[4];
+      const int phys = (kq * 4 + ks) ^ (lane & 15);
+      if (MODE == 0) {
+        bf16x8_t bop[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_bf16(u4_get(bcur[nt], ks), scur[nt]);
+        for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_bf16(g.b[nt][ks], sc[nt]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8_t aop =
-            *reinterpret_cast<const bf16x8_t*>(&sA[cur][mt * 16 + (lane & 15)][kq * 32 + ks * 8]);
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8_t aop = *reinterpret_cast<const bf16x8_t*>(
+              &sA[buf][(mt * 16 + (lane & 15)) * 256 + phys * 16]);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
+          for (int nt = 0; nt < 4; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
+        }
+      } else {
+        f16x8_t bop[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_f16(g.b[nt][ks], sc[nt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f16x8_t aop = *reinterpret_cast<const f16x8_t*>(
+              &sA[buf][(mt * 16 + (lane & 15)) * 256 + phys * 16]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
+        }
       }
-    }
-    if (s + 1 < nsteps) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[cur ^ 1][a_r[q]][a_c[q] * 8]) = av[q];
-    }
-    __syncthreads();
-  }
-
-  // epilogue: h = silu(g) * u -> fp16, rows of this tile
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = mt * 16 + (lane >> 4) * 4 + j;
-      if (r >= nrows) continue;
-      _Float16* hrow = a.ws.h + (size_t)(row0 + r) * I;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float g = acc[mt][nt][j], u = acc[mt][nt + 2][j];
-        hrow[c0 + nt * 16 + (lane & 15)] = (_Float16)(silu(g) * u);
-      }
-    }
-}
-
-// ---------------------------------------------------------------- down GEMM
-
-__global__ void __launch_bounds__(kP_Threads)
-prefill_down_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kP_BM][kP_LdsRow];
-  int e, row0, nrows, nb;
-  if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = a.H, I = a.I;
-  const int c0 = nb * kP_DN_Cols + wave * 64;              // first output column of the wave
-
-  const _Float16* arow[4];
-  int a_r[4], a_c[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int chunk = tid + kP_Threads * q;
-    a_r[q] = chunk >> 4;
-    a_c[q] = chunk & 15;
-    const int rr = min(a_r[q], nrows - 1);
-    arow[q] = a.ws.h + (size_t)(row0 + rr) * I;
-  }
-  const size_t row_b = (size_t)I / 2, row_s = (size_t)I / 32;
-  const uint8_t* wbase = a.dn + (size_t)e * ((size_t)H * row_b);
-  const uint8_t* sbase = a.dns + (size_t)e * ((size_t)H * row_s);
-  const uint8_t* brow[4];
-  const uint8_t* bsc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int wr = c0 + nt * 16 + (lane & 15);
-    brow[nt] = wbase + (size_t)wr * row_b;
-    bsc[nt] = sbase + (size_t)wr * row_s;
-  }
-  const int kq = lane >> 4;
-
-  f32x4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nsteps = I / kP_KS;
-  uint4 av[4];
-  uint4 bv[4];
-  uint32_t bs[4];
-  auto load_step = [&](int s) {
-    const int k0 = s * kP_KS;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      av[q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + a_c[q] * 8);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int kb = (k0 >> 5) + kq;
-      bv[nt] = *reinterpret_cast<const uint4*>(brow[nt] + (size_t)kb * 16);
-      bs[nt] = bsc[nt][kb];
     }
   };
-  load_step(0);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[0][a_r[q]][a_c[q] * 8]) = av[q];
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    uint4 bcur[4];
-    float scur[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      bcur[nt] = bv[nt];
-      scur[nt] = e8m0_to_f32(bs[nt]);
-    }
-    if (s + 1 < nsteps) load_step(s + 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      f16x8_t bop[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_f16(u4_get(bcur[nt], ks), scur[nt]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f16x8_t aop =
-            *reinterpret_cast<const f16x8_t*>(&sA[cur][mt * 16 + (lane & 15)][kq * 32 + ks * 8]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
-      }
-    }
-    if (s + 1 < nsteps) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&sA[cur ^ 1][a_r[q]][a_c[q] * 8]) = av[q];
-    }
+  // step s: load step s+2 into (g2, ar_ld), compute step s (g, LDS half s & 1), then
+  // publish the tile of step s+1 (ar_st, loaded one step earlier) to the other half
+  auto step = [&](int s, GemmStage& g, GemmStage& g2, u32x4_t* ar_ld, const u32x4_t* ar_st) {
+    if (s >= nsteps) return;
+    if (s + 2 < nsteps) issue(s + 2, g2, ar_ld);
+    compute(g, s & 1);
+    if (s + 1 < nsteps) store_a(ar_st, (s & 1) ^ 1);
     __syncthreads();
+  };
+  // one period of the rings (6 steps); stage s % 3, activation tile s % 2
+  auto period = [&](int s0) {
+    step(s0 + 0, st0, st2, ar0, ar1);
+    step(s0 + 1, st1, st0, ar1, ar0);
+    step(s0 + 2, st2, st1, ar0, ar1);
+    step(s0 + 3, st0, st2, ar1, ar0);
+    step(s0 + 4, st1, st0, ar0, ar1);
+    step(s0 + 5, st2, st1, ar1, ar0);
+  };
+
+  issue(0, st0, ar0);
+  if (nsteps > 1) issue(1, st1, ar1);
+  store_a(ar0, 0);
+  __syncthreads();
+  if (NSTEPS > 0) {
+#pragma unroll
+    for (int s0 = 0; s0 < NSTEPS; s0 += 6) period(s0);
+  } else {
+    for (int s0 = 0; s0 < nsteps; s0 += 6) period(s0);
   }
 
-  // epilogue: the route's own output row, scaled by its gate
+  if (MODE == 0) {
+    // h = silu(g) * u -> fp16, rows of this tile
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = mt * 16 + (lane >> 4) * 4 + j;
-      if (r >= nrows) continue;
-      const int route = a.ws.perm[row0 + r];
-      const float g = a.w[route];
-      float* yrow = a.ws.yr + (size_t)route * H;
+      for (int j = 0; j < 4; ++j) {
+        const int r = mt * 16 + (lane >> 4) * 4 + j;
+        if (r >= nrows) continue;
+        _Float16* hrow = a.ws.h + (size_t)(row0 + r) * I;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) yrow[c0 + nt * 16 + (lane & 15)] = g * acc[mt][nt][j];
-    }
+        for (int nt = 0; nt < 2; ++nt) {
+          const float g = acc[mt][nt][j], u = acc[mt][nt + 2][j];
+          hrow[c0 + nt * 16 + (lane & 15)] = (_Float16)(silu(g) * u);
+        }
+      }
+  } else {
+    // the route's own output row, scaled by its gate
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = mt * 16 + (lane >> 4) * 4 + j;
+        if (r >= nrows) continue;
+        const int route = a.ws.perm[row0 + r];
+        const float g = a.w[route];
+        float* yrow = a.ws.yr + (size_t)route * H;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) yrow[c0 + nt * 16 + (lane & 15)] = g * acc[mt][nt][j];
+      }
+  }
 }
 
 // ---------------------------------------------------------------- combine
@@ -595,12 +567,18 @@ extern "C" int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const
   a.n_nb = I / kP_GU_Cols;
   int g = max_mt * a.n_nb;
   g = (g + 7) & ~7;
-  hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g), dim3(kP_Threads), 0, s, a);
+  if (H / kP_KS == 32)
+    hipLaunchKernelGGL((prefill_gemm_kernel<0, 32>), dim3(g), dim3(kP_Threads), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_gemm_kernel<0, 0>), dim3(g), dim3(kP_Threads), 0, s, a);
   MC_LAUNCH_CHECK();
   a.n_nb = H / kP_DN_Cols;
   g = max_mt * a.n_nb;
   g = (g + 7) & ~7;
-  hipLaunchKernelGGL(prefill_down_kernel, dim3(g), dim3(kP_Threads), 0, s, a);
+  if (I / kP_KS == 16)
+    hipLaunchKernelGGL((prefill_gemm_kernel<1, 16>), dim3(g), dim3(kP_Threads), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_gemm_kernel<1, 0>), dim3(g), dim3(kP_Threads), 0, s, a);
   MC_LAUNCH_CHECK();
   const int64_t n4 = (int64_t)T * H / 4;
   int64_t gc = (n4 + 255) / 256;
