@@ -46,6 +46,7 @@ constexpr int kP_GU_Cols = 128;    // intermediate columns per gate_up tile (32 
 constexpr int kP_DN_Cols = 256;    // output columns per down tile (64 per wave)
 constexpr int kP_LdsRow = kP_KS + 8;   // padded LDS row (elements)
 constexpr int kP_MaxE = 1024;
+constexpr int kP_MaxK = 8192;      // largest H or I (sizes the generic kernel's scale table)
 
 struct PrefillWs {
   int32_t* counts;      // [E]
@@ -249,10 +250,20 @@ struct GemmStage {
   uint32_t s[4];      // its scale byte
 };
 
+// Block scale table in LDS: the 256 weight rows of a block x (K / 32) e8m0 bytes, one
+// dword per K step (its 4 MX blocks).  Row stride kScaleRow(NSTEPS) bytes; the 16-byte
+// chunk c of row r is stored at chunk c ^ (r % 16 * stride / 256), so the 16 rows one
+// scale read touches land in distinct banks.
+__host__ __device__ constexpr int scale_row_bytes(int nsteps_fixed) {
+  return nsteps_fixed > 0 ? nsteps_fixed * 4 : kP_MaxK / 32;
+}
+
 template <int MODE, int NSTEPS>   // MODE 0: gate_up (bf16, SwiGLU), 1: down (fp16, gated rows)
-__global__ void __launch_bounds__(kP_Threads)
+__global__ void __launch_bounds__(kP_Threads, 2)   // two blocks per CU: <= 256 registers per lane
 prefill_gemm_kernel(PrefillArgs a) {
+  constexpr int SROW = scale_row_bytes(NSTEPS);
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kP_StageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sS[kP_Threads * SROW];
   int e, row0, nrows, nb;
   if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -276,9 +287,9 @@ prefill_gemm_kernel(PrefillArgs a) {
     aptr[q] = rowp + c * 8;
     aslot[q] = i * 16;
   }
-  // weight rows of the lane's 4 column tiles
+  // weight rows of the lane's 4 column tiles; srow_g = scales of table row tid
   const uint8_t* brow[4];
-  const uint8_t* bsc[4];
+  const uint8_t* srow_g;
   int c0;
   {
     const size_t row_b = (size_t)K / 2, row_s = (size_t)K / 32;
@@ -293,14 +304,13 @@ prefill_gemm_kernel(PrefillArgs a) {
       sbase = a.dns + (size_t)e * ((size_t)H * row_s);
       c0 = nb * kP_DN_Cols + wave * 64;
     }
+    // table row tid = wave * 64 + nt * 16 + r holds the scales of weight row wrow(nt, r)
+    auto wrow = [&](int nt, int r) {
+      return MODE == 0 ? (nt < 2 ? 0 : I) + c0 + (nt & 1) * 16 + r : c0 + nt * 16 + r;
+    };
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      int wr;
-      if (MODE == 0) wr = (nt < 2 ? 0 : I) + c0 + (nt & 1) * 16 + (lane & 15);
-      else wr = c0 + nt * 16 + (lane & 15);
-      brow[nt] = wbase + (size_t)wr * row_b;
-      bsc[nt] = sbase + (size_t)wr * row_s;
-    }
+    for (int nt = 0; nt < 4; ++nt) brow[nt] = wbase + (size_t)wrow(nt, lane & 15) * row_b;
+    srow_g = sbase + (size_t)wrow((tid >> 4) & 3, tid & 15) * row_s;
   }
   const int kq = lane >> 4;                             // MX block of the step this lane owns
 
@@ -320,10 +330,14 @@ prefill_gemm_kernel(PrefillArgs a) {
     for (int q = 0; q < 4; ++q) ar[q] = *reinterpret_cast<const u32x4_t*>(aptr[q] + k0);
     const int kb = (k0 >> 5) + kq;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      g.b[nt] = *reinterpret_cast<const u32x4_t*>(brow[nt] + (size_t)kb * 16);
-      g.s[nt] = bsc[nt][kb];
-    }
+    for (int nt = 0; nt < 4; ++nt) g.b[nt] = *reinterpret_cast<const u32x4_t*>(brow[nt] + (size_t)kb * 16);
+  };
+  // scale byte of step s for the lane's 4 column tiles, from the LDS table
+  const int sw = ((lane & 15) * SROW) >> 8;
+  auto scales = [&](int s, GemmStage& g) {
+    const int off = (((s >> 2) ^ sw) << 4) + ((s & 3) << 2) + kq;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) g.s[nt] = sS[(wave * 64 + nt * 16 + (lane & 15)) * SROW + off];
   };
   auto store_a = [&](const u32x4_t* ar, int buf) {
 #pragma unroll
@@ -332,7 +346,13 @@ prefill_gemm_kernel(PrefillArgs a) {
   auto compute = [&](const GemmStage& g, int buf) {
     float sc[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) sc[nt] = e8m0_to_f32(g.s[nt]);
+    for (int nt = 0; nt < 4; ++nt) {
+      // the empty asm anchors the scale decode here: hoisted next to its load it
+      // would wait for that load within the step that issued it
+      uint32_t raw = g.s[nt];
+      asm volatile("" : "+v"(raw));
+      sc[nt] = e8m0_to_f32(raw);
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int phys = (kq * 4 + ks) ^ (lane & 15);
@@ -367,7 +387,12 @@ prefill_gemm_kernel(PrefillArgs a) {
   // publish the tile of step s+1 (ar_st, loaded one step earlier) to the other half
   auto step = [&](int s, GemmStage& g, GemmStage& g2, u32x4_t* ar_ld, const u32x4_t* ar_st) {
     if (s >= nsteps) return;
-    if (s + 2 < nsteps) issue(s + 2, g2, ar_ld);
+    if (s + 2 < nsteps) {
+      issue(s + 2, g2, ar_ld);
+      scales(s + 2, g2);
+    }
+    // keep the loads ahead of this step's MFMAs (the scheduler would sink them)
+    __builtin_amdgcn_sched_barrier(0);
     compute(g, s & 1);
     if (s + 1 < nsteps) store_a(ar_st, (s & 1) ^ 1);
     __syncthreads();
@@ -382,10 +407,26 @@ prefill_gemm_kernel(PrefillArgs a) {
     step(s0 + 5, st2, st1, ar1, ar0);
   };
 
+  // prologue: this thread's row of the scale table, then the first two steps
+  {
+    uint8_t* dst = sS + tid * SROW;
+    const int swt = ((tid & 15) * SROW) >> 8;
+    if ((nsteps & 3) == 0) {
+      for (int c = 0; c < (nsteps >> 2); ++c)
+        *reinterpret_cast<u32x4_t*>(dst + ((c ^ swt) << 4)) =
+            *reinterpret_cast<const u32x4_t*>(srow_g + c * 16);
+    } else {
+      for (int d = 0; d < nsteps; ++d)
+        *reinterpret_cast<uint32_t*>(dst + (((d >> 2) ^ swt) << 4) + ((d & 3) << 2)) =
+            *reinterpret_cast<const uint32_t*>(srow_g + d * 4);
+    }
+  }
   issue(0, st0, ar0);
   if (nsteps > 1) issue(1, st1, ar1);
   store_a(ar0, 0);
   __syncthreads();
+  scales(0, st0);
+  if (nsteps > 1) scales(1, st1);
   if (NSTEPS > 0) {
 #pragma unroll
     for (int s0 = 0; s0 < NSTEPS; s0 += 6) period(s0);
@@ -512,6 +553,8 @@ extern "C" int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const
   MC_REQUIRE(H % kP_DN_Cols == 0 && I % kP_GU_Cols == 0 && H % kP_KS == 0 && I % kP_KS == 0,
              "moe_experts_prefill: H=%d must be a multiple of %d and I=%d of %d", H, kP_DN_Cols, I,
              kP_GU_Cols);
+  MC_REQUIRE(H <= kP_MaxK && I <= kP_MaxK, "moe_experts_prefill: H=%d and I=%d must be <= %d", H, I,
+             kP_MaxK);
   MC_REQUIRE(ws_bytes >= moe_experts_prefill_ws_bytes(T, k, E, H, I),
              "moe_experts_prefill: workspace %zu < %zu bytes", ws_bytes,
              moe_experts_prefill_ws_bytes(T, k, E, H, I));
