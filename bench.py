@@ -41,6 +41,9 @@ def _parse():
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--fill-through", action="store_true",
+                    help="let the expert pass read filled experts from the host and write their slots "
+                         "(default: mc_fill_slots copy first)")
     return ap.parse_args()
 
 
@@ -110,7 +113,8 @@ def main():
     cache = CacheState(cfg.L, cfg.E, cfg.S)
     cache.reset()
     layers = [DecodeLayer(cache, host, pool, shared, DecodeBuffers(1, cfg.k, cfg.H, cfg.I),
-                          frac_q16=1 << 16, renorm=cfg.renorm) for _ in range(cfg.L)]
+                          frac_q16=1 << 16, renorm=cfg.renorm, fill_through=args.fill_through)
+              for _ in range(cfg.L)]
     logits_buf = torch.empty_like(logits_all[0])
     x_buf = torch.empty_like(x_all[0])
 

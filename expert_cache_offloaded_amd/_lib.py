@@ -44,6 +44,11 @@ class Prefetch(C.Structure):
                 ("copy", C.c_void_p), ("dst_free", C.c_void_p), ("done", C.c_void_p)]
 
 
+class FillList(C.Structure):
+    _fields_ = [("host", C.POINTER(Banks)), ("fill_flat", C.c_void_p), ("fill_slot", C.c_void_p),
+                ("n_fill", C.c_void_p), ("kcap", C.c_int32)]
+
+
 class Hybrid(C.Structure):
     _fields_ = [("x_bf16", C.c_void_p), ("ids_raw", C.c_void_p), ("slots", C.c_void_p),
                 ("w", C.c_void_p), ("T", C.c_int32), ("k", C.c_int32), ("layer", C.c_int32),
@@ -66,7 +71,7 @@ _SIGS = {
     "mc_fill_slots": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, _P]),
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
-                                     _P, C.c_size_t, _P, _I32, _P, _P]),
+                                     _P, C.c_size_t, _P, _I32, _P, _P, C.POINTER(FillList)]),
     "mc_prefill_sort_routes": (C.c_int, [_P, _I32, _I32, _P, _I32, _P, C.c_size_t, _P, _P, _P, _P]),
     "moe_experts_prefill_ws_bytes": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "moe_experts_prefill": (C.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, C.POINTER(Banks), _P, C.c_size_t,
@@ -187,13 +192,27 @@ def decode_ws_bytes(T: int, k: int, I: int) -> int:
     return int(lib().moe_experts_decode_ws_bytes(T, k, I))
 
 
+def make_fill_list(host: Banks, fill_flat, fill_slot, n_fill) -> FillList:
+    """Fill list of a lookup call for fill-through decode (device tensors)."""
+    f = FillList()
+    f.host = C.pointer(host)
+    f.fill_flat = _ptr(fill_flat)
+    f.fill_slot = _ptr(fill_slot)
+    f.n_fill = _ptr(n_fill)
+    f.kcap = fill_flat.numel()
+    f._keep = (host, fill_flat, fill_slot, n_fill)
+    return f
+
+
 def moe_experts_decode(x, slots, w, n_tok, pool: Banks, shared: Optional[Banks], ws, y_acc,
-                       accumulate: int = 1, y_bf16=None, stream=None) -> None:
+                       accumulate: int = 1, y_bf16=None, stream=None,
+                       fill: Optional[FillList] = None) -> None:
     T, k = slots.shape
     _check("moe_experts_decode", lib().moe_experts_decode(
         _ptr(x), _ptr(slots), _ptr(w), T, k, _ptr(n_tok), C.byref(pool),
         C.byref(shared) if shared is not None else None, _ptr(ws), ws.numel() * ws.element_size(),
-        _ptr(y_acc), accumulate, _ptr(y_bf16), _stream(stream)))
+        _ptr(y_acc), accumulate, _ptr(y_bf16), _stream(stream),
+        C.byref(fill) if fill is not None else None))
 
 
 

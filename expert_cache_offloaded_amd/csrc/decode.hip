@@ -21,6 +21,11 @@
 //      its rows first, then computes; the waves' partial sums meet in LDS and are
 //      added in a fixed order, so every output element is written once (no atomics,
 //      run-to-run identical).  The same pass writes the bf16 output when asked.
+// Fill-through: when the call carries the lookup's fill list, a unit whose slot is
+// being filled reads its rows from the pinned host entry instead (over the host
+// link) and stores them into the slot from the registers that hold them, so the
+// fill and the expert pass are one stream of loads.  gate_up records each route's
+// host source in the workspace; down reads it there.
 #include "mc_common.h"
 
 namespace mc {
@@ -35,6 +40,14 @@ constexpr int kMaxTok = 64;
 constexpr int kB_LdsBytes = 64 * 1024;
 
 // ---------------------------------------------------------------- chunk dots
+
+// 16-byte weight load marked non-temporal: every weight byte of a call is used once,
+// and the same form serves HBM slots and pinned host entries (fill-through).
+__device__ __forceinline__ uint4 stream_load16(const uint4* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // x pairs: packed bf16 pairs of the chunk's activations.
 // MXFP4 chunk: 32 elements, 16 B codes, one e8m0 scale; x: 16 dwords.
@@ -115,7 +128,35 @@ struct DecodeArgs {
   uint16_t* y_bf16;           // [T][H] or null
   int32_t accumulate;
   int32_t has_shared;
+  // fill-through (f_gu == nullptr: off): device views of the host banks, the list
+  const uint8_t* f_gu;
+  const uint8_t* f_gus;
+  const uint8_t* f_dn;
+  const uint8_t* f_dns;
+  int64_t n_host;
+  const int32_t* fill_flat;
+  const int32_t* fill_slot;
+  const int32_t* n_fill;
+  int32_t kcap;
+  int32_t* rsrc;              // [T*k] host flat id a route's weights come from, -1 = slot
 };
+
+// Host entry that fills `slot` in this call, or -1 (wave-uniform; lanes search the
+// list 64 entries at a time).
+__device__ int64_t fill_source(const DecodeArgs& a, int slot) {
+  const int lane = threadIdx.x & 63;
+  const int nf = min(max(*a.n_fill, 0), a.kcap);
+  for (int base = 0; base < nf; base += 64) {
+    const int i = base + lane;
+    const bool hit = i < nf && a.fill_slot[i] == slot;
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int64_t f = a.fill_flat[base + __builtin_ctzll(m)];
+      return (f >= 0 && f < a.n_host) ? f : -1;
+    }
+  }
+  return -1;
+}
 
 __device__ __forceinline__ int valid_tokens(const DecodeArgs& a) {
   return a.n_tok ? min(max(*a.n_tok, 0), a.T) : a.T;
@@ -180,14 +221,25 @@ gate_up_kernel(DecodeArgs a) {
 
   const uint8_t* gu;
   const uint8_t* gus = nullptr;
+  uint8_t* wb_gu = nullptr;        // fill-through: the slot entry the rows are stored to
+  uint8_t* wb_gus = nullptr;
+  int64_t src = -1;
   int slot = -1;
   if (shared_unit) {
     gu = a.sh_gu;
     gus = a.sh_gus;
   } else {
     slot = s_slot[s_first[u]];
-    gu = a.gu + (size_t)slot * (2 * (size_t)I * row_bytes);
-    if (FMT == MC_MXFP4) gus = a.gus + (size_t)slot * ((size_t)2 * I * H / 32);
+    const size_t per_gu = 2 * (size_t)I * row_bytes, per_gus = (size_t)2 * I * H / 32;
+    gu = a.gu + (size_t)slot * per_gu;
+    if (FMT == MC_MXFP4) gus = a.gus + (size_t)slot * per_gus;
+    if (a.f_gu) src = fill_source(a, slot);
+    if (src >= 0) {
+      wb_gu = const_cast<uint8_t*>(gu);
+      wb_gus = const_cast<uint8_t*>(gus);
+      gu = a.f_gu + (size_t)src * per_gu;
+      if (FMT == MC_MXFP4) gus = a.f_gus + (size_t)src * per_gus;
+    }
   }
 
   // all loads of the wave's 8 rows first (chunk index clamped; out-of-row lanes are
@@ -208,7 +260,7 @@ gate_up_kernel(DecodeArgs a) {
     const uint4* rp = reinterpret_cast<const uint4*>(gu + (size_t)row * row_bytes);
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      wv[r][q] = rp[cq[q]];
+      wv[r][q] = stream_load16(rp + cq[q]);
       if (FMT == MC_MXFP4) sb[r][q] = gus[(size_t)row * (H / 32) + cq[q]];
     }
   }
@@ -225,6 +277,7 @@ gate_up_kernel(DecodeArgs a) {
       if (r_next >= nr) break;
       route = r_next++;
       t = route / a.k;
+      if (blockIdx.y == 0 && threadIdx.x == 0) a.rsrc[route] = (int32_t)src;
     }
     const uint32_t* xrow = reinterpret_cast<const uint32_t*>(a.x + (size_t)t * H);
     uint32_t xp[CPL][ELEMS / 2];
@@ -267,6 +320,19 @@ gate_up_kernel(DecodeArgs a) {
       dst[i0 + lane] = silu(g) * up;
     }
   }
+  // fill-through: the rows this wave read from the host go into the slot
+  if (wb_gu) {
+#pragma unroll
+    for (int r = 0; r < 2 * kA_WaveRows; ++r) {
+      const int row = r < kA_WaveRows ? i0 + r : I + i0 + (r - kA_WaveRows);
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        if (!okq[q]) continue;
+        reinterpret_cast<uint4*>(wb_gu + (size_t)row * row_bytes)[cq[q]] = wv[r][q];
+        if (FMT == MC_MXFP4) wb_gus[(size_t)row * (H / 32) + cq[q]] = (uint8_t)sb[r][q];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- down kernel
@@ -278,10 +344,14 @@ down_kernel(DecodeArgs a) {
   __shared__ float s_part[4][kB_Rows];
   __shared__ int32_t s_rslot[kMaxRoutes];        // slot of each route (-1 = none)
   __shared__ float s_rgate[kMaxRoutes];
+  __shared__ int32_t s_rsrc[kMaxRoutes];         // fill-through host source, -1 = slot
   const int nt = valid_tokens(a);
   for (int r = threadIdx.x; r < nt * a.k; r += kThreads) {
-    s_rslot[r] = pool_slot(a, r);
+    const int sl = pool_slot(a, r);
+    s_rslot[r] = sl;
     s_rgate[r] = a.w[r];
+    const int src = (a.f_dn && sl >= 0) ? a.rsrc[r] : -1;
+    s_rsrc[r] = (src >= 0 && src < a.n_host) ? src : -1;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -316,6 +386,8 @@ down_kernel(DecodeArgs a) {
   uint4 wv[kB_RoutesPerWave][PASSES][CPLB];
   uint32_t sb[kB_RoutesPerWave][PASSES][CPLB];
   float gate[kB_RoutesPerWave];
+  uint8_t* wb[kB_RoutesPerWave];           // fill-through: slot entry to store the rows to
+  uint8_t* wbs[kB_RoutesPerWave];
   // the wave's routes v0, v0+4, v0+8 of token t: gates and all row loads
   auto load_group = [&](int t, int v0) {
 #pragma unroll
@@ -324,12 +396,21 @@ down_kernel(DecodeArgs a) {
       const uint8_t* dn = a.dn;            // any readable address when there is nothing to read
       const uint8_t* dns = a.dns;
       gate[j] = 0.0f;
+      wb[j] = nullptr;
+      wbs[j] = nullptr;
       if (v < k) {
         const int s = s_rslot[t * k + v];
         if (s >= 0) {
           dn = a.dn + (size_t)s * per;
           if (FMT == MC_MXFP4) dns = a.dns + (size_t)s * per_s;
           gate[j] = s_rgate[t * k + v];
+          const int src = s_rsrc[t * k + v];
+          if (src >= 0) {
+            wb[j] = const_cast<uint8_t*>(dn);
+            wbs[j] = const_cast<uint8_t*>(dns);
+            dn = a.f_dn + (size_t)src * per;
+            if (FMT == MC_MXFP4) dns = a.f_dns + (size_t)src * per_s;
+          }
         }
       } else if (v == k && a.has_shared) {
         dn = a.sh_dn;
@@ -340,7 +421,7 @@ down_kernel(DecodeArgs a) {
       for (int p = 0; p < PASSES; ++p)
 #pragma unroll
         for (int q = 0; q < CPLB; ++q) {
-          wv[j][p][q] = reinterpret_cast<const uint4*>(dn + (size_t)rowp[p] * row_bytes)[cq[q]];
+          wv[j][p][q] = stream_load16(reinterpret_cast<const uint4*>(dn + (size_t)rowp[p] * row_bytes) + cq[q]);
           if (FMT == MC_MXFP4) sb[j][p][q] = dns[(size_t)rowp[p] * (I / 32) + cq[q]];
         }
     }
@@ -392,6 +473,22 @@ down_kernel(DecodeArgs a) {
                                    ? dot_chunk_mx_f32(wq, e8m0_to_f32(sb[j][p][q]), hv, 0.0f)
                                    : dot_chunk_bf_f32(wq, hv, 0.0f);
             acc[p] = fmaf(gate[j], part, acc[p]);
+          }
+        }
+      }
+      // fill-through: rows read from the host go into the slot (rows of this block)
+#pragma unroll
+      for (int j = 0; j < kB_RoutesPerWave; ++j) {
+        if (!wb[j]) continue;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          const int rl = row_sub + RPP * p, row = r0 + rl;
+          if (rl >= kB_Rows || row >= H) continue;
+#pragma unroll
+          for (int q = 0; q < CPLB; ++q) {
+            if (!okq[q]) continue;
+            reinterpret_cast<uint4*>(wb[j] + (size_t)row * row_bytes)[cq[q]] = wv[j][p][q];
+            if (FMT == MC_MXFP4) wbs[j][(size_t)row * (I / 32) + cq[q]] = (uint8_t)sb[j][p][q];
           }
         }
       }
@@ -461,16 +558,22 @@ static int pow2_at_least(int v) {
 
 using namespace mc;
 
+// workspace: h of every route [T*k][I] and of the shared expert [T][I] (fp32), then
+// the routes' fill-through sources [T*k] (int32)
+static size_t ws_h_bytes(int32_t T, int32_t k, int32_t I) {
+  return ((size_t)T * k + (size_t)T) * (size_t)I * sizeof(float);
+}
+
 extern "C" size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I) {
   if (T < 0 || k < 0 || I < 0) return 0;
-  return ((size_t)T * k + (size_t)T) * (size_t)I * sizeof(float);
+  return ws_h_bytes(T, k, I) + (size_t)T * k * sizeof(int32_t);
 }
 
 extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w,
                                   int32_t T, int32_t k, const int32_t* n_tok,
                                   const mc_banks* pool, const mc_banks* shared, void* ws,
                                   size_t ws_bytes, float* y_acc, int32_t accumulate, void* y_bf16,
-                                  hipStream_t s) {
+                                  hipStream_t s, const mc_fill_list* fill) {
   clear_error();
   int rc;
   if ((rc = check_banks(pool, "moe_experts_decode pool")) != MC_OK) return rc;
@@ -539,6 +642,25 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
   a.y_bf16 = static_cast<uint16_t*>(y_bf16);
   a.accumulate = accumulate;
   a.has_shared = has_shared;
+  a.rsrc = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ws_h_bytes(T, k, I));
+  if (fill) {
+    if ((rc = check_banks(fill->host, "moe_experts_decode fill host")) != MC_OK) return rc;
+    MC_REQUIRE(fill->host->fmt == fmt && fill->host->H == H && fill->host->I == I,
+               "moe_experts_decode: fill host banks differ from the pool in format or shape");
+    MC_REQUIRE(fill->kcap >= 0 && fill->fill_flat && fill->fill_slot && fill->n_fill,
+               "moe_experts_decode: bad fill list");
+    if ((rc = host_device_view(fill->host->gate_up, &a.f_gu, "moe_experts_decode: fill host bank")) ||
+        (rc = host_device_view(fill->host->gate_up_scale, &a.f_gus, "moe_experts_decode: fill host bank")) ||
+        (rc = host_device_view(fill->host->down, &a.f_dn, "moe_experts_decode: fill host bank")) ||
+        (rc = host_device_view(fill->host->down_scale, &a.f_dns, "moe_experts_decode: fill host bank")))
+      return rc;
+    a.n_host = fill->host->n;
+    a.fill_flat = fill->fill_flat;
+    a.fill_slot = fill->fill_slot;
+    a.n_fill = fill->n_fill;
+    a.kcap = fill->kcap;
+    if (a.kcap == 0) a.f_gu = a.f_dn = nullptr;
+  }
 
   dim3 grid_a(T * k + has_shared, I / kA_RowsI);
   if (fmt == MC_MXFP4)

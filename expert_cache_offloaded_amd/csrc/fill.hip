@@ -69,7 +69,7 @@ static const void* g_view_host[64];
 static const uint8_t* g_view_dev[64];
 static int g_view_n = 0, g_view_next = 0;
 
-static int device_view(const void* host, const uint8_t** out, const char* what) {
+int host_device_view(const void* host, const uint8_t** out, const char* what) {
   if (host == nullptr) {
     *out = nullptr;
     return MC_OK;
@@ -86,7 +86,7 @@ static int device_view(const void* host, const uint8_t** out, const char* what) 
   hipError_t e = hipHostGetDevicePointer(&d, const_cast<void*>(host), 0);
   if (e != hipSuccess || d == nullptr) {
     (void)hipGetLastError();
-    set_error("mc_fill_slots: %s is not pinned host memory (%s)", what, hipGetErrorString(e));
+    set_error("%s is not pinned host memory (%s)", what, hipGetErrorString(e));
     return MC_EINVAL;
   }
   *out = static_cast<const uint8_t*>(d);
@@ -126,7 +126,7 @@ extern "C" int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const i
     g.bytes[b] = nbytes[b];
     if (nbytes[b] == 0) continue;
     MC_REQUIRE(nbytes[b] % 16 == 0, "mc_fill_slots: bank %d entry is not a multiple of 16 bytes", b);
-    if ((rc = device_view(hs[b], &g.src[b], "host bank")) != MC_OK) return rc;
+    if ((rc = host_device_view(hs[b], &g.src[b], "mc_fill_slots: host bank")) != MC_OK) return rc;
     g.dst[b] = static_cast<uint8_t*>(ds[b]);
     chunks += (int)((nbytes[b] + kFillChunk - 1) / kFillChunk);
   }

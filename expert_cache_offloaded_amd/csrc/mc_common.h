@@ -64,6 +64,11 @@ inline BankBytes bank_bytes(int fmt, int H, int I) {
 // Host validation of a bank descriptor; returns MC_OK or MC_EINVAL with a message.
 int check_banks(const mc_banks* b, const char* what, bool need_nonempty = true);
 
+// Device-visible address of pinned host memory (NULL maps to NULL); MC_EINVAL with a
+// message if `host` is not pinned.  Translations are cached, so a call made during
+// stream capture needs no runtime query once the same allocation was seen.
+int host_device_view(const void* host, const uint8_t** out, const char* what);
+
 // ---------------------------------------------------------------- device helpers
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -107,10 +107,21 @@ class DecodeLayer:
 
     def __init__(self, cache: CacheState, host: BankSet, pool: BankSet, shared: Optional[BankSet],
                  bufs: DecodeBuffers, frac_q16: int = 1 << 16, fixed_cap: int = 1, min_fill: int = 1,
-                 renorm: int = 1, hybrid: bool = False, host_pool: Optional[L.HostPool] = None):
+                 renorm: int = 1, hybrid: bool = False, host_pool: Optional[L.HostPool] = None,
+                 fill_through: bool = False):
         self.cache, self.host, self.pool, self.shared, self.b = cache, host, pool, shared, bufs
         self.frac_q16, self.fixed_cap, self.min_fill, self.renorm = frac_q16, fixed_cap, min_fill, renorm
         self.hybrid = hybrid
+        if not hybrid and pool.n < bufs.T * bufs.k:
+            # with fewer slots than routes a call can overflow misses to the host set,
+            # which only the hybrid branch computes
+            raise ValueError("offload mode needs at least T*k = %d slots (pool has %d); use hybrid"
+                             % (bufs.T * bufs.k, pool.n))
+        # fill-through: the expert pass reads the filled experts from the host and writes
+        # their slots (no separate fill copy); by default mc_fill_slots runs first (on
+        # the Qwen-shaped decode the two measure within 2 %, the copy ahead)
+        self.fill = (L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill)
+                     if fill_through else None)
         self.host_pool = host_pool
         if hybrid:
             nb = L.hybrid_stage_bytes(bufs.T, bufs.k, bufs.H)
@@ -136,16 +147,17 @@ class DecodeLayer:
             w_gpu = b.gpu_w
         else:
             w_gpu = b.w
-        L.fill_slots(self.host.desc, self.pool.desc, b.fill_flat, b.fill_slot, b.n_fill, stream)
+        if self.fill is None:
+            L.fill_slots(self.host.desc, self.pool.desc, b.fill_flat, b.fill_slot, b.n_fill, stream)
         sh = self._shared_desc(layer)
         if self.hybrid:
             # GPU partial in fp32; the merge adds the host partial and rounds once
             L.moe_experts_decode(x, b.slots, w_gpu, n_tok, self.pool.desc, sh, b.ws, b.y_acc,
-                                 accumulate=0, y_bf16=None, stream=stream)
+                                 accumulate=0, y_bf16=None, stream=stream, fill=self.fill)
             L.hybrid_split_merge(hy, L.MC_MERGE, stream)
         else:
             L.moe_experts_decode(x, b.slots, w_gpu, n_tok, self.pool.desc, sh, b.ws, b.y_acc,
-                                 accumulate=0, y_bf16=b.y, stream=stream)
+                                 accumulate=0, y_bf16=b.y, stream=stream, fill=self.fill)
         return b.y
 
     def _shared_desc(self, layer):

@@ -187,6 +187,26 @@ int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const int32_t* fil
                   const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap, hipStream_t s);
 
 /*
+ * Fill list of one lookup call, handed to moe_experts_decode so that the fill of the
+ * chosen misses happens inside the expert pass ("fill-through"): a route whose slot
+ * is fill_slot[i] (i < *n_fill) reads its weights from host entry fill_flat[i] over
+ * the host link, and the same pass writes every byte of that entry into the slot.
+ * The slot then holds exactly what mc_fill_slots would have copied; the host link
+ * carries each filled expert once, and the hits' HBM traffic runs beside it instead
+ * of after it.  All list pointers are device memory, as written by
+ * slot_cache_lookup_evict; host = pinned host banks by flat id (same fmt/H/I as the
+ * pool).  Entries with a flat id outside [0, host->n) are ignored (the route then
+ * reads its slot as usual).
+ */
+typedef struct {
+  const mc_banks* host;
+  const int32_t* fill_flat;  /* [kcap] */
+  const int32_t* fill_slot;  /* [kcap] */
+  const int32_t* n_fill;     /* [1]    */
+  int32_t kcap;
+} mc_fill_list;
+
+/*
  * Workspace bytes of moe_experts_decode for up to T tokens x k routes.
  */
 size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I);
@@ -207,14 +227,20 @@ size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I);
  *   pool       device slot banks; shared: NULL or a device bank whose entry 0 is the
  *              layer's shared expert (same fmt, H, I).
  *   ws         device workspace of moe_experts_decode_ws_bytes(T, k, I) bytes (the
- *              gate_up results h), 16-byte aligned; one workspace per call in flight.
+ *              gate_up results h and each route's weight source), 16-byte aligned;
+ *              one workspace per call in flight.
+ *   fill       NULL (every routed slot is resident), or the fill list of this call's
+ *              lookup (mc_fill_list): those slots are read from the host and written
+ *              in the same pass, so no separate mc_fill_slots is needed.  With T > 1 a
+ *              filled expert's down rows are read from the host once per token that
+ *              routes to it.
  * Two kernel launches (gate_up + SwiGLU, then down + combine).  Needs H % 64 == 0,
  * I % 64 == 0, T <= 64, T*k <= 1024, (k + 1) * I * 4 <= 64 KiB.
  */
 int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w, int32_t T,
                        int32_t k, const int32_t* n_tok, const mc_banks* pool,
                        const mc_banks* shared, void* ws, size_t ws_bytes, float* y_acc,
-                       int32_t accumulate, void* y_bf16, hipStream_t s);
+                       int32_t accumulate, void* y_bf16, hipStream_t s, const mc_fill_list* fill);
 
 
 /* ------------------------------------------------------------------------- */

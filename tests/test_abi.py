@@ -81,10 +81,10 @@ def test_validation_errors_do_not_need_a_gpu():
     # bank checks
     b = L.Banks()
     b.fmt, b.H, b.I, b.n = L.MC_MXFP4, 100, 64, 4
-    assert lib.moe_experts_decode(ids, ids, w, 1, 2, None, C.byref(b), None, ids, 0, w, 0, None, None) == L.MC_EINVAL
+    assert lib.moe_experts_decode(ids, ids, w, 1, 2, None, C.byref(b), None, ids, 0, w, 0, None, None, None) == L.MC_EINVAL
     assert "multiples of 64" in L.last_error()
     b.H = 64
-    assert lib.moe_experts_decode(ids, ids, w, 1, 2, None, C.byref(b), None, ids, 0, w, 0, None, None) == L.MC_EINVAL
+    assert lib.moe_experts_decode(ids, ids, w, 1, 2, None, C.byref(b), None, ids, 0, w, 0, None, None, None) == L.MC_EINVAL
     assert lib.mc_host_pool_create(0, None) is None
 
 

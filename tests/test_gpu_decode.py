@@ -153,8 +153,9 @@ def _step_oracle(cfg, o, layer, ids, w, x, banks, frac, shared=None):
     return res, y
 
 
-@pytest.mark.parametrize("frac", [1 << 16, 1 << 15])
-def test_tiny_trace_end_to_end(frac):
+@pytest.mark.parametrize("frac,fill_through", [(1 << 16, False), (1 << 15, False), (1 << 16, True),
+                                               (1 << 15, True)])
+def test_tiny_trace_end_to_end(frac, fill_through):
     """The tiny config through route -> lookup -> split -> fill -> experts -> merge, every step
     (4 slots for up to 8 unique experts: overflow misses run on the host branch)."""
     from expert_cache_offloaded_amd import HostPool
@@ -169,7 +170,7 @@ def test_tiny_trace_end_to_end(frac):
     cs.reset()
     hp = HostPool(2)
     dl = DecodeLayer(cs, host, pool, None, DecodeBuffers(cfg.T, cfg.k, cfg.H, cfg.I), frac_q16=frac,
-                     hybrid=True, host_pool=hp)
+                     hybrid=True, host_pool=hp, fill_through=fill_through)
     o = LruOracle(cfg.L, cfg.E, cfg.S)
     x_dev = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda")
     for s in range(cfg.steps):
@@ -233,3 +234,58 @@ def test_dsv4_shaped_hybrid_steps(ratio, p):
                 assert rel_l2(dl.b.y_host.cpu().numpy(), yh) <= 1e-4
     assert o.stats[3] > 0          # some misses did run on the host
     hp.close()
+
+
+@pytest.mark.parametrize("cname,T,steps", [("qwen_decode", 1, 4), ("zipf_decode", 4, 3)])
+def test_fill_through_equals_fill_then_decode(cname, T, steps):
+    """Fill-through (the expert pass reads filled experts from the host and writes their
+    slots) against the separate fill copy followed by the expert pass: outputs, slots
+    and every pool byte identical after each layer call; outputs against the oracle."""
+    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer
+    from oracle import route
+    # S >= T*k keeps every miss fillable (no overflow to the host set)
+    cfg = synth.CONFIGS[cname].with_(L=3, E=32, S=max(14, T * 8 + 6), steps=steps, T=T)
+    tr = synth.trace(cfg)
+    host_np = synth.host_pool(cfg)
+    host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
+    sh_np = synth.shared_pool(cfg) if cfg.shared else None
+    shared = (BankSet({k: t_of(v).cuda() for k, v in sh_np.items()}, cfg.H, cfg.I, cfg.fmt)
+              if sh_np is not None else None)
+    runs = []
+    for ft in (True, False):
+        pool = BankSet(empty_device_banks(cfg, cfg.S), cfg.H, cfg.I, cfg.fmt)
+        cs = CacheState(cfg.L, cfg.E, cfg.S)
+        cs.reset()
+        dl = DecodeLayer(cs, host, pool, shared, DecodeBuffers(T, cfg.k, cfg.H, cfg.I),
+                         frac_q16=1 << 16, renorm=cfg.renorm, fill_through=ft)
+        runs.append((pool, cs, dl))
+    x_dev = torch.empty((T, cfg.H), dtype=torch.int16, device="cuda")
+    n_fills = 0
+    for s in range(cfg.steps):
+        lgs = synth.step_logits(cfg, tr[s], s)
+        for l in range(cfg.L):
+            x = synth.activations(cfg, s, l, T=T)
+            x_dev.copy_(t_of(x))
+            lg = torch.from_numpy(lgs[l]).cuda()
+            ys = [dl(l, lg, x_dev).clone() for _, _, dl in runs]
+            torch.cuda.synchronize()
+            assert torch.equal(ys[0], ys[1]), (s, l)
+            assert torch.equal(runs[0][2].b.slots, runs[1][2].b.slots)
+            n_fills += int(runs[0][2].b.n_fill.item())
+            # resident slots hold identical bytes (free slots are uninitialised memory)
+            id_of = runs[0][1].t["id_of"].cpu().numpy()
+            assert np.array_equal(id_of, runs[1][1].t["id_of"].cpu().numpy())
+            res = torch.from_numpy(np.nonzero(id_of >= 0)[0]).cuda()
+            for name in runs[0][0].t:
+                assert torch.equal(runs[0][0].t[name][res], runs[1][0].t[name][res]), (s, l, name)
+            if l == 0:
+                ids, w = route(lgs[l], cfg.k)
+                yref = decode_layer(x, ids, w, host_np, l, cfg.E, cfg.fmt, cfg.H, cfg.I, shared=sh_np)
+                assert_bf16_close(ys[0], yref, "step %d" % s)
+    assert n_fills > 0
+    st = runs[0][1].state()
+    for sl in range(cfg.S):
+        f = int(st["id_of"][sl])
+        if f >= 0:
+            for name, arr in runs[0][0].t.items():
+                assert torch.equal(arr[sl].cpu(), t_of(host_np[name][f]))
