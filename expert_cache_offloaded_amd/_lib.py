@@ -68,6 +68,8 @@ _SIGS = {
     "moe_route": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "slot_cache_lookup_evict": (C.c_int, [C.POINTER(Cache), _I32, _P, _I32, _I32, _P, C.c_uint32,
                                           _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _P]),
+    "moe_route_lookup": (C.c_int, [_P, _I32, _P, _P, C.POINTER(Cache), _I32, _I32, _I32, _P, C.c_uint32,
+                                   _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "mc_fill_slots": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, _P]),
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
@@ -180,6 +182,16 @@ def slot_cache_lookup_evict(cache: Cache, layer: int, ids, n_tok, frac_q16: int,
         C.byref(cache), layer, _ptr(ids), T, k, _ptr(n_tok), frac_q16, fixed_cap, min_fill,
         _ptr(slots), _ptr(fill_flat), _ptr(fill_slot), _ptr(n_fill), _ptr(host_flat), _ptr(n_host),
         fill_flat.numel(), _stream(stream)))
+
+
+def moe_route_lookup(logits, renorm: int, ids, w, cache: Cache, layer: int, n_tok, frac_q16: int,
+                     fixed_cap: int, min_fill: int, slots, fill_flat, fill_slot, n_fill, host_flat,
+                     n_host, stream=None) -> None:
+    T, k = ids.shape
+    _check("moe_route_lookup", lib().moe_route_lookup(
+        _ptr(logits), renorm, _ptr(ids), _ptr(w), C.byref(cache), layer, T, k, _ptr(n_tok), frac_q16,
+        fixed_cap, min_fill, _ptr(slots), _ptr(fill_flat), _ptr(fill_slot), _ptr(n_fill),
+        _ptr(host_flat), _ptr(n_host), fill_flat.numel(), _stream(stream)))
 
 
 def fill_slots(host: Banks, pool: Banks, fill_flat, fill_slot, n_fill, stream=None) -> None:

@@ -14,7 +14,11 @@
 // takes the slots carrying it in ascending slot order, which yields the victims in
 // (stamp, slot) order without sorting.  Every round takes at least one slot, so the
 // loop ends after at most q rounds.
-#include "mc_common.h"
+//
+// moe_route_lookup runs the router and this lookup as one launch: the workgroup's
+// 16 wavefronts first route the call's tokens (one wavefront per token, the
+// routine of moe_route) into LDS, and the lookup reads the ids from there.
+#include "route_dev.h"
 
 namespace mc {
 
@@ -83,10 +87,13 @@ __device__ int64_t block_min_i64(int64_t v, int64_t* sh) {
   return r;
 }
 
+template <bool ROUTE>
 __global__ void __launch_bounds__(kLkThreads)
-lookup_kernel(int32_t L, int32_t E, int32_t S, int32_t* __restrict__ slot_of,
+lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restrict__ topk_ids,
+              float* __restrict__ topk_w,
+              int32_t L, int32_t E, int32_t S, int32_t* __restrict__ slot_of,
               int32_t* __restrict__ id_of, int64_t* __restrict__ stamp, int64_t* __restrict__ clock_p,
-              int64_t* __restrict__ stats, int32_t layer, const int32_t* __restrict__ ids, int32_t T,
+              int64_t* __restrict__ stats, int32_t layer, const int32_t* ids, int32_t T,
               int32_t k, const int32_t* __restrict__ n_tok, uint32_t frac_q16, int32_t fixed_cap,
               int32_t min_fill, int32_t* __restrict__ slots, int32_t* __restrict__ fill_flat,
               int32_t* __restrict__ fill_slot, int32_t* __restrict__ n_fill,
@@ -98,8 +105,25 @@ lookup_kernel(int32_t L, int32_t E, int32_t S, int32_t* __restrict__ slot_of,
   __shared__ int s_scan[kLkThreads / 64 + 1];
   __shared__ int64_t s_min[kLkThreads / 64 + 1];
   __shared__ int s_err;
+  __shared__ int32_t s_ids[ROUTE ? kLkMaxRoutes : 1];
 
   const int tid = threadIdx.x;
+  // 0. (fused form) route every token of the call: ids go to LDS and to topk_ids
+  if (ROUTE) {
+    const int lane = tid & 63;
+    for (int t = tid >> 6; t < T; t += kLkThreads / 64) {   // wave-uniform
+      int id;
+      float gate;
+      route_token_any(logits + (size_t)t * E, E, k, renorm, &id, &gate);
+      if (lane < k) {
+        s_ids[t * k + lane] = id;
+        topk_ids[(size_t)t * k + lane] = id;
+        topk_w[(size_t)t * k + lane] = gate;
+      }
+    }
+    __syncthreads();
+    ids = s_ids;
+  }
   const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
   const int nroutes = nt * k;
   const int64_t clock = *clock_p + 1;
@@ -241,6 +265,24 @@ lookup_kernel(int32_t L, int32_t E, int32_t S, int32_t* __restrict__ slot_of,
 
 using namespace mc;
 
+// argument checks shared by both entry points
+static int check_lookup(const mc_cache* c, int32_t layer, int32_t T, int32_t k, uint32_t frac_q16,
+                        int32_t fixed_cap, int32_t kcap, const char* fn) {
+  MC_REQUIRE(c != nullptr, "%s: cache is NULL", fn);
+  MC_REQUIRE(c->L > 0 && c->E > 0 && c->S > 0, "%s: L=%d E=%d S=%d", fn, c->L, c->E, c->S);
+  MC_REQUIRE(c->E <= kLkMaxE, "%s: E=%d exceeds %d", fn, c->E, kLkMaxE);
+  MC_REQUIRE((int64_t)c->L * c->E < (1ll << 31), "%s: L*E too large", fn);
+  MC_REQUIRE(c->slot_of && c->id_of && c->stamp && c->clock && c->stats, "%s: NULL table pointer", fn);
+  MC_REQUIRE(layer >= 0 && layer < c->L, "%s: layer=%d not in [0, %d)", fn, layer, c->L);
+  MC_REQUIRE(T >= 0 && k >= 1, "%s: T=%d k=%d", fn, T, k);
+  MC_REQUIRE((int64_t)T * k <= kLkMaxRoutes, "%s: T*k=%lld exceeds %d", fn, (long long)T * k,
+             kLkMaxRoutes);
+  MC_REQUIRE(frac_q16 <= 65536u, "%s: frac_q16=%u exceeds 65536", fn, frac_q16);
+  MC_REQUIRE(fixed_cap >= 0, "%s: fixed_cap=%d must be >= 0", fn, fixed_cap);
+  MC_REQUIRE(kcap >= T * k, "%s: kcap=%d < T*k=%d", fn, kcap, T * k);
+  return MC_OK;
+}
+
 extern "C" int slot_cache_lookup_evict(const mc_cache* c, int32_t layer, const int32_t* ids,
                                        int32_t T, int32_t k, const int32_t* n_tok,
                                        uint32_t frac_q16, int32_t fixed_cap, int32_t min_fill,
@@ -248,27 +290,39 @@ extern "C" int slot_cache_lookup_evict(const mc_cache* c, int32_t layer, const i
                                        int32_t* n_fill, int32_t* host_flat, int32_t* n_host,
                                        int32_t kcap, hipStream_t s) {
   clear_error();
-  MC_REQUIRE(c != nullptr, "slot_cache_lookup_evict: cache is NULL");
-  MC_REQUIRE(c->L > 0 && c->E > 0 && c->S > 0, "slot_cache_lookup_evict: L=%d E=%d S=%d",
-             c->L, c->E, c->S);
-  MC_REQUIRE(c->E <= kLkMaxE, "slot_cache_lookup_evict: E=%d exceeds %d", c->E, kLkMaxE);
-  MC_REQUIRE((int64_t)c->L * c->E < (1ll << 31), "slot_cache_lookup_evict: L*E too large");
-  MC_REQUIRE(c->slot_of && c->id_of && c->stamp && c->clock && c->stats,
-             "slot_cache_lookup_evict: NULL table pointer");
-  MC_REQUIRE(layer >= 0 && layer < c->L, "slot_cache_lookup_evict: layer=%d not in [0, %d)",
-             layer, c->L);
-  MC_REQUIRE(T >= 0 && k >= 1, "slot_cache_lookup_evict: T=%d k=%d", T, k);
-  MC_REQUIRE((int64_t)T * k <= kLkMaxRoutes, "slot_cache_lookup_evict: T*k=%lld exceeds %d",
-             (long long)T * k, kLkMaxRoutes);
-  MC_REQUIRE(frac_q16 <= 65536u, "slot_cache_lookup_evict: frac_q16=%u exceeds 65536", frac_q16);
-  MC_REQUIRE(fixed_cap >= 0, "slot_cache_lookup_evict: fixed_cap=%d must be >= 0", fixed_cap);
-  MC_REQUIRE(kcap >= T * k, "slot_cache_lookup_evict: kcap=%d < T*k=%d", kcap, T * k);
+  int rc;
+  if ((rc = check_lookup(c, layer, T, k, frac_q16, fixed_cap, kcap, "slot_cache_lookup_evict")) != MC_OK)
+    return rc;
   MC_REQUIRE(ids && slots && fill_flat && fill_slot && n_fill && host_flat && n_host,
              "slot_cache_lookup_evict: NULL pointer");
-  hipLaunchKernelGGL(lookup_kernel, dim3(1), dim3(kLkThreads), 0, s, c->L, c->E, c->S, c->slot_of,
-                     c->id_of, c->stamp, c->clock, c->stats, layer, ids, T, k, n_tok, frac_q16,
-                     fixed_cap, min_fill, slots, fill_flat, fill_slot, n_fill, host_flat, n_host,
-                     kcap);
+  hipLaunchKernelGGL(lookup_kernel<false>, dim3(1), dim3(kLkThreads), 0, s, nullptr, 0, nullptr,
+                     nullptr, c->L, c->E, c->S, c->slot_of, c->id_of, c->stamp, c->clock, c->stats,
+                     layer, ids, T, k, n_tok, frac_q16, fixed_cap, min_fill, slots, fill_flat,
+                     fill_slot, n_fill, host_flat, n_host, kcap);
+  MC_LAUNCH_CHECK();
+  return MC_OK;
+}
+
+extern "C" int moe_route_lookup(const float* logits, int32_t renorm, int32_t* topk_ids,
+                                float* topk_w, const mc_cache* c, int32_t layer, int32_t T,
+                                int32_t k, const int32_t* n_tok, uint32_t frac_q16,
+                                int32_t fixed_cap, int32_t min_fill, int32_t* slots,
+                                int32_t* fill_flat, int32_t* fill_slot, int32_t* n_fill,
+                                int32_t* host_flat, int32_t* n_host, int32_t kcap, hipStream_t s) {
+  clear_error();
+  int rc;
+  if ((rc = check_lookup(c, layer, T, k, frac_q16, fixed_cap, kcap, "moe_route_lookup")) != MC_OK)
+    return rc;
+  MC_REQUIRE(c->E <= kRouteMaxE, "moe_route_lookup: E=%d exceeds %d", c->E, kRouteMaxE);
+  MC_REQUIRE(k <= c->E && k <= 32, "moe_route_lookup: k=%d must be in [1, min(E, 32)]", k);
+  MC_REQUIRE(renorm == 0 || renorm == 1, "moe_route_lookup: renorm=%d must be 0 or 1", renorm);
+  MC_REQUIRE(logits && topk_ids && topk_w && slots && fill_flat && fill_slot && n_fill && host_flat &&
+                 n_host,
+             "moe_route_lookup: NULL pointer");
+  hipLaunchKernelGGL(lookup_kernel<true>, dim3(1), dim3(kLkThreads), 0, s, logits, renorm, topk_ids,
+                     topk_w, c->L, c->E, c->S, c->slot_of, c->id_of, c->stamp, c->clock, c->stats,
+                     layer, topk_ids, T, k, n_tok, frac_q16, fixed_cap, min_fill, slots, fill_flat,
+                     fill_slot, n_fill, host_flat, n_host, kcap);
   MC_LAUNCH_CHECK();
   return MC_OK;
 }

@@ -3,8 +3,8 @@
 torch allocates every buffer (device tensors, pinned host tensors) and provides the
 stream; each step of the path is one call into ``libmc.so``:
 
-  moe_route -> slot_cache_lookup_evict -> [hybrid_split_merge(SPLIT)] -> mc_fill_slots
-            -> moe_experts_decode -> hybrid_split_merge(MERGE) | mc_finish_bf16
+  moe_route_lookup (= moe_route + slot_cache_lookup_evict) -> [hybrid_split_merge(SPLIT)]
+            -> mc_fill_slots -> moe_experts_decode -> [hybrid_split_merge(MERGE)]
 
 which follows [jjl357] "6.8 CPU 与 GPU 并发执行的顺序" and [wanger] "代码全链路":
 the host branch is started before the fills and the GPU experts, and the two
@@ -132,10 +132,10 @@ class DecodeLayer:
     def __call__(self, layer: int, logits: torch.Tensor, x: torch.Tensor, n_tok=None, stream=None):
         """logits fp32 [T, E], x bf16 bits [T, H] (device) -> self.b.y (bf16 bits)."""
         b = self.b
-        L.moe_route(logits, b.k, self.renorm, b.ids, b.w, stream)
-        L.slot_cache_lookup_evict(self.cache.desc, layer, b.ids, n_tok, self.frac_q16, self.fixed_cap,
-                                  self.min_fill, b.slots, b.fill_flat, b.fill_slot, b.n_fill,
-                                  b.host_flat, b.n_host, stream)
+        # route + lookup in one launch (same results as moe_route then slot_cache_lookup_evict)
+        L.moe_route_lookup(logits, self.renorm, b.ids, b.w, self.cache.desc, layer, n_tok, self.frac_q16,
+                           self.fixed_cap, self.min_fill, b.slots, b.fill_flat, b.fill_slot, b.n_fill,
+                           b.host_flat, b.n_host, stream)
         if self.hybrid:
             key = (layer, x.data_ptr(), None if n_tok is None else n_tok.data_ptr())
             hy = self._hy.get(key)

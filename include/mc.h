@@ -173,6 +173,20 @@ int slot_cache_lookup_evict(const mc_cache* c, int32_t layer, const int32_t* ids
                             int32_t* n_host, int32_t kcap, hipStream_t s);
 
 /*
+ * Routing and lookup of one decode layer call in a single launch: exactly
+ * moe_route(logits, T, c->E, k, renorm, topk_ids, topk_w) followed by
+ * slot_cache_lookup_evict(c, layer, topk_ids, T, k, n_tok, ...) with the same
+ * outputs, but the ids stay on chip between the two steps ([jjl357] "8.2": the
+ * control flow of a step lives in device data, and fewer launches per layer).
+ * Argument meaning, layout and limits are those of the two calls (c->E <= 1024).
+ */
+int moe_route_lookup(const float* logits, int32_t renorm, int32_t* topk_ids, float* topk_w,
+                     const mc_cache* c, int32_t layer, int32_t T, int32_t k, const int32_t* n_tok,
+                     uint32_t frac_q16, int32_t fixed_cap, int32_t min_fill, int32_t* slots,
+                     int32_t* fill_flat, int32_t* fill_slot, int32_t* n_fill, int32_t* host_flat,
+                     int32_t* n_host, int32_t kcap, hipStream_t s);
+
+/*
  * Fill fetch ([jjl357] "6.7" step 3 and "6.8": one fused batch copy of the chosen
  * misses into their victim slots).  Copies every bank of host entry fill_flat[i]
  * into pool entry fill_slot[i] for i < *n_fill, as a kernel that reads the pinned

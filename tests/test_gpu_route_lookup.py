@@ -158,3 +158,62 @@ def test_lookup_invalid_ids_and_masks():
         assert a["fills"] == b["fills"] and a["host"] == b["host"]
         _compare_state(g, o)
     assert o.stats[6] == 6
+
+
+def test_route_signed_zero_and_inf_ties():
+    """-0 and +0 are equal logits (the lower id wins); -inf logits rank last."""
+    lg = np.array([[0.0, -0.0, -0.0, 0.0, -np.inf, 1.0, -1.0, -np.inf],
+                   [-0.0, -np.inf, 0.0, -np.inf, -0.0, -np.inf, -np.inf, -np.inf]], np.float32)
+    for k in (3, 6, 8):
+        ids, w = _route_gpu(lg, k, 1)
+        rid, rw = route(lg, k, 1)
+        assert np.array_equal(ids, rid), k
+        assert np.max(np.abs(w - rw)) < 2e-6
+
+
+@pytest.mark.parametrize("cname,T,S,steps", [("qwen_decode", 1, 600, 12), ("zipf_decode", 16, 512, 6),
+                                              ("tiny", 4, 4, 32)])
+def test_route_lookup_fused_equals_separate(cname, T, S, steps):
+    """moe_route_lookup (one launch) against moe_route + slot_cache_lookup_evict on a
+    second cache: ids, gates, slots, fill/host lists and the whole cache state bit for
+    bit after every call; with a device valid count below T on the batched trace."""
+    from expert_cache_offloaded_amd import moe_route, moe_route_lookup, slot_cache_lookup_evict
+    from expert_cache_offloaded_amd.runtime import CacheState
+    cfg = synth.CONFIGS[cname].with_(steps=steps, T=T, S=S, L=min(synth.CONFIGS[cname].L, 6))
+    tr = synth.trace(cfg)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    sides = []
+    for _ in range(2):
+        cs = CacheState(cfg.L, cfg.E, cfg.S)
+        cs.reset()
+        sides.append(dict(cs=cs, ids=torch.empty((T, cfg.k), **i32),
+                          w=torch.empty((T, cfg.k), dtype=torch.float32, device="cuda"),
+                          slots=torch.empty((T, cfg.k), **i32), ff=torch.empty(T * cfg.k, **i32),
+                          fs=torch.empty(T * cfg.k, **i32), nf=torch.empty(1, **i32),
+                          hf=torch.empty(T * cfg.k, **i32), nh=torch.empty(1, **i32)))
+    ntok = torch.empty(1, **i32)
+    r = np.random.default_rng(3)
+    for s in range(cfg.steps):
+        lgs = synth.step_logits(cfg, tr[s], s)
+        for l in range(cfg.L):
+            lg = torch.from_numpy(np.ascontiguousarray(lgs[l])).cuda()
+            nt = None
+            if T > 1 and s % 2:
+                ntok.fill_(int(r.integers(0, T + 1)))
+                nt = ntok
+            a, b = sides
+            frac = (1 << 16) if cname != "tiny" else (1 << 15)
+            moe_route_lookup(lg, cfg.renorm, a["ids"], a["w"], a["cs"].desc, l, nt, frac, 1, 1, a["slots"],
+                             a["ff"], a["fs"], a["nf"], a["hf"], a["nh"])
+            moe_route(lg, cfg.k, cfg.renorm, b["ids"], b["w"])
+            slot_cache_lookup_evict(b["cs"].desc, l, b["ids"], nt, frac, 1, 1, b["slots"], b["ff"], b["fs"],
+                                    b["nf"], b["hf"], b["nh"])
+            torch.cuda.synchronize()
+            for key in ("ids", "w", "slots", "nf", "nh"):
+                assert torch.equal(a[key], b[key]), (s, l, key)
+            nf, nh = int(a["nf"].item()), int(a["nh"].item())
+            assert torch.equal(a["ff"][:nf], b["ff"][:nf]) and torch.equal(a["fs"][:nf], b["fs"][:nf])
+            assert torch.equal(a["hf"][:nh], b["hf"][:nh])
+            sa, sb = a["cs"].state(), b["cs"].state()
+            for key in sa:
+                assert np.array_equal(sa[key], sb[key]), (s, l, key)
