@@ -28,6 +28,14 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_pmc.txt")
+# kernels of each measured entry point and the source file they are built from
+TRAFFIC_KERNELS = {
+    "moe_experts_decode": ("decode.hip", ("gate_up_kernel", "down_kernel")),
+    "moe_experts_prefill": ("prefill.hip", ("sort_count_kernel", "sort_plan_kernel", "sort_scatter_kernel",
+                                            "prefill_gemm_kernel", "prefill_combine_kernel")),
+}
 METRIC = "MoE-layer decode tok/s (bs=1) + prefill tok/s at 8k; HBM GB/s & MFMA % peak"
 
 
@@ -41,10 +49,133 @@ def _parse():
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run only the workload the HBM traffic counters are taken on, then exit")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the traffic table from two rocprofv3 --pmc counter CSVs, then exit")
     ap.add_argument("--fill-through", action="store_true",
                     help="let the expert pass read filled experts from the host and write their slots "
                          "(default: mc_fill_slots copy first)")
     return ap.parse_args()
+
+
+def _src_sha(name):
+    import hashlib
+    with open(os.path.join(HERE, "expert_cache_offloaded_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_bytes(entry):
+    """HBM bytes per call of `entry` from the committed counter table, or None when the
+    table is missing or its kernels' source has changed since the counters were taken."""
+    src = TRAFFIC_KERNELS[entry][0]
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                p = line.split()
+                if len(p) == 6 and p[0] == "traffic" and p[1] == entry:
+                    if p[2] != src or p[3] != _src_sha(src):
+                        return None
+                    return int(p[4].split("=")[1]) + int(p[5].split("=")[1])
+    except OSError:
+        return None
+    return None
+
+
+def pmc_summary(fetch_csv, write_csv):
+    """Traffic table from FETCH_SIZE / WRITE_SIZE runs of --pmc-workload.  Each counter
+    is scaled by what it reads for the workload's 256 MiB device copy (rocclr copy
+    kernel dispatches of known size)."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+                acc[name].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    print("# HBM traffic per dispatch from rocprofv3 counters on MI355X (ROCm 7.2), made by:")
+    print("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_f -o run -- "
+          "python3 -u bench.py --pmc-workload")
+    print("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_w -o run -- "
+          "python3 -u bench.py --pmc-workload")
+    print("#   python3 bench.py --pmc-summary gpurun_out/pmc_f/run_counter_collection.csv "
+          "gpurun_out/pmc_w/run_counter_collection.csv")
+    print("# 'traffic' lines: calibrated bytes per call of each entry point, keyed by the sha256 "
+          "prefix of the kernel source they were taken on (bench.py reports null once it changes).")
+    fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, _ = per_kernel(write_csv, "WRITE_SIZE")
+    copy = "__amd_rocclr_copyBuffer"
+    chunk_kib = (256 << 10) / nf[copy] * 3     # 3 copies of 256 MiB over nf dispatches
+    f_fac, w_fac = chunk_kib / fetch[copy], chunk_kib / write[copy]
+    print("# calibration: 256 MiB device copy in %d dispatches of %.0f KiB: FETCH_SIZE %.1f KiB, "
+          "WRITE_SIZE %.1f KiB per dispatch -> factors %.4f (fetch), %.4f (write)"
+          % (nf[copy], chunk_kib, fetch[copy], write[copy], f_fac, w_fac))
+    print("# %-44s %12s %12s %14s %14s" % ("kernel", "FETCH KiB", "WRITE KiB", "read bytes", "write bytes"))
+    rows = {}
+    for k in sorted(fetch):
+        rb, wb = fetch[k] * 1024 * f_fac, write.get(k, 0.0) * 1024 * w_fac
+        rows[k] = (rb, wb)
+        print("# %-44s %12.1f %12.1f %14.0f %14.0f" % (k[:44], fetch[k], write.get(k, 0.0), rb, wb))
+    for entry, (src, kernels) in TRAFFIC_KERNELS.items():
+        rb = sum(v[0] for k, v in rows.items() if any(k.startswith("mc::" + n) for n in kernels))
+        wb = sum(v[1] for k, v in rows.items() if any(k.startswith("mc::" + n) for n in kernels))
+        print("traffic %s %s %s fetch_bytes=%d write_bytes=%d" % (entry, src, _src_sha(src), rb, wb))
+
+
+def pmc_workload():
+    """What the traffic counters are taken on: a 256 MiB device copy (calibration), 20
+    Qwen-shaped expert passes over resident experts (8 routed + shared, bs 1) and one
+    8192-token prefill layer (E 256, top-6, H 4096, I 2048)."""
+    import torch
+
+    import synth
+    from expert_cache_offloaded_amd import _lib as L
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    a.fill_(3)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    cfg = synth.CONFIGS["qwen_decode"]
+    n = 64
+    pool_np = synth.host_pool(cfg.with_(L=1, E=n))
+    pool = {k: torch.from_numpy(v).cuda() for k, v in pool_np.items()}
+    sh = {k: torch.from_numpy(v).cuda() for k, v in synth.shared_pool(cfg.with_(L=1)).items()}
+    pb, sb = L.make_banks(cfg.fmt, cfg.H, cfg.I, pool), L.make_banks(cfg.fmt, cfg.H, cfg.I, sh)
+    r = np.random.default_rng(0)
+    x = torch.from_numpy(synth.activations(cfg, 0).view(np.int16)).cuda()
+    w = torch.full((1, cfg.k), 0.125, dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.decode_ws_bytes(1, cfg.k, cfg.I), dtype=torch.uint8, device="cuda")
+    y = torch.zeros((1, cfg.H), dtype=torch.float32, device="cuda")
+    for _ in range(20):
+        slots = torch.from_numpy(r.choice(n, cfg.k, replace=False).astype(np.int32)[None]).cuda()
+        L.moe_experts_decode(x, slots, w, None, pb, sb, ws, y, accumulate=1)
+    torch.cuda.synchronize()
+    del pool
+    cfg = synth.CONFIGS["prefill"]
+    T, E, k, H, I = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I
+    from expert_cache_offloaded_amd.runtime import alloc_banks
+    bt = alloc_banks(E, H, I, cfg.fmt, pin=True)
+    fill_host_pool(cfg.with_(L=1), bt)
+    dev = {k_: v.cuda() for k_, v in bt.items()}
+    buf = L.make_banks(cfg.fmt, H, I, dev)
+    xp = torch.from_numpy(synth.activations(cfg, 0).view(np.int16)).cuda()
+    lg = torch.from_numpy(synth.uniform_logits(cfg)).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wp = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    L.moe_route(lg, k, 1, ids, wp)
+    wsp = torch.empty(L.prefill_ws_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    yp = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    L.moe_experts_prefill(xp, ids, wp, None, E, buf, wsp, yp)
+    torch.cuda.synchronize()
+    print("pmc workload done", flush=True)
 
 
 def log(msg):
@@ -79,6 +210,12 @@ def fill_host_pool(cfg, banks):
 
 def main():
     args = _parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.pmc_workload:
+        pmc_workload()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures a single GPU: the method runs on one GPU (its expert pool, slot "
               "cache and host link); --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -212,7 +349,7 @@ def main():
                                "10240 slots, locality p=0.8",
                    "global_batch": 1, "layers": cfg.L, "slots": cfg.S, "locality": cfg.p},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes("moe_experts_decode"),
                      "kernel": "moe_experts_decode", "bytes_per_launch": int(bytes_per_call),
                      "us_per_launch": round(us_per_call, 3)},
         "decode": {"miss_rate": round(miss_rate, 4), "fills_per_token": round(float(d[2]) / K, 2),
@@ -338,7 +475,7 @@ def bench_prefill(args, torch, L, synth):
            "overlap_ideal": round(ideal, 3)}
     tflops = flops / t_comp * 1e-9
     roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
-            "frac": round(tflops / 2500.0, 4), "traffic": None,
+            "frac": round(tflops / 2500.0, 4), "traffic": traffic_bytes("moe_experts_prefill"),
             "kernel": "moe_experts_prefill (route + sort + gate_up + down + combine)",
             "flop_per_launch": flops, "ms_per_launch": round(t_comp, 4)}
     return pre, roof
