@@ -49,6 +49,10 @@ def _parse():
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill part (for profiling); prints its objects alone")
+    ap.add_argument("--prefill-resident-only", action="store_true",
+                    help="prefill: time only the resident layer (no serialized / double-buffered passes)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run only the workload the HBM traffic counters are taken on, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -228,6 +232,10 @@ def main():
                                                    alloc_banks)
 
     L.lib()   # fails loudly if the library is not built
+    if args.prefill_only:
+        pre, roof = bench_prefill(args, torch, L, synth)
+        print(json.dumps({"prefill": pre, "roofline_prefill": roof}), flush=True)
+        return
     cfg = synth.CONFIGS["qwen_decode"]
     W, K = args.warmup, args.steps
     n_steps = W + K
@@ -430,54 +438,65 @@ def bench_prefill(args, torch, L, synth):
     log("prefill compute (resident layer): %.3f ms, %.0f tok/s, %.0f TFLOP/s"
         % (t_comp, T / t_comp * 1e3, flops / t_comp * 1e-9))
 
-    # serialized: copy a layer, then compute it
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for l in range(cfg.L):
-        copy_layer(l, 0, comp)
-        layer_compute(l, 0)
-    torch.cuda.synchronize()
-    t_serial = (time.perf_counter() - t0) * 1e3 / cfg.L
+    # serialized: copy a layer, then compute it (GPU events; best of two passes, the
+    # first pass also pays first-use costs of the host pages)
+    def serial_pass():
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        for l in range(cfg.L):
+            copy_layer(l, 0, comp)
+            layer_compute(l, 0)
+        e1.record(comp)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
 
     # double buffer: layer l computes from buffer l % 2 while l+1 streams into the other
-    done = [torch.cuda.Event() for _ in range(2)]
-    free = [torch.cuda.Event() for _ in range(2)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    copy_layer(0, 0, copy)
-    done[0].record(copy)
-    for l in range(cfg.L):
-        b = l % 2
-        comp.wait_event(done[b])
-        nxt = None
-        if l + 1 < cfg.L:
-            copy.wait_event(free[1 - b])
-            nxt = L.make_prefetch(host, (l + 1) * E, bufs[1 - b], copy)
-        layer_compute(l, b, nxt)
-        if nxt is not None:
-            done[1 - b].record(copy)
-        free[b].record(comp)
-    torch.cuda.synchronize()
-    t_pipe_total = (time.perf_counter() - t0) * 1e3
-    t_pipe = t_pipe_total / cfg.L
-    t_link = t_serial - t_comp
-    link_gbs = layer_bytes / (t_link * 1e-3) / 1e9
-    ideal = (t_comp + t_link) / max(t_comp, t_link)
-    log("prefill serialized %.1f ms/layer, double-buffered %.1f ms/layer (overlap %.3f of ideal %.3f)"
-        % (t_serial, t_pipe, t_serial / t_pipe, ideal))
-    pre = {"workload": "8192-token prefill, 4 MoE layers, E=256 top-6 uniform routing, H=4096, I=2048, "
-                       "MXFP4 experts, double-buffered 256-expert layer pool",
-           "tokens": T, "layers": cfg.L,
-           "compute_ms_per_layer": round(t_comp, 4), "compute_tok_s": round(T / t_comp * 1e3, 1),
-           "serial_ms_per_layer": round(t_serial, 3), "pipelined_ms_per_layer": round(t_pipe, 3),
-           "pipelined_tok_s": round(T / t_pipe * 1e3, 1), "layer_pool_bytes": int(layer_bytes),
-           "link_gbs": round(link_gbs, 2), "overlap_speedup": round(t_serial / t_pipe, 3),
-           "overlap_ideal": round(ideal, 3)}
+    def pipelined_pass():
+        done = [torch.cuda.Event() for _ in range(2)]
+        free = [torch.cuda.Event() for _ in range(2)]
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(copy)
+        copy_layer(0, 0, copy)
+        done[0].record(copy)
+        for l in range(cfg.L):
+            b = l % 2
+            comp.wait_event(done[b])
+            nxt = None
+            if l + 1 < cfg.L:
+                copy.wait_event(free[1 - b])
+                nxt = L.make_prefetch(host, (l + 1) * E, bufs[1 - b], copy)
+            layer_compute(l, b, nxt)
+            if nxt is not None:
+                done[1 - b].record(copy)
+            free[b].record(comp)
+        e1.record(comp)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
     tflops = flops / t_comp * 1e-9
     roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
             "frac": round(tflops / 2500.0, 4), "traffic": traffic_bytes("moe_experts_prefill"),
             "kernel": "moe_experts_prefill (route + sort + gate_up + down + combine)",
             "flop_per_launch": flops, "ms_per_launch": round(t_comp, 4)}
+    pre = {"workload": "8192-token prefill, 4 MoE layers, E=256 top-6 uniform routing, H=4096, I=2048, "
+                       "MXFP4 experts, double-buffered 256-expert layer pool",
+           "tokens": T, "layers": cfg.L,
+           "compute_ms_per_layer": round(t_comp, 4), "compute_tok_s": round(T / t_comp * 1e3, 1)}
+    if args.prefill_resident_only:
+        return pre, roof
+    t_serial = min(serial_pass() for _ in range(2)) / cfg.L
+    t_pipe = min(pipelined_pass() for _ in range(2)) / cfg.L
+    t_link = t_serial - t_comp
+    link_gbs = layer_bytes / (t_link * 1e-3) / 1e9
+    ideal = (t_comp + t_link) / max(t_comp, t_link)
+    log("prefill serialized %.1f ms/layer, double-buffered %.1f ms/layer (overlap %.3f of ideal %.3f)"
+        % (t_serial, t_pipe, t_serial / t_pipe, ideal))
+    pre.update({"serial_ms_per_layer": round(t_serial, 3), "pipelined_ms_per_layer": round(t_pipe, 3),
+                "pipelined_tok_s": round(T / t_pipe * 1e3, 1), "layer_pool_bytes": int(layer_bytes),
+                "link_gbs": round(link_gbs, 2), "overlap_speedup": round(t_serial / t_pipe, 3),
+                "overlap_ideal": round(ideal, 3)})
     return pre, roof
 
 
