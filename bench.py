@@ -366,6 +366,18 @@ def main():
                    "wall_s": round(wall, 3)},
     }
 
+    # ------------------------------------------------------------------ bandwidth profile
+    # the start-up profile of the two miss paths on this machine (link gather vs host
+    # expert kernel, alone and overlapped) -> fetched fraction and backend choice
+    workers = L.HostPool(min(16, len(os.sched_getaffinity(0))))
+    prof = L.bandwidth_profile(host.desc, pool.desc, workers, 8, seconds=1.0)
+    workers.close()
+    prof["workers"] = workers.n_threads
+    log("bandwidth profile: link %.1f GB/s, host experts %.1f GB/s (overlapped %.1f / %.1f) -> "
+        "fetch fraction %.3f, %s" % (prof["pcie_gbs"], prof["cpu_gbs"], prof["pcie_ov_gbs"],
+                                     prof["cpu_ov_gbs"], prof["frac_q16"] / 65536.0, prof["backend"]))
+    out["bandwidth_profile"] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in prof.items()}
+
     # ------------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, tr, logits, xs, host_np, sh_np, args.cpu_tokens)

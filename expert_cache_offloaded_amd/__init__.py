@@ -8,4 +8,5 @@ from . import _lib  # noqa: F401
 from ._lib import (MC_BF16, MC_MXFP4, Banks, Cache, HostPool, McError, abi_version,  # noqa: F401
                    cache_reset, decode_ws_bytes, fetch_fraction_q16, fill_slots, finish_bf16,
                    host_experts, hybrid_split_merge, lib, make_banks, make_cache, make_hybrid,
-                   moe_experts_decode, moe_route, moe_route_lookup, slot_cache_lookup_evict)
+                   moe_experts_decode, moe_route, moe_route_lookup, slot_cache_lookup_evict,
+                   bandwidth_profile, recommend_backend)

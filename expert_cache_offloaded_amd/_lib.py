@@ -44,6 +44,12 @@ class Prefetch(C.Structure):
                 ("copy", C.c_void_p), ("dst_free", C.c_void_p), ("done", C.c_void_p)]
 
 
+class BwProfile(C.Structure):
+    _fields_ = [("pcie_gbs", C.c_double), ("cpu_gbs", C.c_double), ("pcie_ov_gbs", C.c_double),
+                ("cpu_ov_gbs", C.c_double), ("expert_bytes", C.c_double), ("frac_q16", C.c_uint32),
+                ("hybrid", C.c_int32)]
+
+
 class FillList(C.Structure):
     _fields_ = [("host", C.POINTER(Banks)), ("fill_flat", C.c_void_p), ("fill_slot", C.c_void_p),
                 ("n_fill", C.c_void_p), ("kcap", C.c_int32)]
@@ -81,6 +87,9 @@ _SIGS = {
     "mc_host_pool_create": (_P, [_I32, _P]),
     "mc_host_pool_destroy": (None, [_P]),
     "mc_host_experts": (C.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, C.POINTER(Banks), _P]),
+    "mc_bandwidth_profile": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _I32, C.c_double, C.c_double,
+                                       _P, C.POINTER(BwProfile)]),
+    "mc_recommend_backend": (C.c_int32, [C.c_double, C.c_double, C.c_double]),
     "mc_hybrid_stage_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "hybrid_split_merge": (C.c_int, [C.POINTER(Hybrid), _I32, _P]),
     "mc_finish_bf16": (C.c_int, [_P, _I32, _I32, _P, _P, _P]),
@@ -322,3 +331,21 @@ def make_hybrid(x, ids_raw, slots, w, layer: int, E: int, n_tok, host: Banks, po
 
 def hybrid_split_merge(h: Hybrid, phase: int, stream=None) -> None:
     _check("hybrid_split_merge", lib().hybrid_split_merge(C.byref(h), phase, _stream(stream)))
+
+
+def recommend_backend(cpu_gbs: float, pcie_gbs: float, threshold: float = 2.0) -> str:
+    """'hybrid' iff cpu_gbs > threshold * pcie_gbs, else 'offload'."""
+    return "hybrid" if lib().mc_recommend_backend(cpu_gbs, pcie_gbs, threshold) else "offload"
+
+
+def bandwidth_profile(host: Banks, pool: Banks, workers: Optional[HostPool], n_experts: int,
+                      seconds: float = 1.0, threshold: float = 2.0, stream=None) -> dict:
+    """Start-up bandwidth profile (synchronous): stand-alone and overlapped rates of the
+    fill kernel and the host expert kernel, the fetched fraction and the backend."""
+    out = BwProfile()
+    _check("mc_bandwidth_profile", lib().mc_bandwidth_profile(
+        C.byref(host), C.byref(pool), workers.handle if workers is not None else None, n_experts, seconds,
+        threshold, _stream(stream), C.byref(out)))
+    return {"pcie_gbs": out.pcie_gbs, "cpu_gbs": out.cpu_gbs, "pcie_ov_gbs": out.pcie_ov_gbs,
+            "cpu_ov_gbs": out.cpu_ov_gbs, "expert_bytes": out.expert_bytes, "frac_q16": out.frac_q16,
+            "backend": "hybrid" if out.hybrid else "offload", "threshold": threshold}

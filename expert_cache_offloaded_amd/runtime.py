@@ -167,3 +167,35 @@ class DecodeLayer:
         if d is None:
             d = self._sh[layer] = self.shared.entry(layer)
         return d.desc
+
+
+def save_bw_profile(path: str, profile: dict, fmt: str, gpu_name: str) -> None:
+    """Store a bandwidth profile (from ``bandwidth_profile``) under (GPU, expert format):
+    [wanger] "1. 启动时" — the engine looks the fraction up by the experts' format and the
+    GPU at start-up.  JSON {gpu_name: {fmt: profile}}, merged into an existing file."""
+    import json
+    import os
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data.setdefault(gpu_name, {})[fmt] = profile
+    tmp = path + ".tmp"
+    with open(tmp, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    os.replace(tmp, path)
+
+
+def load_fetch_fraction(path: str, fmt: str, gpu_name: str) -> int:
+    """frac_q16 of the stored profile for (GPU, format), or 0 — the fixed-cap mode that
+    [wanger] "1. 启动时" falls back to when there is no usable profile."""
+    import json
+    import os
+    if not os.path.exists(path):
+        return 0
+    with open(path) as f:
+        data = json.load(f)
+    prof = data.get(gpu_name, {}).get(fmt)
+    if not prof:
+        return 0
+    return int(prof.get("frac_q16", 0))

@@ -336,6 +336,38 @@ int mc_host_experts(mc_host_pool* pool, const void* x_bf16, const int32_t* ids, 
                     int32_t T, int32_t k, int32_t layer, int32_t E, const mc_banks* host,
                     float* y);
 
+/*
+ * Start-up bandwidth profile ([wanger] "第一层带宽比：选后端" and "实测版本：overlap 带宽取代
+ * 假设").  Measures the two paths a hybrid decode layer runs, on this machine:
+ *   pcie_gbs     the fill kernel (mc_fill_slots) copying host entries [0, n) into pool
+ *                slots [0, n), alone (bytes of the n experts per second)
+ *   cpu_gbs      mc_host_experts for one token routed to those n experts, alone
+ *   pcie_ov_gbs, cpu_ov_gbs  the same two while both run at once, each sized from its
+ *                stand-alone rate to take about seconds/2
+ *   frac_q16     mc_fetch_fraction_q16(pcie_gbs, cpu_gbs, pcie_ov_gbs, cpu_ov_gbs)
+ *   hybrid       mc_recommend_backend(cpu_gbs, pcie_gbs, threshold)
+ * Synchronous (waits on s; not for capture); about `seconds` of wall time.  Overwrites
+ * pool slots [0, n) and uses device memory of its own for the fill list.  host: pinned
+ * host banks; pool: device banks (same fmt/H/I); workers: NULL = calling thread.
+ * 1 <= n_experts <= min(host->n, pool->n, 4096); 0 < seconds <= 60; threshold > 0.
+ */
+typedef struct {
+  double pcie_gbs, cpu_gbs, pcie_ov_gbs, cpu_ov_gbs;
+  double expert_bytes;       /* bytes of one expert entry (all banks) */
+  uint32_t frac_q16;
+  int32_t hybrid;            /* 1 = hybrid, 0 = offload */
+} mc_bw_profile;
+
+int mc_bandwidth_profile(const mc_banks* host, const mc_banks* pool, mc_host_pool* workers,
+                         int32_t n_experts, double seconds, double threshold, hipStream_t s,
+                         mc_bw_profile* out);
+
+/*
+ * Backend choice ([wanger] "第一层带宽比：选后端"): 1 (hybrid) iff
+ * cpu_gbs > threshold * pcie_gbs, else 0 (offload).  The page's threshold is 2.0.
+ */
+int32_t mc_recommend_backend(double cpu_gbs, double pcie_gbs, double threshold);
+
 /* Pinned staging bytes of one hybrid layer call (header + x, ids, w, y_host). */
 size_t mc_hybrid_stage_bytes(int32_t T, int32_t k, int32_t H);
 

@@ -21,5 +21,5 @@ defines it; every function here has at least one pin in ``tests/test_oracle_*``.
 from .formats import bf16_to_f64, e2m1_value, decode_mxfp4, expert_matrices  # noqa: F401
 from .moe import (expert_ffn, expert_ffn_loops, route, decode_layer, hybrid_partials,  # noqa: F401
                   prefill_grouped, prefill_per_token, sort_routes)
-from .cache import (LruOracle, lru_bruteforce, split_count, fetch_fraction_q16,  # noqa: F401
+from .cache import (LruOracle, lru_bruteforce, split_count, fetch_fraction_q16, recommend_backend,  # noqa: F401
                     miss_latency, best_q_bruteforce)

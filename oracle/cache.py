@@ -113,6 +113,17 @@ def fetch_fraction_q16(b_p: float, b_h: float, p_ov: float = 0.0, c_ov: float = 
     return int(min(max(v, 1), Q16))
 
 
+def recommend_backend(cpu_gbs: float, pcie_gbs: float, threshold: float = 2.0) -> str:
+    """Backend choice of the bandwidth profile ([wanger] "第一层带宽比：选后端"): the
+    ratio of the host expert kernel's bandwidth to the link's decides; above the
+    threshold (2.0 on that page) the CPU branch is worth having ("hybrid"), otherwise
+    every miss goes over the link ("offload")."""
+    ratio = Fraction(cpu_gbs) / Fraction(pcie_gbs) if pcie_gbs > 0 else None
+    if ratio is None:
+        return "hybrid" if cpu_gbs > 0 else "offload"
+    return "hybrid" if ratio > Fraction(threshold) else "offload"
+
+
 def miss_latency(q: int, m: int, b_p, b_h):
     """Exposed miss time of the Qiita latency model (S cancels): exact rational or inf.
 

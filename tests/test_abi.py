@@ -93,3 +93,23 @@ def test_host_pool_lifecycle():
     for n in (1, 2, 5):
         p = HostPool(n)
         p.close()
+
+
+@pytest.mark.parametrize("cpu,pcie,thr", [(47.5, 11.8, 2.0), (53.8, 49.0, 2.0), (2.0, 1.0, 2.0),
+                                          (2.0000001, 1.0, 2.0), (30.0, 10.0, 3.0), (31.0, 10.0, 3.0),
+                                          (1.0, 0.0, 2.0), (0.0, 5.0, 2.0)])
+def test_recommend_backend_matches_oracle(cpu, pcie, thr):
+    from expert_cache_offloaded_amd import recommend_backend
+    from oracle import recommend_backend as ref
+    assert recommend_backend(cpu, pcie, thr) == ref(cpu, pcie, thr)
+
+
+def test_bw_profile_store_roundtrip(tmp_path):
+    from expert_cache_offloaded_amd.runtime import load_fetch_fraction, save_bw_profile
+    p = str(tmp_path / "bw.json")
+    assert load_fetch_fraction(p, "mxfp4", "gfx950") == 0            # no profile: fixed cap
+    save_bw_profile(p, {"frac_q16": 20000, "pcie_gbs": 50.0}, "mxfp4", "gfx950")
+    save_bw_profile(p, {"frac_q16": 65536}, "bf16", "gfx950")
+    assert load_fetch_fraction(p, "mxfp4", "gfx950") == 20000
+    assert load_fetch_fraction(p, "bf16", "gfx950") == 65536
+    assert load_fetch_fraction(p, "mxfp4", "other") == 0

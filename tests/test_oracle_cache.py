@@ -195,3 +195,19 @@ def test_qiita_replay_miss_rate(row):
         lru.lookup(0, tr[s][None, :], 1 << 16)
     got = 100.0 * lru.stats[STAT_MISSES] / accesses
     assert round(got, 1) == rate
+
+
+def test_recommend_backend_pages_machines():
+    """[wanger] "第一层带宽比": hybrid iff the host kernel's bandwidth exceeds 2.0x the link's.
+    Pinned by the pages' machines ([jjl357] "9.1 测试硬件" bandwidths): the RTX 4060 Laptop
+    (B_P 11.8, B_H 47.5 GB/s) is the case whose misses largely run on the CPU branch
+    ([jjl357] "12. Cross-Hardware Results": its low B_P/B_H sends more misses to the CPU); the RTX 5090 Desktop
+    (49.0 / 53.8) fetches every miss over the link (q = m, [qiita] "8.")."""
+    from oracle import recommend_backend
+    assert recommend_backend(47.5, 11.8) == "hybrid"
+    assert recommend_backend(53.8, 49.0) == "offload"
+    # the threshold itself is not enough: strictly greater
+    assert recommend_backend(2.0, 1.0) == "offload"
+    assert recommend_backend(2.0000001, 1.0) == "hybrid"
+    assert recommend_backend(3.0, 1.0, threshold=3.0) == "offload"
+    assert recommend_backend(1.0, 0.0) == "hybrid"
