@@ -57,9 +57,10 @@ def _parse():
                     help="run only the workload the HBM traffic counters are taken on, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic table from two rocprofv3 --pmc counter CSVs, then exit")
-    ap.add_argument("--fill-through", action="store_true",
-                    help="let the expert pass read filled experts from the host and write their slots "
-                         "(default: mc_fill_slots copy first)")
+    ap.add_argument("--fill-mode", choices=("copy", "through", "split"), default="copy",
+                    help="how misses reach their slots: copy (mc_fill_slots first), through (the expert "
+                         "pass reads the host and writes the slots), split (gate_up through, down banks "
+                         "copied on a side stream)")
     return ap.parse_args()
 
 
@@ -258,7 +259,7 @@ def main():
     cache = CacheState(cfg.L, cfg.E, cfg.S)
     cache.reset()
     layers = [DecodeLayer(cache, host, pool, shared, DecodeBuffers(1, cfg.k, cfg.H, cfg.I),
-                          frac_q16=1 << 16, renorm=cfg.renorm, fill_through=args.fill_through)
+                          frac_q16=1 << 16, renorm=cfg.renorm, fill_mode=args.fill_mode)
               for _ in range(cfg.L)]
     logits_buf = torch.empty_like(logits_all[0])
     x_buf = torch.empty_like(x_all[0])

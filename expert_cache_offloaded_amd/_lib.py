@@ -52,7 +52,11 @@ class BwProfile(C.Structure):
 
 class FillList(C.Structure):
     _fields_ = [("host", C.POINTER(Banks)), ("fill_flat", C.c_void_p), ("fill_slot", C.c_void_p),
-                ("n_fill", C.c_void_p), ("kcap", C.c_int32)]
+                ("n_fill", C.c_void_p), ("kcap", C.c_int32), ("gate_up_only", C.c_int32),
+                ("down_after", C.c_void_p)]
+
+
+MC_BANK_GATE_UP, MC_BANK_GATE_UP_SCALE, MC_BANK_DOWN, MC_BANK_DOWN_SCALE, MC_BANK_ALL = 1, 2, 4, 8, 15
 
 
 class Hybrid(C.Structure):
@@ -77,6 +81,7 @@ _SIGS = {
     "moe_route_lookup": (C.c_int, [_P, _I32, _P, _P, C.POINTER(Cache), _I32, _I32, _I32, _P, C.c_uint32,
                                    _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "mc_fill_slots": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, _P]),
+    "mc_fill_slots_banks": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, C.c_uint32, _P]),
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
                                      _P, C.c_size_t, _P, _I32, _P, _P, C.POINTER(FillList)]),
@@ -203,6 +208,12 @@ def moe_route_lookup(logits, renorm: int, ids, w, cache: Cache, layer: int, n_to
         _ptr(host_flat), _ptr(n_host), fill_flat.numel(), _stream(stream)))
 
 
+def fill_slots_banks(host: Banks, pool: Banks, fill_flat, fill_slot, n_fill, banks: int, stream=None) -> None:
+    _check("mc_fill_slots_banks", lib().mc_fill_slots_banks(
+        C.byref(host), C.byref(pool), _ptr(fill_flat), _ptr(fill_slot), _ptr(n_fill), fill_flat.numel(),
+        banks, _stream(stream)))
+
+
 def fill_slots(host: Banks, pool: Banks, fill_flat, fill_slot, n_fill, stream=None) -> None:
     _check("mc_fill_slots", lib().mc_fill_slots(C.byref(host), C.byref(pool), _ptr(fill_flat),
                                                 _ptr(fill_slot), _ptr(n_fill), fill_flat.numel(),
@@ -213,15 +224,19 @@ def decode_ws_bytes(T: int, k: int, I: int) -> int:
     return int(lib().moe_experts_decode_ws_bytes(T, k, I))
 
 
-def make_fill_list(host: Banks, fill_flat, fill_slot, n_fill) -> FillList:
-    """Fill list of a lookup call for fill-through decode (device tensors)."""
+def make_fill_list(host: Banks, fill_flat, fill_slot, n_fill, gate_up_only: bool = False,
+                   down_after=None) -> FillList:
+    """Fill list of a lookup call for fill-through decode (device tensors).  down_after:
+    a recorded torch.cuda.Event the down pass waits for (or None)."""
     f = FillList()
     f.host = C.pointer(host)
     f.fill_flat = _ptr(fill_flat)
     f.fill_slot = _ptr(fill_slot)
     f.n_fill = _ptr(n_fill)
     f.kcap = fill_flat.numel()
-    f._keep = (host, fill_flat, fill_slot, n_fill)
+    f.gate_up_only = 1 if gate_up_only else 0
+    f.down_after = down_after.cuda_event if down_after is not None else None
+    f._keep = (host, fill_flat, fill_slot, n_fill, down_after)
     return f
 
 

@@ -659,6 +659,9 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
     a.fill_slot = fill->fill_slot;
     a.n_fill = fill->n_fill;
     a.kcap = fill->kcap;
+    MC_REQUIRE(fill->gate_up_only == 0 || fill->gate_up_only == 1,
+               "moe_experts_decode: fill gate_up_only=%d", fill->gate_up_only);
+    if (fill->gate_up_only) a.f_dn = a.f_dns = nullptr;   // down reads the slots
     if (a.kcap == 0) a.f_gu = a.f_dn = nullptr;
   }
 
@@ -668,6 +671,7 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
   else
     launch_gate_up<MC_BF16>(a, cpl, grid_a, s);
   MC_LAUNCH_CHECK();
+  if (fill && fill->down_after) MC_HIP(hipStreamWaitEvent(s, fill->down_after, 0));
   dim3 grid_b((H + kB_Rows - 1) / kB_Rows);
   if (fmt == MC_MXFP4)
     launch_down<MC_MXFP4>(a, lpr, cplb, grid_b, lds, s);

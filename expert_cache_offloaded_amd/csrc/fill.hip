@@ -105,7 +105,14 @@ using namespace mc;
 extern "C" int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
                              const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap,
                              hipStream_t s) {
+  return mc_fill_slots_banks(host, pool, fill_flat, fill_slot, n_fill, kcap, MC_BANK_ALL, s);
+}
+
+extern "C" int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
+                                   const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap,
+                                   uint32_t banks, hipStream_t s) {
   clear_error();
+  MC_REQUIRE(banks != 0 && (banks & ~(uint32_t)MC_BANK_ALL) == 0, "mc_fill_slots: bank mask 0x%x", banks);
   int rc;
   if ((rc = check_banks(host, "mc_fill_slots host")) != MC_OK) return rc;
   if ((rc = check_banks(pool, "mc_fill_slots pool")) != MC_OK) return rc;
@@ -123,8 +130,8 @@ extern "C" int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const i
   int chunks = 0;
   for (int b = 0; b < 4; ++b) {
     g.chunk0[b] = chunks;
-    g.bytes[b] = nbytes[b];
-    if (nbytes[b] == 0) continue;
+    g.bytes[b] = (banks >> b) & 1u ? nbytes[b] : 0;    // banks left out get no chunks
+    if (g.bytes[b] == 0) continue;
     MC_REQUIRE(nbytes[b] % 16 == 0, "mc_fill_slots: bank %d entry is not a multiple of 16 bytes", b);
     if ((rc = host_device_view(hs[b], &g.src[b], "mc_fill_slots: host bank")) != MC_OK) return rc;
     g.dst[b] = static_cast<uint8_t*>(ds[b]);

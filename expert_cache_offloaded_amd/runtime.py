@@ -108,21 +108,34 @@ class DecodeLayer:
     def __init__(self, cache: CacheState, host: BankSet, pool: BankSet, shared: Optional[BankSet],
                  bufs: DecodeBuffers, frac_q16: int = 1 << 16, fixed_cap: int = 1, min_fill: int = 1,
                  renorm: int = 1, hybrid: bool = False, host_pool: Optional[L.HostPool] = None,
-                 fill_through: bool = False):
+                 fill_mode: str = "copy"):
         self.cache, self.host, self.pool, self.shared, self.b = cache, host, pool, shared, bufs
         self.frac_q16, self.fixed_cap, self.min_fill, self.renorm = frac_q16, fixed_cap, min_fill, renorm
         self.hybrid = hybrid
+        self.host_pool = host_pool
         if not hybrid and pool.n < bufs.T * bufs.k:
             # with fewer slots than routes a call can overflow misses to the host set,
             # which only the hybrid branch computes
             raise ValueError("offload mode needs at least T*k = %d slots (pool has %d); use hybrid"
                              % (bufs.T * bufs.k, pool.n))
-        # fill-through: the expert pass reads the filled experts from the host and writes
-        # their slots (no separate fill copy); by default mc_fill_slots runs first (on
-        # the Qwen-shaped decode the two measure within 2 %, the copy ahead)
-        self.fill = (L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill)
-                     if fill_through else None)
-        self.host_pool = host_pool
+        # how the chosen misses reach their slots:
+        #   copy    mc_fill_slots, then the expert pass reads the slots
+        #   through the expert pass reads the filled experts from the host and writes the slots
+        #   split   the gate_up pass fills through its banks while mc_fill_slots_banks copies
+        #           the down banks on a side stream; the down pass waits for that copy
+        if fill_mode not in ("copy", "through", "split"):
+            raise ValueError("fill_mode must be copy, through or split")
+        self.fill_mode = fill_mode
+        self.fill = None
+        if fill_mode == "split":
+            self.side = torch.cuda.Stream()
+            self.ev_lookup = torch.cuda.Event()
+            self.ev_fill = torch.cuda.Event()
+            self.ev_fill.record()            # creates the event, so its handle can go in the list
+            self.fill = L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill,
+                                         gate_up_only=True, down_after=self.ev_fill)
+        elif fill_mode == "through":
+            self.fill = L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill)
         if hybrid:
             nb = L.hybrid_stage_bytes(bufs.T, bufs.k, bufs.H)
             self.stage = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
@@ -147,8 +160,15 @@ class DecodeLayer:
             w_gpu = b.gpu_w
         else:
             w_gpu = b.w
-        if self.fill is None:
+        if self.fill_mode == "copy":
             L.fill_slots(self.host.desc, self.pool.desc, b.fill_flat, b.fill_slot, b.n_fill, stream)
+        elif self.fill_mode == "split":
+            cur = stream if stream is not None else torch.cuda.current_stream()
+            self.ev_lookup.record(cur)
+            self.side.wait_event(self.ev_lookup)
+            L.fill_slots_banks(self.host.desc, self.pool.desc, b.fill_flat, b.fill_slot, b.n_fill,
+                               L.MC_BANK_DOWN | L.MC_BANK_DOWN_SCALE, self.side)
+            self.ev_fill.record(self.side)
         sh = self._shared_desc(layer)
         if self.hybrid:
             # GPU partial in fp32; the merge adds the host partial and rounds once

@@ -200,6 +200,20 @@ int moe_route_lookup(const float* logits, int32_t renorm, int32_t* topk_ids, flo
 int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
                   const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap, hipStream_t s);
 
+/* Bank bits of mc_fill_slots_banks. */
+enum { MC_BANK_GATE_UP = 1, MC_BANK_GATE_UP_SCALE = 2, MC_BANK_DOWN = 4, MC_BANK_DOWN_SCALE = 8,
+       MC_BANK_ALL = 15 };
+
+/*
+ * mc_fill_slots restricted to the banks in `banks` (a nonzero mask of MC_BANK_*): the
+ * other banks of the slots are left as they are.  Used with a gate_up-only
+ * fill-through pass (mc_fill_list.gate_up_only), which writes the gate_up banks while
+ * this copies the down banks on another stream.
+ */
+int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
+                        const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap,
+                        uint32_t banks, hipStream_t s);
+
 /*
  * Fill list of one lookup call, handed to moe_experts_decode so that the fill of the
  * chosen misses happens inside the expert pass ("fill-through"): a route whose slot
@@ -218,6 +232,13 @@ typedef struct {
   const int32_t* fill_slot;  /* [kcap] */
   const int32_t* n_fill;     /* [1]    */
   int32_t kcap;
+  /* 1: only the gate_up pass reads the host and writes the gate_up banks; the down pass
+   * reads the slots, whose down banks the caller fills (mc_fill_slots_banks with
+   * MC_BANK_DOWN | MC_BANK_DOWN_SCALE, e.g. on another stream, concurrently with the
+   * gate_up pass).  0: both passes fill through. */
+  int32_t gate_up_only;
+  /* NULL, or an event the down pass waits for (the caller's down-bank fill) */
+  hipEvent_t down_after;
 } mc_fill_list;
 
 /*

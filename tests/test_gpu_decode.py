@@ -153,9 +153,9 @@ def _step_oracle(cfg, o, layer, ids, w, x, banks, frac, shared=None):
     return res, y
 
 
-@pytest.mark.parametrize("frac,fill_through", [(1 << 16, False), (1 << 15, False), (1 << 16, True),
-                                               (1 << 15, True)])
-def test_tiny_trace_end_to_end(frac, fill_through):
+@pytest.mark.parametrize("frac,fill_mode", [(1 << 16, "copy"), (1 << 15, "copy"), (1 << 16, "through"),
+                                            (1 << 15, "through"), (1 << 15, "split")])
+def test_tiny_trace_end_to_end(frac, fill_mode):
     """The tiny config through route -> lookup -> split -> fill -> experts -> merge, every step
     (4 slots for up to 8 unique experts: overflow misses run on the host branch)."""
     from expert_cache_offloaded_amd import HostPool
@@ -170,7 +170,7 @@ def test_tiny_trace_end_to_end(frac, fill_through):
     cs.reset()
     hp = HostPool(2)
     dl = DecodeLayer(cs, host, pool, None, DecodeBuffers(cfg.T, cfg.k, cfg.H, cfg.I), frac_q16=frac,
-                     hybrid=True, host_pool=hp, fill_through=fill_through)
+                     hybrid=True, host_pool=hp, fill_mode=fill_mode)
     o = LruOracle(cfg.L, cfg.E, cfg.S)
     x_dev = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda")
     for s in range(cfg.steps):
@@ -239,8 +239,10 @@ def test_dsv4_shaped_hybrid_steps(ratio, p):
 @pytest.mark.parametrize("cname,T,steps", [("qwen_decode", 1, 4), ("zipf_decode", 4, 3)])
 def test_fill_through_equals_fill_then_decode(cname, T, steps):
     """Fill-through (the expert pass reads filled experts from the host and writes their
-    slots) against the separate fill copy followed by the expert pass: outputs, slots
-    and every pool byte identical after each layer call; outputs against the oracle."""
+    slots) and the split form (gate_up fills through while the down banks are copied on a
+    side stream) against the separate fill copy followed by the expert pass: outputs,
+    slots and every resident pool byte identical after each layer call; outputs against
+    the oracle."""
     from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer
     from oracle import route
     # S >= T*k keeps every miss fillable (no overflow to the host set)
@@ -252,12 +254,12 @@ def test_fill_through_equals_fill_then_decode(cname, T, steps):
     shared = (BankSet({k: t_of(v).cuda() for k, v in sh_np.items()}, cfg.H, cfg.I, cfg.fmt)
               if sh_np is not None else None)
     runs = []
-    for ft in (True, False):
+    for mode in ("through", "split", "copy"):
         pool = BankSet(empty_device_banks(cfg, cfg.S), cfg.H, cfg.I, cfg.fmt)
         cs = CacheState(cfg.L, cfg.E, cfg.S)
         cs.reset()
         dl = DecodeLayer(cs, host, pool, shared, DecodeBuffers(T, cfg.k, cfg.H, cfg.I),
-                         frac_q16=1 << 16, renorm=cfg.renorm, fill_through=ft)
+                         frac_q16=1 << 16, renorm=cfg.renorm, fill_mode=mode)
         runs.append((pool, cs, dl))
     x_dev = torch.empty((T, cfg.H), dtype=torch.int16, device="cuda")
     n_fills = 0
@@ -269,15 +271,16 @@ def test_fill_through_equals_fill_then_decode(cname, T, steps):
             lg = torch.from_numpy(lgs[l]).cuda()
             ys = [dl(l, lg, x_dev).clone() for _, _, dl in runs]
             torch.cuda.synchronize()
-            assert torch.equal(ys[0], ys[1]), (s, l)
-            assert torch.equal(runs[0][2].b.slots, runs[1][2].b.slots)
             n_fills += int(runs[0][2].b.n_fill.item())
-            # resident slots hold identical bytes (free slots are uninitialised memory)
             id_of = runs[0][1].t["id_of"].cpu().numpy()
-            assert np.array_equal(id_of, runs[1][1].t["id_of"].cpu().numpy())
             res = torch.from_numpy(np.nonzero(id_of >= 0)[0]).cuda()
-            for name in runs[0][0].t:
-                assert torch.equal(runs[0][0].t[name][res], runs[1][0].t[name][res]), (s, l, name)
+            for other in runs[1:]:
+                assert torch.equal(ys[0], ys[runs.index(other)]), (s, l)
+                assert torch.equal(runs[0][2].b.slots, other[2].b.slots)
+                # resident slots hold identical bytes (free slots are uninitialised memory)
+                assert np.array_equal(id_of, other[1].t["id_of"].cpu().numpy())
+                for name in runs[0][0].t:
+                    assert torch.equal(runs[0][0].t[name][res], other[0].t[name][res]), (s, l, name)
             if l == 0:
                 ids, w = route(lgs[l], cfg.k)
                 yref = decode_layer(x, ids, w, host_np, l, cfg.E, cfg.fmt, cfg.H, cfg.I, shared=sh_np)
