@@ -320,15 +320,18 @@ prefill_gemm_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // register rings: three weight stages, two activation tiles (named, so that every
-  // index is static and nothing is placed in scratch memory)
+  // register rings: three weight stages (loaded two steps ahead) and three activation
+  // tiles (loaded three steps ahead); named, so that every index is static and nothing
+  // is placed in scratch memory
   GemmStage st0, st1, st2;
-  u32x4_t ar0[4], ar1[4];
-  auto issue = [&](int s, GemmStage& g, u32x4_t* ar) {
+  u32x4_t ar0[4], ar1[4], ar2[4];
+  auto issue_a = [&](int s, u32x4_t* ar) {
     const int k0 = s * kP_KS;
 #pragma unroll
     for (int q = 0; q < 4; ++q) ar[q] = *reinterpret_cast<const u32x4_t*>(aptr[q] + k0);
-    const int kb = (k0 >> 5) + kq;
+  };
+  auto issue_w = [&](int s, GemmStage& g) {
+    const int kb = ((s * kP_KS) >> 5) + kq;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) g.b[nt] = *reinterpret_cast<const u32x4_t*>(brow[nt] + (size_t)kb * 16);
   };
@@ -383,12 +386,14 @@ prefill_gemm_kernel(PrefillArgs a) {
       }
     }
   };
-  // step s: load step s+2 into (g2, ar_ld), compute step s (g, LDS half s & 1), then
-  // publish the tile of step s+1 (ar_st, loaded one step earlier) to the other half
+  // step s: load the activation tile of step s+3 (ar_ld) and the weights of step s+2
+  // (g2), compute step s (g, LDS half s & 1), then publish the tile of step s+1 (ar_st,
+  // loaded two steps earlier) to the other half
   auto step = [&](int s, GemmStage& g, GemmStage& g2, u32x4_t* ar_ld, const u32x4_t* ar_st) {
     if (s >= nsteps) return;
+    if (s + 3 < nsteps) issue_a(s + 3, ar_ld);
     if (s + 2 < nsteps) {
-      issue(s + 2, g2, ar_ld);
+      issue_w(s + 2, g2);
       scales(s + 2, g2);
     }
     // keep the loads ahead of this step's MFMAs (the scheduler would sink them)
@@ -397,14 +402,11 @@ prefill_gemm_kernel(PrefillArgs a) {
     if (s + 1 < nsteps) store_a(ar_st, (s & 1) ^ 1);
     __syncthreads();
   };
-  // one period of the rings (6 steps); stage s % 3, activation tile s % 2
+  // one period of the rings (3 steps): weight stage s % 3, activation tile s % 3
   auto period = [&](int s0) {
     step(s0 + 0, st0, st2, ar0, ar1);
-    step(s0 + 1, st1, st0, ar1, ar0);
-    step(s0 + 2, st2, st1, ar0, ar1);
-    step(s0 + 3, st0, st2, ar1, ar0);
-    step(s0 + 4, st1, st0, ar0, ar1);
-    step(s0 + 5, st2, st1, ar1, ar0);
+    step(s0 + 1, st1, st0, ar1, ar2);
+    step(s0 + 2, st2, st1, ar2, ar0);
   };
 
   // prologue: this thread's row of the scale table, then the first two steps
@@ -421,17 +423,22 @@ prefill_gemm_kernel(PrefillArgs a) {
             *reinterpret_cast<const uint32_t*>(srow_g + d * 4);
     }
   }
-  issue(0, st0, ar0);
-  if (nsteps > 1) issue(1, st1, ar1);
+  issue_a(0, ar0);
+  issue_w(0, st0);
+  if (nsteps > 1) {
+    issue_a(1, ar1);
+    issue_w(1, st1);
+  }
+  if (nsteps > 2) issue_a(2, ar2);
   store_a(ar0, 0);
   __syncthreads();
   scales(0, st0);
   if (nsteps > 1) scales(1, st1);
   if (NSTEPS > 0) {
 #pragma unroll
-    for (int s0 = 0; s0 < NSTEPS; s0 += 6) period(s0);
+    for (int s0 = 0; s0 < NSTEPS; s0 += 3) period(s0);
   } else {
-    for (int s0 = 0; s0 < nsteps; s0 += 6) period(s0);
+    for (int s0 = 0; s0 < nsteps; s0 += 3) period(s0);
   }
 
   if (MODE == 0) {
