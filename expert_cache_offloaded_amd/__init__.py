@@ -9,4 +9,4 @@ from ._lib import (MC_BF16, MC_MXFP4, Banks, Cache, HostPool, McError, abi_versi
                    cache_reset, decode_ws_bytes, fetch_fraction_q16, fill_slots, finish_bf16,
                    host_experts, hybrid_split_merge, lib, make_banks, make_cache, make_hybrid,
                    moe_experts_decode, moe_route, moe_route_lookup, slot_cache_lookup_evict,
-                   bandwidth_profile, recommend_backend)
+                   bandwidth_profile, recommend_backend, cache_install)

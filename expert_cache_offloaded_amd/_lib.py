@@ -81,6 +81,7 @@ _SIGS = {
     "moe_route_lookup": (C.c_int, [_P, _I32, _P, _P, C.POINTER(Cache), _I32, _I32, _I32, _P, C.c_uint32,
                                    _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "mc_fill_slots": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, _P]),
+    "mc_cache_install": (C.c_int, [C.POINTER(Cache), _P, _I32, _P]),
     "mc_fill_slots_banks": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, C.c_uint32, _P]),
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
@@ -206,6 +207,12 @@ def moe_route_lookup(logits, renorm: int, ids, w, cache: Cache, layer: int, n_to
         _ptr(logits), renorm, _ptr(ids), _ptr(w), C.byref(cache), layer, T, k, _ptr(n_tok), frac_q16,
         fixed_cap, min_fill, _ptr(slots), _ptr(fill_flat), _ptr(fill_slot), _ptr(n_fill),
         _ptr(host_flat), _ptr(n_host), fill_flat.numel(), _stream(stream)))
+
+
+def cache_install(cache: Cache, flat, stream=None) -> None:
+    """flat[i] (device int32) becomes resident in slot i; the cache must be empty there."""
+    _check("mc_cache_install", lib().mc_cache_install(C.byref(cache), _ptr(flat), flat.numel(),
+                                                      _stream(stream)))
 
 
 def fill_slots_banks(host: Banks, pool: Banks, fill_flat, fill_slot, n_fill, banks: int, stream=None) -> None:

@@ -326,3 +326,42 @@ extern "C" int moe_route_lookup(const float* logits, int32_t renorm, int32_t* to
   MC_LAUNCH_CHECK();
   return MC_OK;
 }
+
+namespace mc {
+
+// ---------------------------------------------------------------- install
+
+// flat[i] -> slot i on a cache that holds no expert: slot_of / id_of set, stamp = the
+// current clock (so the installed experts are the least recent at the next call).  An
+// id outside [0, L*E), one already placed (a duplicate in the list) or an occupied slot
+// is skipped and counted in stats[err].
+__global__ void __launch_bounds__(256)
+install_kernel(int32_t LE, int32_t S, int32_t* __restrict__ slot_of, int32_t* __restrict__ id_of,
+               int64_t* __restrict__ stamp, const int64_t* __restrict__ clock_p,
+               int64_t* __restrict__ stats, const int32_t* __restrict__ flat, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n || i >= S) return;
+  const int f = flat[i];
+  if (id_of[i] != -1 || f < 0 || f >= LE || atomicCAS(&slot_of[f], -1, i) != -1) {
+    atomicAdd(reinterpret_cast<unsigned long long*>(&stats[MC_STAT_ERR]), 1ull);
+    return;
+  }
+  id_of[i] = f;
+  stamp[i] = *clock_p;
+}
+
+}  // namespace mc
+
+extern "C" int mc_cache_install(const mc_cache* c, const int32_t* flat, int32_t n, hipStream_t s) {
+  clear_error();
+  MC_REQUIRE(c != nullptr && c->L > 0 && c->E > 0 && c->S > 0, "mc_cache_install: bad cache");
+  MC_REQUIRE(c->slot_of && c->id_of && c->stamp && c->clock && c->stats,
+             "mc_cache_install: NULL table pointer");
+  MC_REQUIRE(n >= 0 && n <= c->S, "mc_cache_install: n=%d not in [0, S=%d]", n, c->S);
+  if (n == 0) return MC_OK;
+  MC_REQUIRE(flat != nullptr, "mc_cache_install: NULL list");
+  hipLaunchKernelGGL(install_kernel, dim3((n + 255) / 256), dim3(256), 0, s, c->L * c->E, c->S,
+                     c->slot_of, c->id_of, c->stamp, c->clock, c->stats, flat, n);
+  MC_LAUNCH_CHECK();
+  return MC_OK;
+}

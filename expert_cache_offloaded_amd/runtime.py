@@ -219,3 +219,18 @@ def load_fetch_fraction(path: str, fmt: str, gpu_name: str) -> int:
     if not prof:
         return 0
     return int(prof.get("frac_q16", 0))
+
+
+def static_placement(warm_ids, cap: int):
+    """Static (prefill-time) placement: the `cap` flat ids routed most often over a
+    warm-up window (host int array of any shape, one entry per routed id, occurrences
+    counted), equal counts in the order of first appearance ([qiita] "5. デコード側の答え
+    その1").  Returns int32 ids in rank order, for ``cache_install``."""
+    import numpy as np
+    flat = np.asarray(warm_ids, dtype=np.int64).ravel()
+    flat = flat[flat >= 0]
+    if flat.size == 0:
+        return np.zeros(0, dtype=np.int32)
+    vals, first, counts = np.unique(flat, return_index=True, return_counts=True)
+    order = np.lexsort((first, -counts))         # count descending, then first appearance
+    return vals[order[:cap]].astype(np.int32)

@@ -187,6 +187,19 @@ int moe_route_lookup(const float* logits, int32_t renorm, int32_t* topk_ids, flo
                      int32_t* n_host, int32_t kcap, hipStream_t s);
 
 /*
+ * Placement without a lookup: flat id flat[i] becomes resident in slot i, for i < n
+ * (device list).  For a fixed placement chosen ahead of decode — the static and
+ * prefill-time placements the pages compare LRU against ([jjl357] "11.2 Expert Cache
+ * Locality"; [qiita] "5. デコード側の答え その1") — and for adopting experts whose bytes
+ * are already in the slots.  Only the tables change (bytes: mc_fill_slots); stamps are
+ * set to the current clock.  The cache must hold no expert in slots [0, n) (right after
+ * mc_cache_reset); ids outside [0, L*E), duplicates and occupied slots are skipped and
+ * counted in stats[MC_STAT_ERR].  A lookup with fixed_cap = 0, min_fill = 0 and
+ * frac_q16 = 0 then never fills or evicts, which keeps such a placement fixed.
+ */
+int mc_cache_install(const mc_cache* c, const int32_t* flat, int32_t n, hipStream_t s);
+
+/*
  * Fill fetch ([jjl357] "6.7" step 3 and "6.8": one fused batch copy of the chosen
  * misses into their victim slots).  Copies every bank of host entry fill_flat[i]
  * into pool entry fill_slot[i] for i < *n_fill, as a kernel that reads the pinned

@@ -22,4 +22,5 @@ from .formats import bf16_to_f64, e2m1_value, decode_mxfp4, expert_matrices  # n
 from .moe import (expert_ffn, expert_ffn_loops, route, decode_layer, hybrid_partials,  # noqa: F401
                   prefill_grouped, prefill_per_token, sort_routes)
 from .cache import (LruOracle, lru_bruteforce, split_count, fetch_fraction_q16, recommend_backend,  # noqa: F401
+                    static_resident_set, static_miss_counts,
                     miss_latency, best_q_bruteforce)

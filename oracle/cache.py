@@ -171,6 +171,21 @@ class LruOracle:
         self.clock = 0
         self.stats = np.zeros(8, dtype=np.int64)
 
+    def install(self, flats) -> None:
+        """A fixed placement made ahead of lookups: flats[i] becomes resident in slot i,
+        stamped with the current clock.  Slots that are occupied, ids out of range and
+        repeated ids are skipped and counted as errors (as the device call does)."""
+        for i, f in enumerate(flats):
+            f = int(f)
+            if i >= self.S:
+                break
+            if self.id_of[i] != -1 or f < 0 or f >= self.L * self.E or self.slot_of[f] != -1:
+                self.stats[STAT_ERR] += 1
+                continue
+            self.slot_of[f] = i
+            self.id_of[i] = f
+            self.stamp[i] = self.clock
+
     def lookup(self, layer: int, ids: np.ndarray, frac_q16: int, fixed_cap: int = 1,
                min_fill: int = 1, kcap: Optional[int] = None, n_tok: Optional[int] = None) -> dict:
         """One layer call: dedup, hits, split, LRU victims, fills, rewrite."""
@@ -268,3 +283,32 @@ def lru_bruteforce(calls, S: int, frac_q16: int = Q16, fixed_cap: int = 1, min_f
         order = [s for s in order if s not in touched] + sorted(touched)
         out.append({"fills": fills, "host": misses[q:], "hits": sorted(U[i] for i in range(len(U)) if U[i] in where)})
     return out, content
+
+
+def static_resident_set(warm_steps, cap: int) -> list:
+    """Static (prefill-time) placement as [qiita] "5. デコード側の答え その1" defines it: the
+    cap most frequent ids over the warm-up steps, fixed from then on.  Each step's routed
+    ids count once per occurrence; equal counts keep the order in which the ids first
+    appear (the behaviour of the page's frequency count).  Returns the ids in rank order."""
+    counts = {}
+    order = []
+    for step in warm_steps:
+        for e in np.asarray(step).ravel().tolist():
+            if e not in counts:
+                counts[e] = 0
+                order.append(e)
+            counts[e] += 1
+    ranked = sorted(order, key=lambda e: (-counts[e], order.index(e)))
+    return ranked[:cap]
+
+
+def static_miss_counts(trace, resident) -> tuple:
+    """(misses, accesses) of a fixed placement over a trace: per step the unique routed
+    ids are the accesses, and those outside the placement miss ([qiita] "5.")."""
+    res = set(int(e) for e in resident)
+    miss = acc = 0
+    for step in trace:
+        u = set(int(e) for e in np.asarray(step).ravel().tolist())
+        acc += len(u)
+        miss += sum(1 for e in u if e not in res)
+    return miss, acc

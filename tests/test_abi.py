@@ -113,3 +113,17 @@ def test_bw_profile_store_roundtrip(tmp_path):
     assert load_fetch_fraction(p, "mxfp4", "gfx950") == 20000
     assert load_fetch_fraction(p, "bf16", "gfx950") == 65536
     assert load_fetch_fraction(p, "mxfp4", "other") == 0
+
+
+def test_static_placement_matches_oracle():
+    import numpy as np
+    import synth
+    from expert_cache_offloaded_amd.runtime import static_placement
+    from oracle import static_resident_set
+    tr = synth.qiita_replay_trace(256, 8, 600, 0.95, 20260825)
+    for cap in (1, 8, 64, 200):
+        assert static_placement(tr[:512], cap).tolist() == static_resident_set(tr[:512], cap)
+    r = np.random.default_rng(4)
+    for _ in range(20):
+        w = r.integers(0, 40, size=(r.integers(1, 30), 6))
+        assert static_placement(w, 10).tolist() == static_resident_set(w, 10)

@@ -211,3 +211,25 @@ def test_recommend_backend_pages_machines():
     assert recommend_backend(2.0000001, 1.0) == "hybrid"
     assert recommend_backend(3.0, 1.0, threshold=3.0) == "offload"
     assert recommend_backend(1.0, 0.0) == "hybrid"
+
+
+def test_static_placement_definition():
+    """Hand-evaluated cases of the static placement rule: counts over the warm-up window,
+    ties in order of first appearance."""
+    from oracle import static_miss_counts, static_resident_set
+    assert static_resident_set([[1, 2, 3], [2, 3, 4], [3]], 2) == [3, 2]
+    assert static_resident_set([[5, 6], [6, 5]], 1) == [5]
+    assert static_resident_set([[7, 7, 1]], 2) == [7, 1]          # repeated ids count twice
+    assert static_miss_counts([[1, 2, 2], [3, 1]], [1]) == (2, 4)  # accesses are unique per step
+
+
+def test_static_placement_qiita_replay():
+    """The page's printed static miss rate on its own trace (golden file)."""
+    from oracle import static_miss_counts, static_resident_set
+    path = os.path.join(os.path.dirname(__file__), "golden", "static_replay.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    for E, K, steps, seed, loc, slots, warm, pct in rows:
+        tr = synth.qiita_replay_trace(int(E), int(K), int(steps), float(loc), int(seed))
+        res = static_resident_set(tr[: int(warm)], int(slots))
+        miss, acc = static_miss_counts(tr, res)
+        assert round(100.0 * miss / acc, 1) == float(pct)
