@@ -234,3 +234,89 @@ def static_placement(warm_ids, cap: int):
     vals, first, counts = np.unique(flat, return_index=True, return_counts=True)
     order = np.lexsort((first, -counts))         # count descending, then first appearance
     return vals[order[:cap]].astype(np.int32)
+
+
+class PrefillRunner:
+    """Prefill over the decode slot pool ([jjl357] "4.3 为什么不用三缓冲或更大缓存").
+
+    The layer buffers are slot ranges of the pool itself, so no separate staging
+    memory exists and the experts still in them when prefill ends become decode's
+    initial cache:
+      * S >= 2E: whole-layer double buffer in slots [0, E) and [E, 2E) (layer l + 1
+        streams host -> HBM on a copy stream while layer l computes);
+      * E <= S < 2E: one layer buffer in slots [0, E), copy then compute, no overlap
+        (the pages fall back to loading on demand when two layers do not fit);
+      * S < E: not supported here (raises).
+    After the last layer the experts left in the buffers are installed in the cache
+    (mc_cache_install on the freshly reset tables)."""
+
+    def __init__(self, cache: "CacheState", host: "BankSet", pool: "BankSet", T: int, k: int):
+        E = cache.E
+        if pool.n < E:
+            raise ValueError("prefill needs at least one layer of slots: E=%d > S=%d" % (E, pool.n))
+        self.cache, self.host, self.pool, self.T, self.k = cache, host, pool, T, k
+        self.double = pool.n >= 2 * E
+        nb = 2 if self.double else 1
+        self.bufs = [BankSet({n: v[b * E:(b + 1) * E] for n, v in pool.t.items()}, pool.H, pool.I, pool.fmt)
+                     for b in range(nb)]
+        self.ws = torch.empty(L.prefill_ws_bytes(T, k, E, pool.H, pool.I), dtype=torch.uint8,
+                              device=pool.t["gate_up"].device)
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=self.ws.device)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=self.ws.device)
+
+    def _copy_layer(self, layer: int, b: int, stream) -> None:
+        E = self.cache.E
+        with torch.cuda.stream(stream):
+            for n, v in self.bufs[b].t.items():
+                v.copy_(self.host.t[n][layer * E:(layer + 1) * E], non_blocking=True)
+
+    def run(self, logits, x, ys, renorm: int = 1):
+        """logits: list of L device fp32 [T, E]; x: device bf16 bits [T, H]; ys: list of L
+        device bf16 [T, H] outputs.  Resets the cache first; returns the installed ids."""
+        Lc, E = self.cache.L, self.cache.E
+        comp = torch.cuda.current_stream()
+        self.cache.reset(comp)
+        if self.double:
+            copy = torch.cuda.Stream()
+            done = [torch.cuda.Event() for _ in range(2)]
+            free = [torch.cuda.Event() for _ in range(2)]
+            copy.wait_stream(comp)
+            self._copy_layer(0, 0, copy)
+            done[0].record(copy)
+            for layer in range(Lc):
+                b = layer % 2
+                comp.wait_event(done[b])
+                nxt = None
+                if layer + 1 < Lc:
+                    copy.wait_event(free[1 - b])
+                    nxt = L.make_prefetch(self.host.desc, (layer + 1) * E, self.bufs[1 - b].desc, copy)
+                L.moe_route(logits[layer], self.k, renorm, self.ids, self.w, comp)
+                L.moe_experts_prefill(x, self.ids, self.w, None, E, self.bufs[b].desc, self.ws, ys[layer], nxt,
+                                      comp)
+                if nxt is not None:
+                    done[1 - b].record(copy)
+                free[b].record(comp)
+            # buffer b holds layer l for the last two layers
+            layer_of = [None, None]
+            for layer in range(max(0, Lc - 2), Lc):
+                layer_of[layer % 2] = layer
+        else:
+            for layer in range(Lc):
+                self._copy_layer(layer, 0, comp)
+                L.moe_route(logits[layer], self.k, renorm, self.ids, self.w, comp)
+                L.moe_experts_prefill(x, self.ids, self.w, None, E, self.bufs[0].desc, self.ws, ys[layer], None,
+                                      comp)
+            layer_of = [Lc - 1]
+        # the experts left in the buffers become the decode cache
+        flats = []
+        for b, layer in enumerate(layer_of):
+            if layer is None:
+                flats.extend([-1] * E)        # an unused buffer: its slots stay empty
+            else:
+                flats.extend(range(layer * E, (layer + 1) * E))
+        while flats and flats[-1] == -1:
+            flats.pop()
+        fl = torch.tensor(flats, dtype=torch.int32, device=self.ws.device)
+        if len(flats):
+            L.cache_install(self.cache.desc, fl, comp)
+        return flats

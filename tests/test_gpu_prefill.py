@@ -156,3 +156,76 @@ def test_double_buffer_equals_serialized():
         ref = prefill_per_token(synth.activations(cfg, 0), ids, w, layer_np, cfg.E, cfg.fmt, cfg.H, cfg.I,
                                 tokens=range(16))
         assert_bf16_close(y[:16], ref, "layer %d" % l)
+
+
+@pytest.mark.parametrize("S", [32, 40, 24])
+def test_prefill_runner_buffers_become_decode_cache(S):
+    """Prefill over the decode slot pool ([jjl357] "4.3"): with S >= 2E the two layer
+    buffers are pool slots (double buffer), with E <= S < 2E one buffer (no overlap).
+    Outputs equal a standalone resident prefill bit for bit; afterwards the experts left
+    in the buffers are the cache's residents (tables equal the oracle's install, slot
+    bytes equal host truth) and a decode call on the last layer hits them all."""
+    from expert_cache_offloaded_amd import _lib as L
+    from expert_cache_offloaded_amd.runtime import (BankSet, CacheState, DecodeBuffers, DecodeLayer,
+                                                   PrefillRunner, alloc_banks)
+    from oracle import LruOracle, decode_layer
+    cfg = synth.CONFIGS["prefill"].with_(L=3, E=16, k=4, H=512, I=256, T=512)
+    host_np = synth.host_pool(cfg)
+    host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(alloc_banks(S, cfg.H, cfg.I, cfg.fmt, device="cuda"), cfg.H, cfg.I, cfg.fmt)
+    cache = CacheState(cfg.L, cfg.E, S)
+    x = t_of(synth.activations(cfg, 0)).cuda()
+    logits = [torch.from_numpy(synth.uniform_logits(cfg, layer=l)).cuda() for l in range(cfg.L)]
+    ys = [torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda") for _ in range(cfg.L)]
+    runner = PrefillRunner(cache, host, pool, cfg.T, cfg.k)
+    assert runner.double == (S >= 2 * cfg.E)
+    flats = runner.run(logits, x, ys)
+    torch.cuda.synchronize()
+    # outputs: a standalone prefill of each layer from its own resident buffer
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.prefill_ws_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
+    for l in range(cfg.L):
+        buf = L.make_banks(cfg.fmt, cfg.H, cfg.I,
+                           device_banks({k: v[l * cfg.E:(l + 1) * cfg.E] for k, v in host_np.items()}))
+        L.moe_route(logits[l], cfg.k, 1, ids, w)
+        y = torch.empty_like(ys[l])
+        L.moe_experts_prefill(x, ids, w, None, cfg.E, buf, ws, y)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ys[l]), l
+    # the cache after prefill: the last one or two layers, installed where they sit
+    last = [cfg.L - 1] if S < 2 * cfg.E else [cfg.L - 2, cfg.L - 1]
+    want = []
+    for b in range(len(last)):
+        layer = [l for l in last if l % 2 == b][0] if len(last) == 2 else last[0]
+        want.extend(range(layer * cfg.E, (layer + 1) * cfg.E))
+    assert flats == want
+    o = LruOracle(cfg.L, cfg.E, S)
+    o.install(want)
+    st = cache.state()
+    assert np.array_equal(st["slot_of"], o.slot_of) and np.array_equal(st["id_of"], o.id_of)
+    assert np.array_equal(st["stats"], o.stats)
+    for sl, f in enumerate(want):
+        for name, arr in pool.t.items():
+            assert torch.equal(arr[sl].cpu(), t_of(host_np[name][f])), (sl, name)
+    # decode on the last layer: every route hits the adopted experts
+    dl = DecodeLayer(cache, host, pool, None, DecodeBuffers(1, cfg.k, cfg.H, cfg.I))
+    lg = torch.from_numpy(synth.uniform_logits(cfg.with_(T=1), layer=cfg.L - 1)).cuda()
+    xd = t_of(synth.activations(cfg, 1, T=1)).cuda()
+    yd = dl(cfg.L - 1, lg, xd)
+    torch.cuda.synchronize()
+    st = cache.state()
+    assert int(st["stats"][1]) == 0 and int(st["stats"][0]) == cfg.k      # hits only
+    from oracle import route
+    rid, rw = route(lg.cpu().numpy(), cfg.k)
+    ref = decode_layer(synth.activations(cfg, 1, T=1), rid, rw, host_np, cfg.L - 1, cfg.E, cfg.fmt, cfg.H, cfg.I)
+    assert_bf16_close(yd, ref, "decode after prefill")
+
+
+def test_prefill_runner_needs_one_layer_of_slots():
+    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, PrefillRunner, alloc_banks
+    cfg = synth.CONFIGS["prefill"].with_(L=2, E=16, k=4, H=512, I=256, T=64)
+    host = BankSet(pinned_banks(cfg, synth.host_pool(cfg)), cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(alloc_banks(8, cfg.H, cfg.I, cfg.fmt, device="cuda"), cfg.H, cfg.I, cfg.fmt)
+    with pytest.raises(ValueError):
+        PrefillRunner(CacheState(cfg.L, cfg.E, 8), host, pool, cfg.T, cfg.k)
