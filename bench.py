@@ -57,6 +57,10 @@ def _parse():
                     help="run only the workload the HBM traffic counters are taken on, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic table from two rocprofv3 --pmc counter CSVs, then exit")
+    ap.add_argument("--c5-sweep", action="store_true",
+                    help="run only the batched Zipf decode sweep (bs 1/4/16 x pools 256..4096 slots, one "
+                         "process, the pool resized between points) and print its table")
+    ap.add_argument("--c5-steps", type=int, default=48, help="timed steps per sweep point")
     ap.add_argument("--fill-mode", choices=("copy", "through", "split"), default="copy",
                     help="how misses reach their slots: copy (mc_fill_slots first), through (the expert "
                          "pass reads the host and writes the slots), split (gate_up through, down banks "
@@ -233,6 +237,9 @@ def main():
                                                    alloc_banks)
 
     L.lib()   # fails loudly if the library is not built
+    if args.c5_sweep:
+        print(json.dumps({"c5_sweep": c5_sweep(args, torch, L, synth)}), flush=True)
+        return
     if args.prefill_only:
         pre, roof = bench_prefill(args, torch, L, synth)
         print(json.dumps({"prefill": pre, "roofline_prefill": roof}), flush=True)
@@ -391,6 +398,77 @@ def main():
         out["prefill"] = pre
         out["roofline_prefill"] = roof
     print(json.dumps(out), flush=True)
+
+
+def c5_sweep(args, torch, L, synth):
+    """Batched decode with skew (40 layers, E=256 top-8, H=2048, I=512, MXFP4, Zipf(1.1)
+    expert popularity): bs in {1, 4, 16} x LRU pools of {256, 512, 1024, 2048, 4096} slots
+    in one process; between points the pool is resized at a safe point (the cache
+    restarts cold) and the same steps are replayed as one captured graph per step."""
+    from expert_cache_offloaded_amd.runtime import (BankSet, CacheState, DecodeBuffers, DecodeLayer,
+                                                   alloc_banks, resize_pool)
+    cfg = synth.CONFIGS["zipf_decode"]
+    sizes = (256, 512, 1024, 2048, 4096)
+    W, K = 16, args.c5_steps
+    log("c5: host pool %d experts" % cfg.n_flat)
+    host_t, _ = build_host_pool(cfg, torch)
+    host = BankSet(host_t, cfg.H, cfg.I, cfg.fmt)
+    S_e = synth.expert_bytes(cfg.H, cfg.I, cfg.fmt)
+    out = []
+    for bs in (1, 4, 16):
+        c = cfg.with_(T=bs)
+        tr = synth.trace(c, steps=W + K)
+        logits = torch.from_numpy(np.stack([synth.step_logits(c, tr[s], s) for s in range(W + K)])).cuda()
+        xs = torch.from_numpy(np.stack([np.stack([synth.activations(c, s, l, T=bs) for l in range(c.L)])
+                                        for s in range(W + K)]).view(np.int16)).cuda()
+        pool = BankSet(alloc_banks(sizes[0], c.H, c.I, c.fmt, device="cuda"), c.H, c.I, c.fmt)
+        cache = CacheState(c.L, c.E, sizes[0])
+        cache.reset()
+        layers = [DecodeLayer(cache, host, pool, None, DecodeBuffers(bs, c.k, c.H, c.I), renorm=c.renorm)
+                  for _ in range(c.L)]
+        lg_buf, x_buf = torch.empty_like(logits[0]), torch.empty_like(xs[0])
+
+        def step():
+            for l in range(c.L):
+                layers[l](l, lg_buf[l], x_buf[l])
+        for i, S in enumerate(sizes):
+            if i:
+                del pool
+                cache, pool = resize_pool(layers, S)
+            lg_buf.copy_(logits[0])
+            x_buf.copy_(xs[0])
+            step()                                  # warm-up step 0, eager (also the capture's warm-up)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            for s in range(1, W):
+                lg_buf.copy_(logits[s])
+                x_buf.copy_(xs[s])
+                g.replay()
+            torch.cuda.synchronize()
+            st0 = cache.t["stats"].cpu().numpy().copy()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for s in range(W, W + K):
+                lg_buf.copy_(logits[s])
+                x_buf.copy_(xs[s])
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / K
+            d = cache.t["stats"].cpu().numpy() - st0
+            miss = float(d[1]) / max(1.0, float(d[0] + d[1]))
+            row = {"bs": bs, "slots": S, "ms_per_step": round(ms, 3), "tok_s": round(bs * 1000.0 / ms, 1),
+                   "miss_rate": round(miss, 4), "unique_per_layer_call": round(float(d[0] + d[1]) / (K * c.L), 2),
+                   "fills_per_step": round(float(d[2]) / K, 1),
+                   "link_gbs": round(float(d[2]) * S_e / (ms * K * 1e-3) / 1e9, 1)}
+            log("c5 bs %2d slots %4d: %.3f ms/step, %.1f tok/s, miss %.3f, %.1f unique/layer, %.0f fills/step"
+                % (bs, S, ms, row["tok_s"], miss, row["unique_per_layer_call"], row["fills_per_step"]))
+            out.append(row)
+            del g
+        del layers, cache, pool
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_prefill(args, torch, L, synth):

@@ -180,6 +180,13 @@ class DecodeLayer:
                                  accumulate=0, y_bf16=b.y, stream=stream, fill=self.fill)
         return b.y
 
+    def rebind(self, cache: "CacheState", pool: "BankSet") -> None:
+        """Point this layer at a rebuilt cache and pool (after ``resize_pool``)."""
+        if not self.hybrid and pool.n < self.b.T * self.b.k:
+            raise ValueError("offload mode needs at least T*k = %d slots (pool has %d); use hybrid"
+                             % (self.b.T * self.b.k, pool.n))
+        self.cache, self.pool = cache, pool
+
     def _shared_desc(self, layer):
         if self.shared is None:
             return None
@@ -320,3 +327,24 @@ class PrefillRunner:
         if len(flats):
             L.cache_install(self.cache.desc, fl, comp)
         return flats
+
+
+def resize_pool(layers, new_S: int, stream=None):
+    """Elastic resize of the expert slot pool at a safe point ([jjl357] "7.2 为什么只能在
+    safe point 调整"): wait until no queued work can still use an old slot address, size a
+    new pool of new_S slots, rebuild the cache tables empty, keep the host expert pool
+    untouched, and let later misses refill the hot experts through the normal path.
+    Rebinds every DecodeLayer of `layers` (they share one cache and pool) and returns
+    (cache, pool); graphs captured against the old pool must be captured again."""
+    if not layers:
+        raise ValueError("resize_pool: no layers")
+    torch.cuda.synchronize()                     # the safe point
+    old = layers[0]
+    L_, E = old.cache.L, old.cache.E
+    pool = BankSet(alloc_banks(new_S, old.pool.H, old.pool.I, old.pool.fmt,
+                               device=old.pool.t["gate_up"].device), old.pool.H, old.pool.I, old.pool.fmt)
+    cache = CacheState(L_, E, new_S, device=old.cache.t["slot_of"].device)
+    cache.reset(stream)
+    for dl in layers:
+        dl.rebind(cache, pool)
+    return cache, pool

@@ -292,3 +292,46 @@ def test_fill_through_equals_fill_then_decode(cname, T, steps):
         if f >= 0:
             for name, arr in runs[0][0].t.items():
                 assert torch.equal(arr[sl].cpu(), t_of(host_np[name][f]))
+
+
+def test_resize_pool_sweeps_in_one_run():
+    """Elastic resize ([jjl357] "7.2"): one process walks a batched Zipf trace (bs 4,
+    6 layers) through pools of 64, 160 and 96 slots, resizing at safe points.  Each
+    segment starts cold and equals a fresh oracle LRU of that size bit for bit (slots,
+    tables, stats); outputs against the oracle on the segment's first and last steps."""
+    from expert_cache_offloaded_amd.runtime import (BankSet, CacheState, DecodeBuffers, DecodeLayer,
+                                                   alloc_banks, resize_pool)
+    from oracle import route
+    cfg = synth.CONFIGS["zipf_decode"].with_(L=6, E=64, T=4, steps=9)
+    tr = synth.trace(cfg)
+    host_np = synth.host_pool(cfg)
+    host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
+    sizes = [64, 160, 96]
+    pool = BankSet(alloc_banks(sizes[0], cfg.H, cfg.I, cfg.fmt, device="cuda"), cfg.H, cfg.I, cfg.fmt)
+    cache = CacheState(cfg.L, cfg.E, sizes[0])
+    cache.reset()
+    layers = [DecodeLayer(cache, host, pool, None, DecodeBuffers(cfg.T, cfg.k, cfg.H, cfg.I), renorm=cfg.renorm)
+              for _ in range(cfg.L)]
+    x_dev = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda")
+    seg = cfg.steps // len(sizes)
+    for i, S in enumerate(sizes):
+        if i:
+            cache, pool = resize_pool(layers, S)
+        o = LruOracle(cfg.L, cfg.E, S)
+        for s in range(i * seg, (i + 1) * seg):
+            lgs = synth.step_logits(cfg, tr[s], s)
+            for l in range(cfg.L):
+                x = synth.activations(cfg, s, l)
+                x_dev.copy_(t_of(x))
+                y = layers[l](l, torch.from_numpy(lgs[l]).cuda(), x_dev)
+                torch.cuda.synchronize()
+                ids, w = route(lgs[l], cfg.k)
+                res = o.lookup(l, ids, 1 << 16, 1, 1)
+                assert np.array_equal(layers[l].b.slots.cpu().numpy(), res["slots"]), (S, s, l)
+                if s in (i * seg, (i + 1) * seg - 1) and l % 3 == 0:
+                    ref = decode_layer(x, ids, w, host_np, l, cfg.E, cfg.fmt, cfg.H, cfg.I)
+                    assert_bf16_close(y, ref, "S %d step %d layer %d" % (S, s, l))
+        st = cache.state()
+        assert np.array_equal(st["stats"], o.stats) and np.array_equal(st["slot_of"], o.slot_of)
+        assert np.array_equal(st["id_of"], o.id_of) and np.array_equal(st["stamp"], o.stamp)
+        assert o.stats[2] > 0
