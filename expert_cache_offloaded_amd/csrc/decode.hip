@@ -10,14 +10,15 @@
 // having every weight load of a wave in flight at once (no branch or conversion
 // between a load and the next one).  Two kernels, no cross-workgroup waiting:
 //   gate_up: workgroup = (unit, 16 intermediate rows); a unit is one distinct slot of
-//      the call (first-occurrence order) or the shared expert.  Each wave owns 4 gate
-//      rows and the 4 matching up rows; lane l reads the 16-byte chunks l, l+64, ...
-//      of every row (one coalesced 1 KiB row slice per load instruction), keeps them
-//      in registers and reuses them for every token that routes to the unit.  Dot
+//      the call, run by the grid column of the first route that holds it, or the
+//      shared expert.  Each wave owns 4 gate rows and the 4 matching up rows; lane
+//      l reads the 16-byte chunks l, l+64, ... of every row (one coalesced 1 KiB
+//      row slice per load instruction), keeps them in registers and reuses them for
+//      every token that routes to the unit.  Dot
 //      products run on packed bf16 (MXFP4 -> bf16 is exact) with fp32 accumulation;
 //      h = silu(g) * u is written in fp32 per route.
-//   down: workgroup = 8 hidden rows for every route of a token.  The token's h
-//      vectors are staged in LDS; each wave takes every fourth route, loads all of
+//   down: workgroup = (8 hidden rows, one token), over every route of the token.
+//      The token's h vectors are staged in LDS; each wave takes every fourth route, loads all of
 //      its rows first, then computes; the waves' partial sums meet in LDS and are
 //      added in a fixed order, so every output element is written once (no atomics,
 //      run-to-run identical).  The same pass writes the bf16 output when asked.
@@ -167,34 +168,10 @@ __device__ __forceinline__ int pool_slot(const DecodeArgs& a, int r) {
   return (s >= 0 && s < a.n_pool) ? s : -1;
 }
 
-// Unit table of the call (every gate_up workgroup builds it): s_slot[r] = slot of
-// route r or -1; s_first[u] = first route of the u-th distinct slot, in route order.
-__device__ int build_units(const DecodeArgs& a, int nr, int32_t* s_slot, int32_t* s_first,
-                           int* s_cnt) {
-  const int tid = threadIdx.x;
-  for (int r = tid; r < nr; r += blockDim.x) s_slot[r] = pool_slot(a, r);
-  __syncthreads();
-  if (tid < 64) {
-    int count = 0;
-    for (int base = 0; base < nr; base += 64) {
-      const int r = base + tid;
-      bool first = false;
-      if (r < nr && s_slot[r] >= 0) {
-        first = true;
-        for (int j = 0; j < r; ++j)
-          if (s_slot[j] == s_slot[r]) {
-            first = false;
-            break;
-          }
-      }
-      const uint64_t m = __ballot(first);
-      if (first) s_first[count + __popcll(m & ((1ull << tid) - 1ull))] = r;
-      count += __popcll(m);
-    }
-    if (tid == 0) *s_cnt = count;
-  }
-  __syncthreads();
-  return *s_cnt;
+// 64 routes from `base` on: lanes whose route is below `end` and holds `slot`.
+__device__ __forceinline__ uint64_t routes_with_slot(const DecodeArgs& a, int base, int end, int slot) {
+  const int j = base + (int)(threadIdx.x & 63);
+  return __ballot(j < end && pool_slot(a, j) == slot);
 }
 
 // ---------------------------------------------------------------- gate_up kernel
@@ -202,15 +179,22 @@ __device__ int build_units(const DecodeArgs& a, int nr, int32_t* s_slot, int32_t
 template <int FMT, int CPL>
 __global__ void __launch_bounds__(kThreads)
 gate_up_kernel(DecodeArgs a) {
-  __shared__ int32_t s_slot[kMaxRoutes];
-  __shared__ int32_t s_first[kMaxRoutes];
-  __shared__ int s_cnt;
+  // column u < T*k: route u's slot, when no earlier route of the call holds it (the
+  // first route of a unit); column T*k: the shared expert
   const int nt = valid_tokens(a);
   const int nr = nt * a.k;
-  const int n_units = build_units(a, nr, s_slot, s_first, &s_cnt);
   const int u = blockIdx.x;
-  const bool shared_unit = a.has_shared && u == n_units;
-  if (u > n_units || (u == n_units && !shared_unit) || (shared_unit && nt == 0)) return;
+  const bool shared_unit = a.has_shared && u == a.T * a.k;
+  int slot = -1;
+  if (shared_unit) {
+    if (nt == 0) return;
+  } else {
+    if (u >= nr) return;
+    slot = pool_slot(a, u);
+    if (slot < 0) return;
+    for (int base = 0; base < u; base += 64)
+      if (routes_with_slot(a, base, u, slot)) return;
+  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
@@ -224,12 +208,10 @@ gate_up_kernel(DecodeArgs a) {
   uint8_t* wb_gu = nullptr;        // fill-through: the slot entry the rows are stored to
   uint8_t* wb_gus = nullptr;
   int64_t src = -1;
-  int slot = -1;
   if (shared_unit) {
     gu = a.sh_gu;
     gus = a.sh_gus;
   } else {
-    slot = s_slot[s_first[u]];
     const size_t per_gu = 2 * (size_t)I * row_bytes, per_gus = (size_t)2 * I * H / 32;
     gu = a.gu + (size_t)slot * per_gu;
     if (FMT == MC_MXFP4) gus = a.gus + (size_t)slot * per_gus;
@@ -265,17 +247,24 @@ gate_up_kernel(DecodeArgs a) {
     }
   }
 
-  int r_next = shared_unit ? 0 : s_first[u];
+  // the unit's routes in route order: a mask per 64 routes, the next one fetched when
+  // this one runs out (the shared expert takes every valid token in turn)
+  int base = u & ~63, t_next = 0;
+  uint64_t unit_routes = shared_unit ? 0 : routes_with_slot(a, base, nr, slot) & (~0ull << (u & 63));
   while (true) {
     int t, route;
     if (shared_unit) {
-      if (r_next >= nt) break;
-      t = r_next++;
+      if (t_next >= nt) break;
+      t = t_next++;
       route = -1;
     } else {
-      while (r_next < nr && s_slot[r_next] != slot) ++r_next;
-      if (r_next >= nr) break;
-      route = r_next++;
+      while (!unit_routes && base + 64 < nr) {
+        base += 64;
+        unit_routes = routes_with_slot(a, base, nr, slot);
+      }
+      if (!unit_routes) break;
+      route = base + __builtin_ctzll(unit_routes);
+      unit_routes &= unit_routes - 1;
       t = route / a.k;
       if (blockIdx.y == 0 && threadIdx.x == 0) a.rsrc[route] = (int32_t)src;
     }
@@ -342,26 +331,36 @@ __global__ void __launch_bounds__(kThreads)
 down_kernel(DecodeArgs a) {
   extern __shared__ float s_h[];                 // [k + 1][I]: one token's route vectors
   __shared__ float s_part[4][kB_Rows];
-  __shared__ int32_t s_rslot[kMaxRoutes];        // slot of each route (-1 = none)
+  __shared__ int32_t s_rslot[kMaxRoutes];        // slot of each route of the token (-1 = none)
   __shared__ float s_rgate[kMaxRoutes];
   __shared__ int32_t s_rsrc[kMaxRoutes];         // fill-through host source, -1 = slot
   const int nt = valid_tokens(a);
-  for (int r = threadIdx.x; r < nt * a.k; r += kThreads) {
+  const int t = blockIdx.y;
+  const int H = a.H, I = a.I, k = a.k;
+  const int r0 = blockIdx.x * kB_Rows;
+  if (t >= nt) {                                 // a token beyond the valid count: its rows
+    if (threadIdx.x < kB_Rows && r0 + (int)threadIdx.x < H) {
+      const size_t o = (size_t)t * H + r0 + threadIdx.x;
+      if (!a.accumulate) a.y[o] = 0.0f;
+      if (a.y_bf16) a.y_bf16[o] = 0;
+    }
+    return;
+  }
+  for (int v = threadIdx.x; v < k; v += kThreads) {
+    const int r = t * k + v;
     const int sl = pool_slot(a, r);
-    s_rslot[r] = sl;
-    s_rgate[r] = a.w[r];
+    s_rslot[v] = sl;
+    s_rgate[v] = a.w[r];
     const int src = (a.f_dn && sl >= 0) ? a.rsrc[r] : -1;
-    s_rsrc[r] = (src >= 0 && src < a.n_host) ? src : -1;
+    s_rsrc[v] = (src >= 0 && src < a.n_host) ? src : -1;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = a.H, I = a.I, k = a.k, T = a.T;
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;
   constexpr int RPP = 64 / LPR;                              // rows per pass of a wave
   constexpr int PASSES = kB_Rows >= RPP ? kB_Rows / RPP : 1;
   const int n_chunks = I / ELEMS;
   const int row_sub = lane / LPR, c_lane = lane % LPR;
-  const int r0 = blockIdx.x * kB_Rows;
   const bool lane_rows = RPP <= kB_Rows || row_sub < kB_Rows;
   const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)I / 2 : (size_t)I * 2;
   const size_t per = (size_t)H * row_bytes;
@@ -388,8 +387,8 @@ down_kernel(DecodeArgs a) {
   float gate[kB_RoutesPerWave];
   uint8_t* wb[kB_RoutesPerWave];           // fill-through: slot entry to store the rows to
   uint8_t* wbs[kB_RoutesPerWave];
-  // the wave's routes v0, v0+4, v0+8 of token t: gates and all row loads
-  auto load_group = [&](int t, int v0) {
+  // the wave's routes v0, v0+4, v0+8: gates and all row loads
+  auto load_group = [&](int v0) {
 #pragma unroll
     for (int j = 0; j < kB_RoutesPerWave; ++j) {
       const int v = v0 + 4 * j;
@@ -399,12 +398,12 @@ down_kernel(DecodeArgs a) {
       wb[j] = nullptr;
       wbs[j] = nullptr;
       if (v < k) {
-        const int s = s_rslot[t * k + v];
+        const int s = s_rslot[v];
         if (s >= 0) {
           dn = a.dn + (size_t)s * per;
           if (FMT == MC_MXFP4) dns = a.dns + (size_t)s * per_s;
-          gate[j] = s_rgate[t * k + v];
-          const int src = s_rsrc[t * k + v];
+          gate[j] = s_rgate[v];
+          const int src = s_rsrc[v];
           if (src >= 0) {
             wb[j] = const_cast<uint8_t*>(dn);
             wbs[j] = const_cast<uint8_t*>(dns);
@@ -427,8 +426,7 @@ down_kernel(DecodeArgs a) {
     }
   };
 
-  for (int t = 0; t < nt; ++t) {
-    if (t > 0) __syncthreads();              // previous token is done with s_h and s_part
+  {
     // h of this token straight into LDS (global_load_lds, 1 KiB per wave instruction),
     // then the first route group's rows: both sets of loads are in flight together
     const int n4 = nvec * I / 4;
@@ -440,7 +438,7 @@ down_kernel(DecodeArgs a) {
       __builtin_amdgcn_global_load_lds(src + e, (__attribute__((address_space(3))) void*)(s_h + ch * 256),
                                        16, 0, 0);
     }
-    if (n_groups > 0) load_group(t, wave);
+    if (n_groups > 0) load_group(wave);
     __builtin_amdgcn_s_waitcnt(0);                     // the LDS copies have landed
     __syncthreads();
 
@@ -449,7 +447,7 @@ down_kernel(DecodeArgs a) {
     for (int p = 0; p < PASSES; ++p) acc[p] = 0.0f;
     for (int g = 0; g < n_groups; ++g) {
       const int v0 = wave + g * kGroup;
-      if (g > 0) load_group(t, v0);
+      if (g > 0) load_group(v0);
 #pragma unroll
       for (int j = 0; j < kB_RoutesPerWave; ++j) {
         const int v = v0 + 4 * j;
@@ -508,14 +506,6 @@ down_kernel(DecodeArgs a) {
       if (a.accumulate) v += *yp;
       *yp = v;
       if (a.y_bf16) a.y_bf16[(size_t)t * H + row] = f32_to_bf16_rne(v);
-    }
-  }
-  // rows of tokens beyond the valid count
-  if (!a.accumulate || a.y_bf16) {
-    for (int i = threadIdx.x; i < (T - nt) * kB_Rows; i += kThreads) {
-      const int t = nt + i / kB_Rows, row = r0 + i % kB_Rows;
-      if (!a.accumulate) a.y[(size_t)t * H + row] = 0.0f;
-      if (a.y_bf16) a.y_bf16[(size_t)t * H + row] = 0;
     }
   }
 }
@@ -672,7 +662,7 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
     launch_gate_up<MC_BF16>(a, cpl, grid_a, s);
   MC_LAUNCH_CHECK();
   if (fill && fill->down_after) MC_HIP(hipStreamWaitEvent(s, fill->down_after, 0));
-  dim3 grid_b((H + kB_Rows - 1) / kB_Rows);
+  dim3 grid_b((H + kB_Rows - 1) / kB_Rows, T);
   if (fmt == MC_MXFP4)
     launch_down<MC_MXFP4>(a, lpr, cplb, grid_b, lds, s);
   else

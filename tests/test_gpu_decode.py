@@ -106,6 +106,17 @@ def test_decode_matches_oracle(name, cname, T, n_slots, hf, shared):
     assert_bf16_close(yb, case["ref"], name)                  # bf16 output bar
 
 
+def test_decode_max_routes_heavy_sharing():
+    """1024 routes (64 tokens x 16) over 32 experts: every unit is routed by ~32 tokens
+    spread over all sixteen 64-route groups, and a fifth of the routes are host-side."""
+    cfg = synth.CONFIGS["zipf_decode"].with_(L=2, E=32, k=16, H=256, I=128)
+    case = _resident_case(cfg, 64, 40, 0.2, seed=11, shared=True)
+    assert len(np.unique(case["slots"][case["slots"] >= 0])) <= 32
+    y, yb = _run_decode(cfg, case)
+    assert rel_l2(y, case["ref"]) <= 1e-4
+    assert_bf16_close(yb, case["ref"], "max-routes")
+
+
 def test_decode_valid_count_and_empty():
     cfg = synth.CONFIGS["zipf_decode"].with_(L=2)
     for nt in (0, 5, 16):
