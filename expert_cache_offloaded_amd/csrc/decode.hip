@@ -329,7 +329,7 @@ gate_up_kernel(DecodeArgs a) {
 template <int FMT, int LPR, int CPLB>
 __global__ void __launch_bounds__(kThreads)
 down_kernel(DecodeArgs a) {
-  extern __shared__ float s_h[];                 // [k + 1][I]: one token's route vectors
+  extern __shared__ float s_h[];                 // [k + 1][I]: one token's route vectors (swizzled)
   __shared__ float s_part[4][kB_Rows];
   __shared__ int32_t s_rslot[kMaxRoutes];        // slot of each route of the token (-1 = none)
   __shared__ float s_rgate[kMaxRoutes];
@@ -346,6 +346,9 @@ down_kernel(DecodeArgs a) {
     }
     return;
   }
+  float y_old = 0.0f;                            // the value accumulated into, read early
+  if (a.accumulate && threadIdx.x < kB_Rows && r0 + (int)threadIdx.x < H)
+    y_old = a.y[(size_t)t * H + r0 + threadIdx.x];
   for (int v = threadIdx.x; v < k; v += kThreads) {
     const int r = t * k + v;
     const int sl = pool_slot(a, r);
@@ -357,6 +360,7 @@ down_kernel(DecodeArgs a) {
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;
+  constexpr int E4 = ELEMS / 4;                              // float4 of h per chunk
   constexpr int RPP = 64 / LPR;                              // rows per pass of a wave
   constexpr int PASSES = kB_Rows >= RPP ? kB_Rows / RPP : 1;
   const int n_chunks = I / ELEMS;
@@ -428,12 +432,16 @@ down_kernel(DecodeArgs a) {
 
   {
     // h of this token straight into LDS (global_load_lds, 1 KiB per wave instruction),
-    // then the first route group's rows: both sets of loads are in flight together
-    const int n4 = nvec * I / 4;
+    // then the first route group's rows: both sets of loads are in flight together.
+    // Float4 e of chunk c sits at LDS float4 c * E4 + (e ^ (c & (E4 - 1))): the lanes
+    // of a row, which read the same e of consecutive chunks, hit different banks, and
+    // each chunk still comes from one contiguous piece of global memory.
+    const int n4 = nvec * I / 4, r4 = I / 4;
     for (int ch = wave; ch * 64 < n4; ch += 4) {
       int i4 = ch * 64 + lane;
       if (i4 >= n4) i4 = n4 - 1;                       // tail lanes re-read a valid vector
-      const int v = (i4 * 4) / I, e = (i4 * 4) % I;
+      const int v = i4 / r4, sl = i4 % r4, c = sl / E4;
+      const int e = (c * E4 + ((sl % E4) ^ (c & (E4 - 1)))) * 4;
       const float* src = v < k ? a.h_route + ((size_t)t * k + v) * I : a.h_shared + (size_t)t * I;
       __builtin_amdgcn_global_load_lds(src + e, (__attribute__((address_space(3))) void*)(s_h + ch * 256),
                                        16, 0, 0);
@@ -455,10 +463,11 @@ down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < CPLB; ++q) {
           float hv[ELEMS];
-          const float4* hs = reinterpret_cast<const float4*>(s_h + (size_t)v * I + (size_t)cq[q] * ELEMS);
+          const float4* hs = reinterpret_cast<const float4*>(s_h + (size_t)v * I) + cq[q] * E4;
+          const int sw = cq[q] & (E4 - 1);
 #pragma unroll
-          for (int e = 0; e < ELEMS / 4; ++e) {
-            const float4 f = hs[e];
+          for (int e = 0; e < E4; ++e) {
+            const float4 f = hs[e ^ sw];
             hv[4 * e + 0] = f.x;
             hv[4 * e + 1] = f.y;
             hv[4 * e + 2] = f.z;
@@ -503,7 +512,7 @@ down_kernel(DecodeArgs a) {
       float v = ((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
                 s_part[3][threadIdx.x];
       float* yp = a.y + (size_t)t * H + row;
-      if (a.accumulate) v += *yp;
+      if (a.accumulate) v += y_old;
       *yp = v;
       if (a.y_bf16) a.y_bf16[(size_t)t * H + row] = f32_to_bf16_rne(v);
     }

@@ -113,15 +113,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// Sum over all 64 lanes of a wavefront; every lane gets the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// v plus the value a DPP lane move brings (every source lane of these moves is valid).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_f32(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+// Sum over aligned groups of 4 / 16 lanes by DPP moves inside a row (no LDS).
+__device__ __forceinline__ float quad_sum(float v) {
+  v = dpp_add_f32<0xB1>(v);          // quad_perm [1,0,3,2]
+  return dpp_add_f32<0x4E>(v);       // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = quad_sum(v);
+  v = dpp_add_f32<0x141>(v);         // row_half_mirror: the other quad of the 8
+  return dpp_add_f32<0x140>(v);      // row_mirror: the other 8 of the row
+}
+
+// Sum over all 64 lanes of a wavefront; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64); every lane
+// gets its group's sum.
 __device__ __forceinline__ float group_sum(float v, int width) {
+  if (width == 4) return quad_sum(v);
+  if (width == 16) return row16_sum(v);
+  if (width == 64) return wave_sum(v);
   for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
