@@ -69,9 +69,15 @@ def _parse():
 
 
 def _src_sha(name):
+    """Hash of a kernel source file together with every header of the library's sources."""
+    import glob
     import hashlib
-    with open(os.path.join(HERE, "expert_cache_offloaded_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    d = os.path.join(HERE, "expert_cache_offloaded_amd", "csrc")
+    h = hashlib.sha256()
+    for path in [os.path.join(d, name)] + sorted(glob.glob(os.path.join(d, "*.h"))):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_bytes(entry):
