@@ -9,7 +9,10 @@
 //
 // One workgroup of 1024 threads.  Unique experts of the call come from a presence
 // table over the layer's E experts (so they are already in ascending flat-id order);
-// ranks of hits/misses come from workgroup prefix sums.  Victims are taken in rounds:
+// ranks of hits/misses come from one workgroup prefix sum.  The layer's slot_of
+// entries (and, for pools of up to 4096 slots, every slot's stamp and id_of) are read
+// into registers when the kernel starts, so those reads overlap the routing and the
+// victim search runs on registers.  Victims are taken in rounds:
 // each round finds the smallest stamp among the evictable slots not yet taken and
 // takes the slots carrying it in ascending slot order, which yields the victims in
 // (stamp, slot) order without sorting.  Every round takes at least one slot, so the
@@ -25,69 +28,62 @@ namespace mc {
 constexpr int kLkThreads = 1024;
 constexpr int kLkMaxE = 4096;
 constexpr int kLkMaxRoutes = 2048;
+constexpr int kLkPerE = kLkMaxE / kLkThreads;     // experts of the layer per thread, at most
+constexpr int kLkFastS = 4096;                    // pools up to this size: slot table in registers
+constexpr int kLkPerS = kLkFastS / kLkThreads;    // slots per thread then
 
-__device__ __forceinline__ int64_t wave_min_i64(int64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    int64_t w = __shfl_xor(v, o, 64);
-    v = w < v ? w : v;
-  }
-  return v;
+// x plus the value a DPP move brings; lanes outside ROW_MASK, and lanes whose source
+// lies outside their row, add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add_i32(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
 }
 
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Inclusive prefix sum over the 64 lanes: shifts inside each row of 16, then row 0's
+// last lane into row 1, row 2's into row 3, and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x = dpp_add_i32<0x111, 0xF>(x);   // row_shr:1
+  x = dpp_add_i32<0x112, 0xF>(x);   // row_shr:2
+  x = dpp_add_i32<0x114, 0xF>(x);   // row_shr:4
+  x = dpp_add_i32<0x118, 0xF>(x);   // row_shr:8
+  x = dpp_add_i32<0x142, 0xA>(x);   // row_bcast:15
+  x = dpp_add_i32<0x143, 0xC>(x);   // row_bcast:31
+  return x;
 }
 
 // Exclusive prefix sum of one int per thread over the workgroup; returns the
-// thread's offset and writes the total to *total (all threads).
+// thread's offset and writes the total to *total (all threads).  Each wave scans its
+// lanes, publishes its total, and then scans the 16 wave totals itself.
 __device__ int block_excl_scan(int v, int* sh_wave, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) sh_wave[wid] = x;
   __syncthreads();
-  if (wid == 0) {
-    int w = lane < kLkThreads / 64 ? sh_wave[lane] : 0;
-    int z = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(z, o, 64);
-      if (lane >= o) z += y;
-    }
-    if (lane < kLkThreads / 64) sh_wave[lane] = z - w;   // exclusive wave offsets
-    if (lane == kLkThreads / 64 - 1) sh_wave[kLkThreads / 64] = z;
-  }
-  __syncthreads();
-  int off = sh_wave[wid] + x - v;
-  *total = sh_wave[kLkThreads / 64];
-  __syncthreads();
-  return off;
+  const int w = lane < kLkThreads / 64 ? sh_wave[lane] : 0;
+  const int wi = wave_incl_scan(w);
+  const int before = __builtin_amdgcn_readlane(wi - w, wid);   // waves ahead of this one
+  *total = __builtin_amdgcn_readlane(wi, kLkThreads / 64 - 1);
+  __syncthreads();                         // sh_wave is written again by the next scan
+  return before + x - v;
 }
 
-__device__ int64_t block_min_i64(int64_t v, int64_t* sh) {
+// Minimum over the workgroup of a non-negative int64 (stamps, INT64_MAX for none):
+// a DPP wave minimum (the route's 64-bit max on the complemented value), one LDS
+// slot per wave, and every wave reduces the 16 slots itself.  The slots are written
+// again only after the caller's next barrier.
+__device__ __forceinline__ int64_t wave_min_nonneg(int64_t v) {
+  return (int64_t)~wave_max_u64(~(uint64_t)v);
+}
+
+__device__ int64_t block_min_nonneg(int64_t v, int64_t* sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  v = wave_min_i64(v);
+  v = wave_min_nonneg(v);
   if (lane == 0) sh[wid] = v;
   __syncthreads();
-  if (wid == 0) {
-    int64_t w = lane < kLkThreads / 64 ? sh[lane] : INT64_MAX;
-    w = wave_min_i64(w);
-    if (lane == 0) sh[kLkThreads / 64] = w;
-  }
-  __syncthreads();
-  int64_t r = sh[kLkThreads / 64];
-  __syncthreads();
-  return r;
+  return wave_min_nonneg(lane < kLkThreads / 64 ? sh[lane] : INT64_MAX);
 }
 
-template <bool ROUTE>
+template <bool ROUTE, bool FAST>
 __global__ void __launch_bounds__(kLkThreads)
 lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restrict__ topk_ids,
               float* __restrict__ topk_w,
@@ -101,13 +97,49 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   __shared__ uint8_t s_present[kLkMaxE];     // 1 if expert e is routed in this call
   __shared__ int32_t s_slot_e[kLkMaxE];      // slot of expert e after the call, -1 = none
   __shared__ int32_t s_victim[kLkMaxRoutes]; // victims in (stamp, slot) order
+  __shared__ int32_t s_vold[FAST ? kLkMaxRoutes : 1];   // the flat id each victim held
   __shared__ int32_t s_miss[kLkMaxRoutes];   // misses, ascending flat id
+  __shared__ uint8_t s_hit_slot[FAST ? kLkFastS : 1];   // 1 if the slot is a hit of this call
+  __shared__ int32_t s_so[kLkMaxE];                     // slot_of of the layer's experts
+  __shared__ int64_t s_st[FAST ? kLkFastS : 1];         // stamp of every slot (FAST)
+  __shared__ int32_t s_id[FAST ? kLkFastS : 1];         // id_of of every slot (FAST)
   __shared__ int s_scan[kLkThreads / 64 + 1];
-  __shared__ int64_t s_min[kLkThreads / 64 + 1];
-  __shared__ int s_err;
+  __shared__ int64_t s_min[kLkThreads / 64];
+  __shared__ int s_err, s_evict;
   __shared__ int32_t s_ids[ROUTE ? kLkMaxRoutes : 1];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wid = tid >> 6;
+  // each thread owns a contiguous run of the layer's experts (so ranks follow e order)
+  // and of the slots
+  const int per = (E + kLkThreads - 1) / kLkThreads;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  const int sper = (S + kLkThreads - 1) / kLkThreads;
+  const int s0 = tid * sper, s1 = min(S, s0 + sper);
+  for (int e = tid; e < E; e += kLkThreads) {
+    s_present[e] = 0;
+    s_slot_e[e] = -1;
+  }
+  if (FAST)
+    for (int sl = tid; sl < S; sl += kLkThreads) s_hit_slot[sl] = 0;
+  if (tid == 0) {
+    s_err = 0;
+    s_evict = 0;
+  }
+  // the tables the lookup reads (the layer's slot_of; with FAST every slot's stamp and
+  // id_of) go to LDS, loaded by the waves that do not route while the others route,
+  // so neither the routing nor the later phases wait on these reads
+  constexpr int kWaves = kLkThreads / 64;
+  const int route_waves = ROUTE ? min(T, kWaves) : 0;
+  auto load_tables = [&](int w_first) {
+    const int nthr = (kWaves - w_first) * 64, i0 = tid - w_first * 64;
+    for (int e = i0; e < E; e += nthr) s_so[e] = slot_of[(int64_t)layer * E + e];
+    if (FAST)
+      for (int sl = i0; sl < S; sl += nthr) {
+        s_st[sl] = stamp[sl];
+        s_id[sl] = id_of[sl];
+      }
+  };
+  if (route_waves < kWaves && wid >= route_waves) load_tables(route_waves);
   // 0. (fused form) route every token of the call: ids go to LDS and to topk_ids
   if (ROUTE) {
     const int lane = tid & 63;
@@ -121,18 +153,12 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
         topk_w[(size_t)t * k + lane] = gate;
       }
     }
-    __syncthreads();
     ids = s_ids;
   }
+  if (route_waves == kWaves) load_tables(0);     // every wave routed
   const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
   const int nroutes = nt * k;
   const int64_t clock = *clock_p + 1;
-
-  for (int e = tid; e < E; e += kLkThreads) {
-    s_present[e] = 0;
-    s_slot_e[e] = -1;
-  }
-  if (tid == 0) s_err = 0;
   __syncthreads();
 
   // 1. presence of the valid routes
@@ -149,28 +175,34 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   if (my_err) atomicAdd(&s_err, my_err);
   __syncthreads();
 
-  // 2. hits are stamped; misses ranked in ascending expert order
-  //    each thread owns a contiguous run of experts so ranks follow e order
-  const int per = (E + kLkThreads - 1) / kLkThreads;
-  const int e0 = tid * per, e1 = min(E, e0 + per);
+  // 2. hits are stamped; misses ranked in ascending expert order (one scan of both
+  //    counts, hits in the high half)
   int my_hits = 0, my_miss = 0;
-  for (int e = e0; e < e1; ++e) {
-    if (!s_present[e]) continue;
-    int s = slot_of[(int64_t)layer * E + e];
-    if (s >= 0 && s < S) {
-      stamp[s] = clock;
-      s_slot_e[e] = s;
+#pragma unroll
+  for (int j = 0; j < kLkPerE; ++j) {
+    const int e = e0 + j;
+    if (e >= e1 || !s_present[e]) continue;
+    const int sl = s_so[e];
+    if (sl >= 0 && sl < S) {
+      stamp[sl] = clock;
+      s_slot_e[e] = sl;
+      if (FAST) s_hit_slot[sl] = 1;
       ++my_hits;
     } else {
       ++my_miss;
     }
   }
-  int n_hits, m;
-  int miss_off = block_excl_scan(my_miss, s_scan, &m);
-  block_excl_scan(my_hits, s_scan, &n_hits);
-  for (int e = e0, i = miss_off; e < e1; ++e)
-    if (s_present[e] && s_slot_e[e] < 0) s_miss[i++] = layer * E + e;
-  __threadfence_block();
+  int both;
+  const int both_off = block_excl_scan((my_hits << 16) | my_miss, s_scan, &both);
+  const int m = both & 0xFFFF, n_hits = both >> 16;
+  {
+    int i = both_off & 0xFFFF;
+#pragma unroll
+    for (int j = 0; j < kLkPerE; ++j) {
+      const int e = e0 + j;
+      if (e < e1 && s_present[e] && s_slot_e[e] < 0) s_miss[i++] = layer * E + e;
+    }
+  }
   __syncthreads();
 
   // 3. split count (integer rule), capped by evictable slots and list capacity
@@ -190,25 +222,51 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   q = min(q, S - n_hits);
   q = min(q, kcap);
 
-  // 4. victims in (stamp, slot) order, in rounds of equal stamp
+  // 4. victims in (stamp, slot) order, in rounds of equal stamp (FAST: on the stamps
+  //    read at the start, a hit of this call counting as stamped now)
   int taken = 0;
   int64_t floor_stamp = -1;   // stamps <= floor_stamp were exhausted by earlier rounds
-  const int sper = (S + kLkThreads - 1) / kLkThreads;
-  const int s0 = tid * sper, s1 = min(S, s0 + sper);
+  int64_t st_e[kLkPerS];
+  if (FAST) {
+#pragma unroll
+    for (int j = 0; j < kLkPerS; ++j)
+      st_e[j] = s0 + j < s1 ? (s_hit_slot[s0 + j] ? clock : s_st[s0 + j]) : INT64_MAX;
+  }
   while (taken < q) {
     int64_t mine = INT64_MAX;
-    for (int s = s0; s < s1; ++s) {
-      int64_t st = stamp[s];
-      if (st > floor_stamp && st < clock && st < mine) mine = st;
+    if (FAST) {
+#pragma unroll
+      for (int j = 0; j < kLkPerS; ++j)
+        if (st_e[j] > floor_stamp && st_e[j] < clock && st_e[j] < mine) mine = st_e[j];
+    } else {
+      for (int sl = s0; sl < s1; ++sl) {
+        const int64_t st = stamp[sl];
+        if (st > floor_stamp && st < clock && st < mine) mine = st;
+      }
     }
-    const int64_t smin = block_min_i64(mine, s_min);
+    const int64_t smin = block_min_nonneg(mine, s_min);
     int cnt = 0;
-    for (int s = s0; s < s1; ++s) cnt += stamp[s] == smin;
+    if (FAST) {
+#pragma unroll
+      for (int j = 0; j < kLkPerS; ++j) cnt += s0 + j < s1 && st_e[j] == smin;
+    } else {
+      for (int sl = s0; sl < s1; ++sl) cnt += stamp[sl] == smin;
+    }
     int tot;
     int off = block_excl_scan(cnt, s_scan, &tot);
     const int need = q - taken;
-    for (int s = s0; s < s1 && off < need; ++s)
-      if (stamp[s] == smin) s_victim[taken + off++] = s;
+    if (FAST) {
+#pragma unroll
+      for (int j = 0; j < kLkPerS; ++j)
+        if (s0 + j < s1 && st_e[j] == smin && off < need) {
+          s_victim[taken + off] = s0 + j;
+          s_vold[taken + off] = s_id[s0 + j];
+          ++off;
+        }
+    } else {
+      for (int sl = s0; sl < s1 && off < need; ++sl)
+        if (stamp[sl] == smin) s_victim[taken + off++] = sl;
+    }
     taken += min(tot, need);
     floor_stamp = smin;
     __syncthreads();
@@ -219,23 +277,24 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   // 5. install the first q misses into the victims
   int my_evict = 0;
   for (int i = tid; i < q; i += kLkThreads) {
-    const int s = s_victim[i];
+    const int sl = s_victim[i];
     const int f = s_miss[i];
-    const int old = id_of[s];
+    const int old = FAST ? s_vold[i] : id_of[sl];
     if (old >= 0 && old < L * E) {
       slot_of[old] = -1;
       ++my_evict;
     }
-    slot_of[f] = s;
-    id_of[s] = f;
-    stamp[s] = clock;
-    s_slot_e[f - layer * E] = s;
+    slot_of[f] = sl;
+    id_of[sl] = f;
+    stamp[sl] = clock;
+    s_slot_e[f - layer * E] = sl;
     fill_flat[i] = f;
-    fill_slot[i] = s;
+    fill_slot[i] = sl;
   }
   for (int i = q + tid; i < m; i += kLkThreads) host_flat[i - q] = s_miss[i];
-  int n_evict;
-  block_excl_scan(my_evict, s_scan, &n_evict);   // includes a barrier
+  if (my_evict) atomicAdd(&s_evict, my_evict);
+  __syncthreads();
+  const int n_evict = s_evict;
 
   // 6. rewrite routes to slots (-1 = host-computed, masked, invalid, beyond n_tok)
   for (int r = tid; r < T * k; r += kLkThreads) {
@@ -295,7 +354,8 @@ extern "C" int slot_cache_lookup_evict(const mc_cache* c, int32_t layer, const i
     return rc;
   MC_REQUIRE(ids && slots && fill_flat && fill_slot && n_fill && host_flat && n_host,
              "slot_cache_lookup_evict: NULL pointer");
-  hipLaunchKernelGGL(lookup_kernel<false>, dim3(1), dim3(kLkThreads), 0, s, nullptr, 0, nullptr,
+  auto kern = c->S <= kLkFastS ? lookup_kernel<false, true> : lookup_kernel<false, false>;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kLkThreads), 0, s, nullptr, 0, nullptr,
                      nullptr, c->L, c->E, c->S, c->slot_of, c->id_of, c->stamp, c->clock, c->stats,
                      layer, ids, T, k, n_tok, frac_q16, fixed_cap, min_fill, slots, fill_flat,
                      fill_slot, n_fill, host_flat, n_host, kcap);
@@ -319,7 +379,8 @@ extern "C" int moe_route_lookup(const float* logits, int32_t renorm, int32_t* to
   MC_REQUIRE(logits && topk_ids && topk_w && slots && fill_flat && fill_slot && n_fill && host_flat &&
                  n_host,
              "moe_route_lookup: NULL pointer");
-  hipLaunchKernelGGL(lookup_kernel<true>, dim3(1), dim3(kLkThreads), 0, s, logits, renorm, topk_ids,
+  auto kern = c->S <= kLkFastS ? lookup_kernel<true, true> : lookup_kernel<true, false>;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kLkThreads), 0, s, logits, renorm, topk_ids,
                      topk_w, c->L, c->E, c->S, c->slot_of, c->id_of, c->stamp, c->clock, c->stats,
                      layer, topk_ids, T, k, n_tok, frac_q16, fixed_cap, min_fill, slots, fill_flat,
                      fill_slot, n_fill, host_flat, n_host, kcap);

@@ -130,9 +130,12 @@ def test_lookup_qwen_shaped_trace():
     assert o.stats[4] > 0          # the pool wrapped: evictions happened
 
 
-@pytest.mark.parametrize("S", [256, 1024])
-def test_lookup_zipf_batched_valid_count(S):
-    cfg = synth.CONFIGS["zipf_decode"].with_(L=6, steps=12, T=16, S=S)
+@pytest.mark.parametrize("L_,E,S,steps", [(6, 256, 256, 12), (6, 256, 1024, 12), (12, 1024, 4096, 24),
+                                          (12, 1024, 4097, 24)])
+def test_lookup_zipf_batched_valid_count(L_, E, S, steps):
+    """Pools up to 4096 slots keep the slot table in LDS, larger ones read it from global
+    memory; the two cases at that edge wrap their pool (about 8000 fills) and evict."""
+    cfg = synth.CONFIGS["zipf_decode"].with_(L=L_, steps=steps, T=16, S=S, E=E)
     tr = synth.trace(cfg)
     g = GpuLookup(cfg.L, cfg.E, cfg.S, cfg.T, cfg.k)
     o = LruOracle(cfg.L, cfg.E, cfg.S)
@@ -145,6 +148,8 @@ def test_lookup_zipf_batched_valid_count(S):
             assert np.array_equal(a["slots"], b["slots"])
             assert a["fills"] == b["fills"] and a["host"] == b["host"]
         _compare_state(g, o)
+    if S >= 4096:
+        assert o.stats[4] > 0                  # the pool wrapped: evictions happened
 
 
 def test_lookup_invalid_ids_and_masks():
