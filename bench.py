@@ -61,6 +61,14 @@ def _parse():
                     help="run only the batched Zipf decode sweep (bs 1/4/16 x pools 256..4096 slots, one "
                          "process, the pool resized between points) and print its table")
     ap.add_argument("--c5-steps", type=int, default=48, help="timed steps per sweep point")
+    ap.add_argument("--c3", action="store_true",
+                    help="DeepSeek-V4-Flash-shaped hybrid decode (43 layers, 1500 slots, pinned pool of "
+                         "all 11008 experts): q* splits for B_H/B_P in {1.5, 2, 3} x locality {0.5, 0.9}, "
+                         "and the split from this machine's bandwidth profile")
+    ap.add_argument("--c3-steps", type=int, default=48, help="timed steps per C3 run")
+    ap.add_argument("--c3-layers", type=int, default=16,
+                    help="layers of the C3 pool actually built (the box pins at most 64 GiB; the slot "
+                         "pool is scaled to the same share of the experts)")
     ap.add_argument("--fill-mode", choices=("copy", "through", "split"), default="copy",
                     help="how misses reach their slots: copy (mc_fill_slots first), through (the expert "
                          "pass reads the host and writes the slots), split (gate_up through, down banks "
@@ -245,6 +253,9 @@ def main():
     L.lib()   # fails loudly if the library is not built
     if args.c5_sweep:
         print(json.dumps({"c5_sweep": c5_sweep(args, torch, L, synth)}), flush=True)
+        return
+    if args.c3:
+        print(json.dumps({"c3_hybrid": c3_runs(args, torch, L, synth)}), flush=True)
         return
     if args.prefill_only:
         pre, roof = bench_prefill(args, torch, L, synth)
@@ -475,6 +486,149 @@ def c5_sweep(args, torch, L, synth):
         del layers, cache, pool
         torch.cuda.empty_cache()
     return out
+
+
+def c3_runs(args, torch, L, synth):
+    """DeepSeek-V4-Flash-shaped hybrid decode (E=256 top-6, H=4096, I=2048, MXFP4, bs=1):
+    misses split by q* = m * B_P / B_H with at least one fill per call; the rest run on the
+    CPU worker pool over the pinned banks while the GPU fills and runs its routes, and the
+    merge waits for the slower branch.  The full model (43 layers, 11008 experts, 147 GB
+    pinned, 1500 slots) does not fit the 64 GiB of host memory a process can pin here, so
+    `--c3-layers` layers are built with the slot pool scaled to the same share of the
+    experts (1500 / 11008); the per-token figure is 43 x the measured per-layer time.
+    One captured graph per step (the host branch is served from the pinned stage by the
+    worker pool's dispatcher, so the step holds kernels only).  The pool holds 64 distinct seeded experts repeated over its entries: the bytes moved are
+    those of the real pool, and the values do not change the timing (the split's numerics
+    are tested at this expert shape)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer, alloc_banks
+    full = synth.CONFIGS["dsv4_hybrid"]
+    n_layers = max(1, min(full.L, args.c3_layers))
+    cfg = full.with_(L=n_layers, S=max(full.k, round(full.S * n_layers / full.L)))
+    W, K = 8, args.c3_steps
+    n_distinct = 64
+    S_e = synth.expert_bytes(cfg.H, cfg.I, cfg.fmt)
+    log("c3: pinned host pool %d experts x %d B (%.1f GB)" % (cfg.n_flat, S_e, cfg.n_flat * S_e / 1e9))
+    host_t, host_free = alloc_pinned_exact(cfg.n_flat, cfg.H, cfg.I, cfg.fmt, torch)
+    views = {k: v.numpy() for k, v in host_t.items()}
+    distinct = [synth.expert_weights(cfg, f) for f in range(n_distinct)]
+    t0 = time.time()
+
+    def fill(f0):
+        for f in range(f0, min(cfg.n_flat, f0 + 256)):
+            for k, a in distinct[f % n_distinct].items():
+                views[k][f] = a
+        if f0 % 2048 == 0:
+            log("c3: host pool %d/%d (%.0f s)" % (f0, cfg.n_flat, time.time() - t0))
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        list(ex.map(fill, range(0, cfg.n_flat, 256)))
+    log("c3: host pool ready (%.0f s)" % (time.time() - t0))
+    host = BankSet(host_t, cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(alloc_banks(cfg.S, cfg.H, cfg.I, cfg.fmt, device="cuda"), cfg.H, cfg.I, cfg.fmt)
+    workers = L.HostPool(min(16, len(os.sched_getaffinity(0))))
+    prof = L.bandwidth_profile(host.desc, pool.desc, workers, 4, seconds=1.0)
+    log("c3: bandwidth profile: link %.1f GB/s, host experts %.1f GB/s -> fetch fraction %.3f, %s"
+        % (prof["pcie_gbs"], prof["cpu_gbs"], prof["frac_q16"] / 65536.0, prof["backend"]))
+    runs = [(r, p, L.fetch_fraction_q16(1.0, r)) for p in (0.5, 0.9) for r in (1.5, 2.0, 3.0)]
+    runs.append(("measured", 0.5, int(prof["frac_q16"])))
+    out = {"workload": "deepseek-v4-flash-shaped hybrid decode: E=256 top-6, H=4096, I=2048, MXFP4, bs=1; "
+                       "%d of the 43 MoE layers built (pinned pool of %d experts), %d slots (the share "
+                       "1500/11008 of the experts); per token = 43 x per layer" % (cfg.L, cfg.n_flat, cfg.S),
+           "layers_built": cfg.L, "slots": cfg.S,
+           "steps": K, "warmup": W, "host_workers": workers.n_threads,
+           "bandwidth_profile": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in prof.items()},
+           "runs": []}
+    for ratio, p, frac in runs:
+        c = cfg.with_(p=p)
+        tr = synth.trace(c, steps=W + K)
+        logits = torch.from_numpy(np.stack([synth.step_logits(c, tr[s], s) for s in range(W + K)])).cuda()
+        xs = torch.from_numpy(np.stack([np.stack([synth.activations(c, s, l) for l in range(c.L)])
+                                        for s in range(W + K)]).view(np.int16)).cuda()
+        cache = CacheState(c.L, c.E, c.S)
+        cache.reset()
+        layers = [DecodeLayer(cache, host, pool, None, DecodeBuffers(1, c.k, c.H, c.I), frac_q16=frac,
+                              min_fill=1, renorm=c.renorm, hybrid=True, host_pool=workers)
+                  for _ in range(c.L)]
+
+        lg_buf, x_buf = torch.empty_like(logits[0]), torch.empty_like(xs[0])
+
+        def step():
+            for l in range(c.L):
+                layers[l](l, lg_buf[l], x_buf[l])
+        lg_buf.copy_(logits[0])
+        x_buf.copy_(xs[0])
+        step()                                  # eager step 0 (also the capture's warm-up)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for s in range(1, W):
+            lg_buf.copy_(logits[s])
+            x_buf.copy_(xs[s])
+            g.replay()
+        torch.cuda.synchronize()
+        st0 = cache.t["stats"].cpu().numpy().copy()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(W, W + K):
+            lg_buf.copy_(logits[s])
+            x_buf.copy_(xs[s])
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        errs = sum(dl.stage.errors() for dl in layers)
+        if errs:
+            raise RuntimeError("c3: %d merge waits ran out" % errs)
+        ms = e0.elapsed_time(e1) / K
+        ms_layer = ms / c.L
+        d = cache.t["stats"].cpu().numpy() - st0
+        row = {"b_h_over_b_p": ratio, "locality": p, "fetch_fraction": round(frac / 65536.0, 4),
+               "ms_per_layer": round(ms_layer, 4), "ms_per_token_43": round(ms_layer * full.L, 3),
+               "tok_s_43": round(1000.0 / (ms_layer * full.L), 2),
+               "miss_rate": round(float(d[1]) / max(1.0, float(d[0] + d[1])), 4),
+               "fills_per_layer": round(float(d[2]) / (K * c.L), 3),
+               "host_routes_per_layer": round(float(d[3]) / (K * c.L), 3),
+               "link_gbs": round(float(d[2]) * S_e / (ms * K * 1e-3) / 1e9, 2),
+               "host_gbs": round(float(d[3]) * S_e / (ms * K * 1e-3) / 1e9, 2)}
+        log("c3 B_H/B_P %s p %.1f f %.3f: %.3f ms/layer (43 layers: %.2f tok/s), miss %.3f, %.2f fills + "
+            "%.2f host routes per layer" % (ratio, p, frac / 65536.0, ms_layer, row["tok_s_43"],
+                                            row["miss_rate"], row["fills_per_layer"], row["host_routes_per_layer"]))
+        out["runs"].append(row)
+        del g
+        for dl in layers:
+            dl.stage.close()
+        del layers, cache, logits, xs
+    workers.close()
+    del host, pool, views, host_t
+    torch.cuda.synchronize()
+    host_free()
+    return out
+
+
+def alloc_pinned_exact(n, H, I, fmt, torch):
+    """Pinned host banks of exactly n entries each, from hipHostMalloc (torch's pinned
+    allocator rounds every block up to a power of two: 147 GB of banks would pin ~204 GiB).
+    Returns the tensors and a function that frees them."""
+    import ctypes as C
+    from expert_cache_offloaded_amd.runtime import bank_shapes
+    hip = C.CDLL("libamdhip64.so")
+    ptrs, out = [], {}
+    for name, (shp, dt) in bank_shapes(H, I, fmt).items():
+        nbytes = n * int(np.prod(shp)) * torch.empty((), dtype=dt).element_size()
+        p = C.c_void_p()
+        log("pinning %s: %.1f GB" % (name, nbytes / 1e9))
+        rc = hip.hipHostMalloc(C.byref(p), C.c_size_t(nbytes), C.c_uint(0))
+        if rc != 0 or not p.value:
+            raise MemoryError("hipHostMalloc of %d bytes failed (%d)" % (nbytes, rc))
+        ptrs.append(p)
+        np_dt = {torch.uint8: np.uint8, torch.int16: np.int16}[dt]
+        arr = np.ctypeslib.as_array(C.cast(p, C.POINTER(C.c_uint8)), shape=(nbytes,)).view(np_dt)
+        out[name] = torch.from_numpy(arr.reshape((n,) + tuple(shp)))
+
+    def free():
+        out.clear()
+        for p in ptrs:
+            hip.hipHostFree(p)
+    return out, free
 
 
 def bench_prefill(args, torch, L, synth):

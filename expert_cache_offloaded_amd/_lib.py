@@ -97,6 +97,9 @@ _SIGS = {
                                        _P, C.POINTER(BwProfile)]),
     "mc_recommend_backend": (C.c_int32, [C.c_double, C.c_double, C.c_double]),
     "mc_hybrid_stage_bytes": (C.c_size_t, [_I32, _I32, _I32]),
+    "mc_hybrid_stage_alloc": (C.c_void_p, [C.c_size_t]),
+    "mc_hybrid_stage_free": (C.c_int, [C.c_void_p]),
+    "mc_hybrid_stage_errors": (C.c_uint32, [C.c_void_p]),
     "hybrid_split_merge": (C.c_int, [C.POINTER(Hybrid), _I32, _P]),
     "mc_finish_bf16": (C.c_int, [_P, _I32, _I32, _P, _P, _P]),
 }
@@ -332,6 +335,40 @@ def host_experts(pool: Optional[HostPool], x, ids, w, layer: int, E: int, host: 
 
 def hybrid_stage_bytes(T: int, k: int, H: int) -> int:
     return int(lib().mc_hybrid_stage_bytes(T, k, H))
+
+
+class HybridStage:
+    """Pinned staging memory of one hybrid layer call (fine-grained, from the library)."""
+
+    def __init__(self, T: int, k: int, H: int):
+        self.nbytes = hybrid_stage_bytes(T, k, H)
+        self.ptr = lib().mc_hybrid_stage_alloc(self.nbytes)
+        if not self.ptr:
+            raise MemoryError(lib().mc_last_error().decode())
+
+    def data_ptr(self) -> int:
+        return self.ptr
+
+    def numel(self) -> int:
+        return self.nbytes
+
+    def element_size(self) -> int:
+        return 1
+
+    def errors(self) -> int:
+        """Merge waits on this stage that ran out (0 when every host branch answered)."""
+        return int(lib().mc_hybrid_stage_errors(self.ptr))
+
+    def close(self) -> None:
+        if self.ptr:
+            _check("mc_hybrid_stage_free", lib().mc_hybrid_stage_free(self.ptr))
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def make_hybrid(x, ids_raw, slots, w, layer: int, E: int, n_tok, host: Banks, pool: HostPool,

@@ -20,17 +20,32 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
 #include <thread>
 #include <vector>
 
+#include "hybrid_stage.h"
 #include "mc.h"
 
 namespace mc {
 void set_error(const char* fmt, ...);
 void clear_error();
+int host_experts_run(mc_host_pool* pool, const uint16_t* x, const int32_t* ids, const float* w,
+                     int T, int k, int layer, int E, const mc_banks* host, float* y);
+
+// Stages served by the dispatchers (every pool's dispatcher scans the entries of its
+// own pool; the lock is held while a stage is served, so dropping a stage waits until
+// no dispatcher is using it).
+struct StageEntry {
+  StageHeader* st;
+  mc_host_pool* pool;
+  uint64_t handled;   // the last request number this entry has completed
+};
+static std::mutex g_stage_mu;
+static std::vector<StageEntry> g_stages;
 }  // namespace mc
 
 // ------------------------------------------------------------------ worker pool
@@ -46,11 +61,9 @@ struct mc_host_pool {
   int generation = 0;
   int acked = 0;
   bool stop = false;
-  // asynchronous job (hybrid branch)
+  // dispatcher of the hybrid stages (the host branch)
   std::thread driver;
-  std::function<void()> job;
-  bool job_pending = false, job_done = true, driver_stop = false;
-  std::condition_variable cv_job, cv_job_done;
+  std::atomic<bool> driver_stop{false};
 
   void worker_loop() {
     int seen = 0;
@@ -97,41 +110,48 @@ struct mc_host_pool {
     fn = nullptr;
   }
 
-  void driver_loop() {
-    for (;;) {
-      std::function<void()> j;
-      {
-        std::unique_lock<std::mutex> lk(mu);
-        cv_job.wait(lk, [&] { return driver_stop || job_pending; });
-        if (driver_stop) return;
-        j = std::move(job);
-        job_pending = false;
-      }
-      j();
-      {
-        std::lock_guard<std::mutex> lk(mu);
-        job_done = true;
-      }
-      cv_job_done.notify_all();
-    }
-  }
-
-  void submit(std::function<void()> j) {
-    {
-      std::unique_lock<std::mutex> lk(mu);
-      cv_job_done.wait(lk, [&] { return job_done; });
-      job = std::move(j);
-      job_pending = true;
-      job_done = false;
-    }
-    cv_job.notify_all();
-  }
-
-  void wait_job() {
-    std::unique_lock<std::mutex> lk(mu);
-    cv_job_done.wait(lk, [&] { return job_done; });
-  }
+  // Serves the hybrid stages of this pool: a stage whose request number has moved past
+  // the last one served gets its host partial computed (this thread takes part in the
+  // parallel work), then its completion number raised.  Polls without pause while calls
+  // keep coming; after about a millisecond without work it polls every 50 us.
+  void driver_loop();
 };
+
+void mc_host_pool::driver_loop() {
+  int idle = 0;
+  while (!driver_stop.load(std::memory_order_relaxed)) {
+    bool served = false;
+    {
+      std::lock_guard<std::mutex> lk(mc::g_stage_mu);
+      for (auto& e : mc::g_stages) {
+        if (e.pool != this) continue;
+        uint8_t* base = reinterpret_cast<uint8_t*>(e.st);
+        mc::StageReq* req = reinterpret_cast<mc::StageReq*>(base + e.st->off_req);
+        const uint64_t seq = __atomic_load_n(&req->seq, __ATOMIC_ACQUIRE);
+        if (seq == e.handled) continue;
+        const mc::StageHeader& h = *e.st;
+        const int nt = std::min(std::max(req->ntok, 0), h.T);
+        float* y = reinterpret_cast<float*>(base + h.off_y);
+        memset(y, 0, sizeof(float) * (size_t)nt * h.H);
+        mc::host_experts_run(this, reinterpret_cast<const uint16_t*>(base + h.off_x),
+                             reinterpret_cast<const int32_t*>(base + h.off_ids),
+                             reinterpret_cast<const float*>(base + h.off_w), nt, h.k, req->layer, h.E,
+                             &h.host, y);
+        mc::StageDone* done = reinterpret_cast<mc::StageDone*>(base + h.off_done);
+        __atomic_store_n(&done->seq, seq, __ATOMIC_RELEASE);
+        e.handled = seq;
+        served = true;
+      }
+    }
+    if (served) {
+      idle = 0;
+    } else if (++idle < 20000) {
+      _mm_pause();
+    } else {
+      std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
+  }
+}
 
 extern "C" mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* cpu_ids) {
   mc::clear_error();
@@ -166,31 +186,38 @@ extern "C" mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* c
 
 extern "C" void mc_host_pool_destroy(mc_host_pool* p) {
   if (!p) return;
-  p->wait_job();
+  p->driver_stop.store(true);
+  p->driver.join();
+  {
+    std::lock_guard<std::mutex> lk(mc::g_stage_mu);
+    mc::g_stages.erase(std::remove_if(mc::g_stages.begin(), mc::g_stages.end(),
+                                      [p](const mc::StageEntry& e) { return e.pool == p; }),
+                       mc::g_stages.end());
+  }
   {
     std::lock_guard<std::mutex> lk(p->mu);
     p->stop = true;
-    p->driver_stop = true;
   }
   p->cv_work.notify_all();
-  p->cv_job.notify_all();
   for (auto& t : p->threads) t.join();
-  p->driver.join();
   delete p;
 }
 
 namespace mc {
 
-void host_pool_submit(mc_host_pool* p, std::function<void()> job) {
-  if (!p) {
-    job();
-    return;
-  }
-  p->submit(std::move(job));
+void host_pool_add_stage(mc_host_pool* pool, StageHeader* stage) {
+  std::lock_guard<std::mutex> lk(g_stage_mu);
+  for (auto& e : g_stages)
+    if (e.st == stage) return;
+  const StageDone* done = reinterpret_cast<const StageDone*>(reinterpret_cast<uint8_t*>(stage) + stage->off_done);
+  g_stages.push_back(StageEntry{stage, pool, __atomic_load_n(&done->seq, __ATOMIC_ACQUIRE)});
 }
 
-void host_pool_wait(mc_host_pool* p) {
-  if (p) p->wait_job();
+void host_pool_drop_stage(StageHeader* stage) {
+  std::lock_guard<std::mutex> lk(g_stage_mu);
+  g_stages.erase(std::remove_if(g_stages.begin(), g_stages.end(),
+                                [stage](const StageEntry& e) { return e.st == stage; }),
+                 g_stages.end());
 }
 
 // ------------------------------------------------------------------ expert kernels

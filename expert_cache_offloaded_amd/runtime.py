@@ -137,8 +137,7 @@ class DecodeLayer:
         elif fill_mode == "through":
             self.fill = L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill)
         if hybrid:
-            nb = L.hybrid_stage_bytes(bufs.T, bufs.k, bufs.H)
-            self.stage = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+            self.stage = L.HybridStage(bufs.T, bufs.k, bufs.H)
         self._hy = {}
         self._sh = {}
 

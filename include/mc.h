@@ -353,7 +353,9 @@ int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const float* w, 
 
 /* Persistent CPU worker pool ([jjl357] "8.3": persistent C++ workers pinned to cores). */
 typedef struct mc_host_pool mc_host_pool;
-/* n_threads >= 1; cpu_ids: NULL = no pinning, else n_threads core ids. NULL on failure. */
+/* n_threads >= 1; cpu_ids: NULL = no pinning, else n_threads core ids. NULL on failure.
+ * Besides its workers the pool runs one dispatcher thread that serves the hybrid stages
+ * registered with it (see hybrid_split_merge); it polls while calls keep coming. */
 mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* cpu_ids);
 void mc_host_pool_destroy(mc_host_pool* p);
 
@@ -402,8 +404,21 @@ int mc_bandwidth_profile(const mc_banks* host, const mc_banks* pool, mc_host_poo
  */
 int32_t mc_recommend_backend(double cpu_gbs, double pcie_gbs, double threshold);
 
-/* Pinned staging bytes of one hybrid layer call (header + x, ids, w, y_host). */
+/* Pinned staging bytes of one hybrid layer call (header, request and completion
+ * words, x, ids, w, y_host). */
 size_t mc_hybrid_stage_bytes(int32_t T, int32_t k, int32_t H);
+
+/*
+ * Staging memory of a hybrid layer call ([jjl357] "6.8": the CPU writes its partial to
+ * pinned memory).  Fine-grained (coherent) pinned host memory, zeroed, so that the GPU
+ * and the host see each other's stores to it while a kernel runs.  Returns NULL on
+ * failure (mc_last_error).  mc_hybrid_stage_free synchronises the device, removes the
+ * stage from the worker pool's dispatcher and frees it; NULL is a no-op.
+ * mc_hybrid_stage_errors: merge waits on the stage that ran out (0 normally).
+ */
+void* mc_hybrid_stage_alloc(size_t bytes);
+int mc_hybrid_stage_free(void* stage);
+uint32_t mc_hybrid_stage_errors(const void* stage);
 
 typedef struct {
   const void* x_bf16;        /* device bf16 [T][H]                                   */
@@ -414,12 +429,12 @@ typedef struct {
   const int32_t* n_tok;      /* device valid count or NULL                           */
   const mc_banks* host;      /* pinned host banks by flat id                         */
   mc_host_pool* pool;        /* CPU workers                                          */
-  void* pinned_stage;        /* caller-owned pinned host memory, mc_hybrid_stage_bytes */
+  void* pinned_stage;        /* from mc_hybrid_stage_alloc, mc_hybrid_stage_bytes      */
   size_t stage_bytes;
   float* gpu_w;              /* device fp32 [T][k] out: w where slot >= 0, else 0   */
   int32_t* host_ids;         /* device int32 [T][k] out: raw id where slot < 0, else -1 */
   float* y_acc;              /* device fp32 [T][H]: GPU partial (moe_experts_decode) */
-  float* y_host;             /* device fp32 [T][H] out: host partial, copied back    */
+  float* y_host;             /* device fp32 [T][H] out: the host partial (rows < n_tok) */
   void* y_bf16;              /* device bf16 [T][H] out: bf16(y_acc + y_host)         */
 } mc_hybrid;
 
@@ -428,14 +443,20 @@ enum { MC_SPLIT_SUBMIT = 0, MC_MERGE = 1 };
 /*
  * Exact split and merge of one decode layer ([jjl357] "6.2", "6.8", "6.9";
  * [wanger] "代码全链路"; [juhe] "为什么可以直接相加").
- * MC_SPLIT_SUBMIT: kernel writes gpu_w and host_ids (complementary masks: every
- *   valid route is on exactly one side), copies x / host_ids / w to the pinned
- *   stage and enqueues the host branch on the worker pool through a host function
- *   that returns at once, so the GPU continues with fills and moe_experts_decode.
- * MC_MERGE: waits (host function) for the host branch, copies its fp32 partial to
- *   y_host, and writes y_bf16 = bf16_rne(y_acc + y_host) — one rounding.
- * Every SPLIT_SUBMIT must be followed by a MERGE on the same stream before the
- * stage is reused.
+ * MC_SPLIT_SUBMIT: one kernel writes gpu_w and host_ids (complementary masks: every
+ *   valid route is on exactly one side), writes x / host ids / w / the valid count /
+ *   the layer into the stage and then raises the stage's request number.  The worker
+ *   pool's dispatcher thread (polling the stages it serves) computes the host partial
+ *   into the stage and raises the completion number; meanwhile the GPU continues
+ *   with fills and moe_experts_decode.  No host function and no copy is enqueued, so
+ *   the sequence can be captured in a hipGraph and replayed.
+ * MC_MERGE: one kernel waits for the completion number (bounded, about 4 s: a wait
+ *   that runs out is counted, see mc_hybrid_stage_errors, and leaves wrong values),
+ *   writes the host partial to y_host and y_bf16 = bf16_rne(y_acc + y_host) — one
+ *   rounding.
+ * Every SPLIT_SUBMIT must be followed by a MERGE on the same stream before the stage
+ * is reused.  A stage keeps the (T, k, H, E, host banks, worker pool) of its first
+ * call (another set is MC_EINVAL).  The pool must outlive the calls on its stages.
  */
 int hybrid_split_merge(const mc_hybrid* h, int32_t phase, hipStream_t s);
 

@@ -247,6 +247,92 @@ def test_dsv4_shaped_hybrid_steps(ratio, p):
     hp.close()
 
 
+def test_hybrid_step_in_a_graph():
+    """The hybrid split and merge enqueue kernels only (the host branch is served from the
+    stage by the worker pool's dispatcher): a captured 3-layer step, replayed with new
+    routes and activations, matches the oracle on every replay, and no merge wait runs out."""
+    from expert_cache_offloaded_amd import HostPool
+    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer
+    from oracle import route
+    cfg = synth.CONFIGS["dsv4_hybrid"].with_(L=3, E=16, S=10, steps=6, p=0.5)
+    tr = synth.trace(cfg)
+    host_np = synth.host_pool(cfg)
+    host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(empty_device_banks(cfg, cfg.S), cfg.H, cfg.I, cfg.fmt)
+    cs = CacheState(cfg.L, cfg.E, cfg.S)
+    cs.reset()
+    frac = 1 << 15
+    hp = HostPool(4)
+    layers = [DecodeLayer(cs, host, pool, None, DecodeBuffers(1, cfg.k, cfg.H, cfg.I), frac_q16=frac,
+                          hybrid=True, host_pool=hp) for _ in range(cfg.L)]
+    lg_buf = torch.empty((cfg.L, 1, cfg.E), dtype=torch.float32, device="cuda")
+    x_buf = torch.empty((cfg.L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    steps = []
+
+    def load(s):
+        lgs = synth.step_logits(cfg, tr[s], s)
+        xs = [synth.activations(cfg, s, l) for l in range(cfg.L)]
+        lg_buf.copy_(torch.from_numpy(lgs))
+        x_buf.copy_(torch.from_numpy(np.stack(xs).view(np.int16)))
+        steps.append((lgs, xs))
+
+    def run():
+        for l in range(cfg.L):
+            layers[l](l, lg_buf[l], x_buf[l])
+
+    def check():
+        torch.cuda.synchronize()
+        lgs, xs = steps[-1]
+        for l in range(cfg.L):
+            ids, w = route(lgs[l], cfg.k)
+            res = o.lookup(l, ids, frac, 1, 1)
+            assert np.array_equal(layers[l].b.slots.cpu().numpy(), res["slots"])
+            yg, yh, _, _ = hybrid_partials(xs[l], ids, res["slots"], w, host_np, l, cfg.E, cfg.fmt, cfg.H, cfg.I)
+            assert_bf16_close(layers[l].b.y, yg + yh, "replay %d layer %d" % (len(steps) - 1, l))
+
+    load(0)
+    run()                                   # eager first step (also the capture's warm-up)
+    check()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for s in range(1, cfg.steps):
+        load(s)
+        g.replay()
+        check()
+    assert o.stats[3] > 0                   # some misses ran on the host during the replays
+    assert all(dl.stage.errors() == 0 for dl in layers)
+    del g
+    for dl in layers:
+        dl.stage.close()
+    hp.close()
+
+
+def test_hybrid_stage_must_be_coherent():
+    """A stage of ordinary pinned memory is refused: its GPU and host stores need not be
+    visible to each other while a kernel runs."""
+    from expert_cache_offloaded_amd import _lib as L
+    from expert_cache_offloaded_amd import HostPool, make_banks
+    cfg = synth.CONFIGS["tiny"]
+    host_np = synth.host_pool(cfg)
+    host = make_banks(cfg.fmt, cfg.H, cfg.I, pinned_banks(cfg, host_np))
+    T, k = 1, cfg.k
+    i32 = dict(dtype=torch.int32, device="cuda")
+    x = torch.zeros((T, cfg.H), dtype=torch.int16, device="cuda")
+    ids, slots = torch.zeros((T, k), **i32), torch.full((T, k), -1, **i32)
+    w = torch.full((T, k), 0.5, dtype=torch.float32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    stage = torch.empty(L.hybrid_stage_bytes(T, k, cfg.H), dtype=torch.uint8, pin_memory=True)
+    hp = HostPool(2)
+    hy = L.make_hybrid(x, ids, slots, w, 0, cfg.E, None, host, hp, stage, torch.empty((T, k), **f32),
+                       torch.empty((T, k), **i32), torch.zeros((T, cfg.H), **f32), torch.zeros((T, cfg.H), **f32),
+                       torch.empty((T, cfg.H), dtype=torch.int16, device="cuda"))
+    with pytest.raises(RuntimeError, match="mc_hybrid_stage_alloc"):
+        L.hybrid_split_merge(hy, L.MC_SPLIT_SUBMIT)
+    hp.close()
+
+
 @pytest.mark.parametrize("cname,T,steps", [("qwen_decode", 1, 4), ("zipf_decode", 4, 3)])
 def test_fill_through_equals_fill_then_decode(cname, T, steps):
     """Fill-through (the expert pass reads filled experts from the host and writes their
