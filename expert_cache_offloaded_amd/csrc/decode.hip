@@ -9,15 +9,15 @@
 // bound by HBM bandwidth; at batch 1 a layer moves only ~15 MB, so what matters is
 // having every weight load of a wave in flight at once (no branch or conversion
 // between a load and the next one).  Two kernels, no cross-workgroup waiting:
-//   gate_up: workgroup = (unit, 16 intermediate rows); a unit is one distinct slot of
+//   gate_up: workgroup = (unit, 4 WR intermediate rows); a unit is one distinct slot of
 //      the call, run by the grid column of the first route that holds it, or the
-//      shared expert.  Each wave owns 4 gate rows and the 4 matching up rows; lane
+//      shared expert.  Each wave owns WR gate rows and the WR matching up rows; lane
 //      l reads the 16-byte chunks l, l+64, ... of every row (one coalesced 1 KiB
 //      row slice per load instruction), keeps them in registers and reuses them for
 //      every token that routes to the unit.  Dot
 //      products run on packed bf16 (MXFP4 -> bf16 is exact) with fp32 accumulation;
 //      h = silu(g) * u is written in fp32 per route.
-//   down: workgroup = (8 hidden rows, one token), over every route of the token.
+//   down: workgroup = (ROWS hidden rows, one token), over every route of the token.
 //      The token's h vectors are staged in LDS; each wave takes every fourth route, loads all of
 //      its rows first, then computes; the waves' partial sums meet in LDS and are
 //      added in a fixed order, so every output element is written once (no atomics,
@@ -32,9 +32,10 @@
 namespace mc {
 
 constexpr int kThreads = 256;
-constexpr int kA_RowsI = 16;                 // gate_up: intermediate rows per workgroup
-constexpr int kA_WaveRows = kA_RowsI / 4;    // per wave: 4 gate + 4 up rows
-constexpr int kB_Rows = 8;                   // down: hidden rows per workgroup
+// gate_up: WR intermediate rows per wave (WR gate + WR up rows), 4 WR per workgroup;
+// down: ROWS hidden rows per workgroup.  Chosen per call: single-token calls take the
+// smaller gate_up tile (more workgroups for few units), batched calls the larger down
+// tile (a token's h staged once for more rows).
 constexpr int kB_RoutesPerWave = 3;          // down: routes a wave holds in registers at once
 constexpr int kMaxRoutes = 1024;
 constexpr int kMaxTok = 64;
@@ -176,7 +177,7 @@ __device__ __forceinline__ uint64_t routes_with_slot(const DecodeArgs& a, int ba
 
 // ---------------------------------------------------------------- gate_up kernel
 
-template <int FMT, int CPL>
+template <int FMT, int CPL, int WR>
 __global__ void __launch_bounds__(kThreads)
 gate_up_kernel(DecodeArgs a) {
   // column u < T*k: route u's slot, when no earlier route of the call holds it (the
@@ -198,7 +199,7 @@ gate_up_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
-  const int i0 = blockIdx.y * kA_RowsI + wave * kA_WaveRows;   // first intermediate row
+  const int i0 = blockIdx.y * (4 * WR) + wave * WR;   // first intermediate row
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;             // elements per 16-B chunk
   const int n_chunks = H / ELEMS;
   const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)H / 2 : (size_t)H * 2;
@@ -234,11 +235,11 @@ gate_up_kernel(DecodeArgs a) {
     okq[q] = c < n_chunks;
     cq[q] = okq[q] ? c : n_chunks - 1;
   }
-  uint4 wv[2 * kA_WaveRows][CPL];
-  uint32_t sb[2 * kA_WaveRows][CPL];
+  uint4 wv[2 * WR][CPL];
+  uint32_t sb[2 * WR][CPL];
 #pragma unroll
-  for (int r = 0; r < 2 * kA_WaveRows; ++r) {
-    const int row = r < kA_WaveRows ? i0 + r : I + i0 + (r - kA_WaveRows);
+  for (int r = 0; r < 2 * WR; ++r) {
+    const int row = r < WR ? i0 + r : I + i0 + (r - WR);
     const uint4* rp = reinterpret_cast<const uint4*>(gu + (size_t)row * row_bytes);
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
@@ -282,9 +283,9 @@ gate_up_kernel(DecodeArgs a) {
         xp[q][4 * v + 3] = xx.w;
       }
     }
-    float acc[2 * kA_WaveRows];
+    float acc[2 * WR];
 #pragma unroll
-    for (int r = 0; r < 2 * kA_WaveRows; ++r) {
+    for (int r = 0; r < 2 * WR; ++r) {
       acc[r] = 0.0f;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
@@ -296,14 +297,14 @@ gate_up_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int r = 0; r < 2 * kA_WaveRows; ++r) acc[r] = wave_sum(acc[r]);
-    if (lane < kA_WaveRows) {
-      float g = acc[0], up = acc[kA_WaveRows];
+    for (int r = 0; r < 2 * WR; ++r) acc[r] = wave_sum(acc[r]);
+    if (lane < WR) {
+      float g = acc[0], up = acc[WR];
 #pragma unroll
-      for (int r = 1; r < kA_WaveRows; ++r)
+      for (int r = 1; r < WR; ++r)
         if (lane == r) {
           g = acc[r];
-          up = acc[kA_WaveRows + r];
+          up = acc[WR + r];
         }
       float* dst = shared_unit ? a.h_shared + (size_t)t * I : a.h_route + (size_t)route * I;
       dst[i0 + lane] = silu(g) * up;
@@ -312,8 +313,8 @@ gate_up_kernel(DecodeArgs a) {
   // fill-through: the rows this wave read from the host go into the slot
   if (wb_gu) {
 #pragma unroll
-    for (int r = 0; r < 2 * kA_WaveRows; ++r) {
-      const int row = r < kA_WaveRows ? i0 + r : I + i0 + (r - kA_WaveRows);
+    for (int r = 0; r < 2 * WR; ++r) {
+      const int row = r < WR ? i0 + r : I + i0 + (r - WR);
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
         if (!okq[q]) continue;
@@ -326,20 +327,20 @@ gate_up_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- down kernel
 
-template <int FMT, int LPR, int CPLB>
+template <int FMT, int LPR, int CPLB, int ROWS>
 __global__ void __launch_bounds__(kThreads)
 down_kernel(DecodeArgs a) {
   extern __shared__ float s_h[];                 // [k + 1][I]: one token's route vectors (swizzled)
-  __shared__ float s_part[4][kB_Rows];
+  __shared__ float s_part[4][ROWS];
   __shared__ int32_t s_rslot[kMaxRoutes];        // slot of each route of the token (-1 = none)
   __shared__ float s_rgate[kMaxRoutes];
   __shared__ int32_t s_rsrc[kMaxRoutes];         // fill-through host source, -1 = slot
   const int nt = valid_tokens(a);
   const int t = blockIdx.y;
   const int H = a.H, I = a.I, k = a.k;
-  const int r0 = blockIdx.x * kB_Rows;
+  const int r0 = blockIdx.x * ROWS;
   if (t >= nt) {                                 // a token beyond the valid count: its rows
-    if (threadIdx.x < kB_Rows && r0 + (int)threadIdx.x < H) {
+    if (threadIdx.x < ROWS && r0 + (int)threadIdx.x < H) {
       const size_t o = (size_t)t * H + r0 + threadIdx.x;
       if (!a.accumulate) a.y[o] = 0.0f;
       if (a.y_bf16) a.y_bf16[o] = 0;
@@ -347,7 +348,7 @@ down_kernel(DecodeArgs a) {
     return;
   }
   float y_old = 0.0f;                            // the value accumulated into, read early
-  if (a.accumulate && threadIdx.x < kB_Rows && r0 + (int)threadIdx.x < H)
+  if (a.accumulate && threadIdx.x < ROWS && r0 + (int)threadIdx.x < H)
     y_old = a.y[(size_t)t * H + r0 + threadIdx.x];
   for (int v = threadIdx.x; v < k; v += kThreads) {
     const int r = t * k + v;
@@ -362,10 +363,10 @@ down_kernel(DecodeArgs a) {
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;
   constexpr int E4 = ELEMS / 4;                              // float4 of h per chunk
   constexpr int RPP = 64 / LPR;                              // rows per pass of a wave
-  constexpr int PASSES = kB_Rows >= RPP ? kB_Rows / RPP : 1;
+  constexpr int PASSES = ROWS >= RPP ? ROWS / RPP : 1;
   const int n_chunks = I / ELEMS;
   const int row_sub = lane / LPR, c_lane = lane % LPR;
-  const bool lane_rows = RPP <= kB_Rows || row_sub < kB_Rows;
+  const bool lane_rows = RPP <= ROWS || row_sub < ROWS;
   const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)I / 2 : (size_t)I * 2;
   const size_t per = (size_t)H * row_bytes;
   const size_t per_s = (size_t)H * I / 32;
@@ -490,7 +491,7 @@ down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
           const int rl = row_sub + RPP * p, row = r0 + rl;
-          if (rl >= kB_Rows || row >= H) continue;
+          if (rl >= ROWS || row >= H) continue;
 #pragma unroll
           for (int q = 0; q < CPLB; ++q) {
             if (!okq[q]) continue;
@@ -504,10 +505,10 @@ down_kernel(DecodeArgs a) {
     for (int p = 0; p < PASSES; ++p) {
       const float sum = group_sum(acc[p], LPR);
       const int rl = row_sub + RPP * p;
-      if (c_lane == 0 && lane_rows && rl < kB_Rows) s_part[wave][rl] = sum;
+      if (c_lane == 0 && lane_rows && rl < ROWS) s_part[wave][rl] = sum;
     }
     __syncthreads();
-    if (threadIdx.x < kB_Rows) {
+    if (threadIdx.x < ROWS) {
       const int row = r0 + threadIdx.x;
       float v = ((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
                 s_part[3][threadIdx.x];
@@ -521,29 +522,43 @@ down_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <int FMT>
-static void launch_gate_up(const DecodeArgs& a, int cpl, dim3 grid, hipStream_t s) {
+template <int FMT, int WR>
+static void launch_gate_up_w(const DecodeArgs& a, int cpl, dim3 grid, hipStream_t s) {
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((gate_up_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gate_up_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((gate_up_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gate_up_kernel<FMT, 1, WR>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gate_up_kernel<FMT, 2, WR>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((gate_up_kernel<FMT, 4, WR>), grid, dim3(kThreads), 0, s, a); break;
   }
 }
 
-template <int FMT, int LPR>
-static void launch_down_l(const DecodeArgs& a, int cplb, dim3 grid, size_t lds, hipStream_t s) {
-  if (cplb == 1)
-    hipLaunchKernelGGL((down_kernel<FMT, LPR, 1>), grid, dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL((down_kernel<FMT, LPR, 2>), grid, dim3(kThreads), lds, s, a);
+template <int FMT>
+static void launch_gate_up(const DecodeArgs& a, int cpl, int wr, dim3 grid, hipStream_t s) {
+  if (wr == 2) launch_gate_up_w<FMT, 2>(a, cpl, grid, s);
+  else launch_gate_up_w<FMT, 4>(a, cpl, grid, s);
 }
 
+template <int FMT, int LPR, int ROWS>
+static void launch_down_l(const DecodeArgs& a, int cplb, dim3 grid, size_t lds, hipStream_t s) {
+  if (cplb == 1)
+    hipLaunchKernelGGL((down_kernel<FMT, LPR, 1, ROWS>), grid, dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((down_kernel<FMT, LPR, 2, ROWS>), grid, dim3(kThreads), lds, s, a);
+}
+
+// rows = 16 only with lpr 4 or 16 (the 64-lane row form keeps 8)
 template <int FMT>
-static void launch_down(const DecodeArgs& a, int lpr, int cplb, dim3 grid, size_t lds, hipStream_t s) {
+static void launch_down(const DecodeArgs& a, int lpr, int cplb, int rows, dim3 grid, size_t lds,
+                        hipStream_t s) {
   switch (lpr) {
-    case 4: launch_down_l<FMT, 4>(a, cplb, grid, lds, s); break;
-    case 16: launch_down_l<FMT, 16>(a, cplb, grid, lds, s); break;
-    default: launch_down_l<FMT, 64>(a, cplb, grid, lds, s); break;
+    case 4:
+      if (rows == 16) launch_down_l<FMT, 4, 16>(a, cplb, grid, lds, s);
+      else launch_down_l<FMT, 4, 8>(a, cplb, grid, lds, s);
+      break;
+    case 16:
+      if (rows == 16) launch_down_l<FMT, 16, 16>(a, cplb, grid, lds, s);
+      else launch_down_l<FMT, 16, 8>(a, cplb, grid, lds, s);
+      break;
+    default: launch_down_l<FMT, 64, 8>(a, cplb, grid, lds, s); break;
   }
 }
 
@@ -664,18 +679,20 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
     if (a.kcap == 0) a.f_gu = a.f_dn = nullptr;
   }
 
-  dim3 grid_a(T * k + has_shared, I / kA_RowsI);
+  const int wr = T == 1 ? 2 : 4;
+  const int rows = (T >= 4 && lpr != 64) ? 16 : 8;
+  dim3 grid_a(T * k + has_shared, I / (4 * wr));
   if (fmt == MC_MXFP4)
-    launch_gate_up<MC_MXFP4>(a, cpl, grid_a, s);
+    launch_gate_up<MC_MXFP4>(a, cpl, wr, grid_a, s);
   else
-    launch_gate_up<MC_BF16>(a, cpl, grid_a, s);
+    launch_gate_up<MC_BF16>(a, cpl, wr, grid_a, s);
   MC_LAUNCH_CHECK();
   if (fill && fill->down_after) MC_HIP(hipStreamWaitEvent(s, fill->down_after, 0));
-  dim3 grid_b((H + kB_Rows - 1) / kB_Rows, T);
+  dim3 grid_b((H + rows - 1) / rows, T);
   if (fmt == MC_MXFP4)
-    launch_down<MC_MXFP4>(a, lpr, cplb, grid_b, lds, s);
+    launch_down<MC_MXFP4>(a, lpr, cplb, rows, grid_b, lds, s);
   else
-    launch_down<MC_BF16>(a, lpr, cplb, grid_b, lds, s);
+    launch_down<MC_BF16>(a, lpr, cplb, rows, grid_b, lds, s);
   MC_LAUNCH_CHECK();
   return MC_OK;
 }
