@@ -36,8 +36,7 @@ split_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ slots,
              int layer, const int32_t* __restrict__ n_tok, float* __restrict__ gpu_w,
              int32_t* __restrict__ host_ids, uint8_t* __restrict__ stage, StageHeader hd) {
   const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
-  int32_t* st_ids = reinterpret_cast<int32_t*>(stage + hd.off_ids);
-  float* st_w = reinterpret_cast<float*>(stage + hd.off_w);
+  int any_host = 0;
   for (int r = threadIdx.x; r < T * k; r += kSplitThreads) {
     const bool valid = r / k < nt;
     const int id = ids[r];
@@ -46,7 +45,14 @@ split_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ slots,
     const bool on_host = valid && slot < 0 && id >= 0 && id < E;
     gpu_w[r] = on_gpu ? w[r] : 0.0f;
     host_ids[r] = on_host ? id : -1;
-    st_ids[r] = on_host ? id : -1;
+    any_host |= on_host;
+  }
+  // a call with no host route leaves the stage alone (its merge does not wait either)
+  if (!__syncthreads_or(any_host)) return;
+  int32_t* st_ids = reinterpret_cast<int32_t*>(stage + hd.off_ids);
+  float* st_w = reinterpret_cast<float*>(stage + hd.off_w);
+  for (int r = threadIdx.x; r < T * k; r += kSplitThreads) {
+    st_ids[r] = host_ids[r];
     st_w[r] = w[r];
   }
   const uint4* xs = reinterpret_cast<const uint4*>(x);
@@ -65,17 +71,19 @@ split_kernel(const int32_t* __restrict__ ids, const int32_t* __restrict__ slots,
   }
 }
 
-// Waits until the host branch has completed this call (thread 0 of each workgroup
-// polls the completion number; bounded: a wait that runs out counts in req.err and
-// the output is then wrong), then y_bf16 = bf16_rne(y_acc + y_host): one rounding of
+// If the call has host routes, waits until the host branch has completed it (thread 0
+// of each workgroup polls the completion number; bounded: a wait that runs out counts
+// in req.err and the output is then wrong); then y_bf16 = bf16_rne(y_acc + y_host): one rounding of
 // the summed fp32 partials; the host partial is also copied to y_host (device).
-__global__ void merge_kernel(const float* __restrict__ y_acc, float* __restrict__ y_host, int T, int H,
-                             const int32_t* __restrict__ n_tok, uint16_t* __restrict__ out,
-                             uint8_t* __restrict__ stage, StageHeader hd) {
-  __shared__ int s_ok;
+__global__ void merge_kernel(const float* __restrict__ y_acc, float* __restrict__ y_host, int T, int k, int H,
+                             const int32_t* __restrict__ n_tok, const int32_t* __restrict__ host_ids,
+                             uint16_t* __restrict__ out, uint8_t* __restrict__ stage, StageHeader hd) {
   StageReq* req = reinterpret_cast<StageReq*>(stage + hd.off_req);
   const StageDone* done = reinterpret_cast<const StageDone*>(stage + hd.off_done);
-  if (threadIdx.x == 0) {
+  int mine = 0;
+  for (int r = threadIdx.x; r < T * k; r += blockDim.x) mine |= host_ids[r] >= 0;
+  const bool any_host = __syncthreads_or(mine);    // the split rang the stage only then
+  if (any_host && threadIdx.x == 0) {
     const uint64_t want = __hip_atomic_load(&req->seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     int ok = 0;
     for (int polls = 0; polls < kMergeSpinPolls; ++polls) {
@@ -86,17 +94,16 @@ __global__ void merge_kernel(const float* __restrict__ y_acc, float* __restrict_
       __builtin_amdgcn_s_sleep(8);
     }
     if (!ok && blockIdx.x == 0) __hip_atomic_fetch_add(&req->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    s_ok = ok;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");   // system scope: the host's stores to y
+  if (any_host) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");   // system scope: the host's stores to y
   const float* yh = reinterpret_cast<const float*>(stage + hd.off_y);
   const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
   const int64_t n = (int64_t)T * H;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const bool valid = (i / H) < nt;
-    const float h = valid ? yh[i] : 0.0f;
+    const float h = valid && any_host ? yh[i] : 0.0f;
     y_host[i] = h;
     out[i] = valid ? f32_to_bf16_rne(y_acc[i] + h) : (uint16_t)0;
   }
@@ -215,8 +222,10 @@ extern "C" int hybrid_split_merge(const mc_hybrid* hy, int32_t phase, hipStream_
   MC_REQUIRE(h->magic == kStageMagic && h->T == T && h->k == k && h->H == H,
              "hybrid_split_merge: MERGE without a matching SPLIT_SUBMIT on this stage");
   MC_REQUIRE(hy->y_acc && hy->y_host && hy->y_bf16, "hybrid_split_merge: NULL pointer (merge)");
+  MC_REQUIRE(hy->host_ids != nullptr, "hybrid_split_merge: NULL host_ids (merge)");
   hipLaunchKernelGGL(merge_kernel, dim3(grid_for((int64_t)T * H)), dim3(256), 0, s, hy->y_acc,
-                     hy->y_host, T, H, hy->n_tok, static_cast<uint16_t*>(hy->y_bf16), stage_dev, *h);
+                     hy->y_host, T, k, H, hy->n_tok, hy->host_ids, static_cast<uint16_t*>(hy->y_bf16),
+                     stage_dev, *h);
   MC_LAUNCH_CHECK();
   return MC_OK;
 }

@@ -445,7 +445,8 @@ enum { MC_SPLIT_SUBMIT = 0, MC_MERGE = 1 };
  * [wanger] "代码全链路"; [juhe] "为什么可以直接相加").
  * MC_SPLIT_SUBMIT: one kernel writes gpu_w and host_ids (complementary masks: every
  *   valid route is on exactly one side), writes x / host ids / w / the valid count /
- *   the layer into the stage and then raises the stage's request number.  The worker
+ *   the layer into the stage and then raises the stage's request number (a call with
+ *   no host route leaves the stage alone and its merge does not wait).  The worker
  *   pool's dispatcher thread (polling the stages it serves) computes the host partial
  *   into the stage and raises the completion number; meanwhile the GPU continues
  *   with fills and moe_experts_decode.  No host function and no copy is enqueued, so
