@@ -598,10 +598,39 @@ def c3_runs(args, torch, L, synth):
             dl.stage.close()
         del layers, cache, logits, xs
     workers.close()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_c3(cfg, full.L, views)
     del host, pool, views, host_t
     torch.cuda.synchronize()
     host_free()
     return out
+
+
+def cpu_baseline_c3(cfg, n_layers_model, views, n_layers=4):
+    """The oracle on one decode token through `n_layers` layers of the C3 pool (route, LRU
+    lookup, unsplit per-token expert sum in float64); per-token time scaled to the model."""
+    from oracle import LruOracle, decode_layer, route
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    tr = synth.trace(cfg, steps=1)
+    lg = synth.step_logits(cfg, tr[0], 0)
+    o = LruOracle(cfg.L, cfg.E, cfg.S)
+    log("cpu baseline: decode oracle, 1 token x %d layers of the C3 pool" % n_layers)
+    t0 = time.perf_counter()
+    for l in range(n_layers):
+        ids, w = route(lg[l], cfg.k, cfg.renorm)
+        o.lookup(l, ids, 1 << 16)
+        decode_layer(synth.activations(cfg, 0, l), ids, w, views, l, cfg.E, cfg.fmt, cfg.H, cfg.I)
+    dt = time.perf_counter() - t0
+    per_token = dt / n_layers * n_layers_model
+    return {"value": round(1.0 / per_token, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": "1 decode token through %d layers (route, LRU lookup, unsplit float64 expert sum); "
+                      "per-token time scaled to %d layers" % (n_layers, n_layers_model),
+            "seconds": round(dt, 2)}
 
 
 def alloc_pinned_exact(n, H, I, fmt, torch):
@@ -748,7 +777,33 @@ def bench_prefill(args, torch, L, synth):
                 "pipelined_tok_s": round(T / t_pipe * 1e3, 1), "layer_pool_bytes": int(layer_bytes),
                 "link_gbs": round(link_gbs, 2), "overlap_speedup": round(t_serial / t_pipe, 3),
                 "overlap_ideal": round(ideal, 3)})
+    if not args.no_cpu_baseline:
+        pre["cpu_baseline"] = cpu_baseline_prefill(cfg, host_t)
     return pre, roof
+
+
+def cpu_baseline_prefill(cfg, host_t, n_experts=8):
+    """The oracle's grouped prefill (route, stable sort, per-expert float64 FFN, scatter-add)
+    on `n_experts` of the 256 experts of layer 0; tok/s scaled to the whole layer."""
+    from oracle import prefill_grouped, route
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    banks = {k: v[:cfg.E].numpy() for k, v in host_t.items()}
+    x = synth.activations(cfg, 0)
+    log("cpu baseline: prefill oracle on %d of %d experts (layer 0)" % (n_experts, cfg.E))
+    t0 = time.perf_counter()
+    ids, w = route(synth.uniform_logits(cfg, layer=0), cfg.k, 1)
+    prefill_grouped(x, ids, w, banks, cfg.E, cfg.fmt, cfg.H, cfg.I, experts=range(n_experts))
+    dt = time.perf_counter() - t0
+    layer_s = dt * cfg.E / n_experts
+    return {"value": round(cfg.T / layer_s, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of the %d experts of one 8192-token layer (their routed tokens), grouped per-expert "
+                      "float64 FFN; tok/s scaled to the whole layer" % (n_experts, cfg.E),
+            "seconds": round(dt, 2)}
 
 
 def cpu_baseline(cfg, tr, logits, xs, host_np, sh_np, n_tokens):
