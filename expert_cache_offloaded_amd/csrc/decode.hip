@@ -182,22 +182,33 @@ __global__ void __launch_bounds__(kThreads)
 gate_up_kernel(DecodeArgs a) {
   // column u < T*k: route u's slot, when no earlier route of the call holds it (the
   // first route of a unit); column T*k: the shared expert
+  // The unit's slot, the slots of its window of 64 routes and the valid count are read
+  // in one round trip (every route index below T*k is readable, valid or not), so the
+  // weight loads wait behind a single dependent read.
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_all = a.T * a.k;
+  const bool shared_unit = a.has_shared && u == n_all;
+  const int wbase = u & ~63;
+  int slot_raw = -1, win_slot = -1;
+  if (!shared_unit) {
+    slot_raw = a.slots[u];
+    if (wbase + lane < n_all) win_slot = a.slots[wbase + lane];
+  }
   const int nt = valid_tokens(a);
   const int nr = nt * a.k;
-  const int u = blockIdx.x;
-  const bool shared_unit = a.has_shared && u == a.T * a.k;
   int slot = -1;
   if (shared_unit) {
     if (nt == 0) return;
   } else {
     if (u >= nr) return;
-    slot = pool_slot(a, u);
+    slot = (slot_raw >= 0 && slot_raw < a.n_pool) ? slot_raw : -1;
     if (slot < 0) return;
-    for (int base = 0; base < u; base += 64)
+    if (__ballot(wbase + lane < u && win_slot == slot)) return;
+    for (int base = 0; base < wbase; base += 64)
       if (routes_with_slot(a, base, u, slot)) return;
   }
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
   const int i0 = blockIdx.y * (4 * WR) + wave * WR;   // first intermediate row
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;             // elements per 16-B chunk
@@ -250,8 +261,9 @@ gate_up_kernel(DecodeArgs a) {
 
   // the unit's routes in route order: a mask per 64 routes, the next one fetched when
   // this one runs out (the shared expert takes every valid token in turn)
-  int base = u & ~63, t_next = 0;
-  uint64_t unit_routes = shared_unit ? 0 : routes_with_slot(a, base, nr, slot) & (~0ull << (u & 63));
+  int base = wbase, t_next = 0;
+  uint64_t unit_routes =
+      shared_unit ? 0 : __ballot(wbase + lane >= u && wbase + lane < nr && win_slot == slot);
   while (true) {
     int t, route;
     if (shared_unit) {
@@ -332,33 +344,17 @@ __global__ void __launch_bounds__(kThreads)
 down_kernel(DecodeArgs a) {
   extern __shared__ float s_h[];                 // [k + 1][I]: one token's route vectors (swizzled)
   __shared__ float s_part[4][ROWS];
-  __shared__ int32_t s_rslot[kMaxRoutes];        // slot of each route of the token (-1 = none)
-  __shared__ float s_rgate[kMaxRoutes];
-  __shared__ int32_t s_rsrc[kMaxRoutes];         // fill-through host source, -1 = slot
-  const int nt = valid_tokens(a);
   const int t = blockIdx.y;
   const int H = a.H, I = a.I, k = a.k;
   const int r0 = blockIdx.x * ROWS;
-  if (t >= nt) {                                 // a token beyond the valid count: its rows
-    if (threadIdx.x < ROWS && r0 + (int)threadIdx.x < H) {
-      const size_t o = (size_t)t * H + r0 + threadIdx.x;
-      if (!a.accumulate) a.y[o] = 0.0f;
-      if (a.y_bf16) a.y_bf16[o] = 0;
-    }
-    return;
-  }
-  float y_old = 0.0f;                            // the value accumulated into, read early
+  // The valid count, the accumulated y and the token's h vectors are read before the
+  // first wait; the wave's slots and gates and then its weight rows follow once the token
+  // is known to be valid (with no count given, at once), so the rows wait behind one
+  // dependent read.
+  const int n_raw = a.n_tok ? *a.n_tok : a.T;
+  float y_old = 0.0f;                            // the value accumulated into
   if (a.accumulate && threadIdx.x < ROWS && r0 + (int)threadIdx.x < H)
     y_old = a.y[(size_t)t * H + r0 + threadIdx.x];
-  for (int v = threadIdx.x; v < k; v += kThreads) {
-    const int r = t * k + v;
-    const int sl = pool_slot(a, r);
-    s_rslot[v] = sl;
-    s_rgate[v] = a.w[r];
-    const int src = (a.f_dn && sl >= 0) ? a.rsrc[r] : -1;
-    s_rsrc[v] = (src >= 0 && src < a.n_host) ? src : -1;
-  }
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;
   constexpr int E4 = ELEMS / 4;                              // float4 of h per chunk
@@ -394,6 +390,19 @@ down_kernel(DecodeArgs a) {
   uint8_t* wbs[kB_RoutesPerWave];
   // the wave's routes v0, v0+4, v0+8: gates and all row loads
   auto load_group = [&](int v0) {
+    // the routes' slots, gates and host sources first, all in flight together (route
+    // index clamped into the token's routes), then the rows that depend on them
+    int s_raw[kB_RoutesPerWave], src_raw[kB_RoutesPerWave];
+    float g_raw[kB_RoutesPerWave];
+    if (k > 0) {
+#pragma unroll
+      for (int j = 0; j < kB_RoutesPerWave; ++j) {
+        const int r = t * k + min(v0 + 4 * j, k - 1);
+        s_raw[j] = a.slots[r];
+        g_raw[j] = a.w[r];
+        src_raw[j] = a.f_dn ? a.rsrc[r] : -1;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kB_RoutesPerWave; ++j) {
       const int v = v0 + 4 * j;
@@ -403,12 +412,12 @@ down_kernel(DecodeArgs a) {
       wb[j] = nullptr;
       wbs[j] = nullptr;
       if (v < k) {
-        const int s = s_rslot[v];
+        const int s = (s_raw[j] >= 0 && s_raw[j] < a.n_pool) ? s_raw[j] : -1;
         if (s >= 0) {
           dn = a.dn + (size_t)s * per;
           if (FMT == MC_MXFP4) dns = a.dns + (size_t)s * per_s;
-          gate[j] = s_rgate[v];
-          const int src = s_rsrc[v];
+          gate[j] = g_raw[j];
+          const int src = src_raw[j] < a.n_host ? src_raw[j] : -1;
           if (src >= 0) {
             wb[j] = const_cast<uint8_t*>(dn);
             wbs[j] = const_cast<uint8_t*>(dns);
@@ -446,6 +455,16 @@ down_kernel(DecodeArgs a) {
       const float* src = v < k ? a.h_route + ((size_t)t * k + v) * I : a.h_shared + (size_t)t * I;
       __builtin_amdgcn_global_load_lds(src + e, (__attribute__((address_space(3))) void*)(s_h + ch * 256),
                                        16, 0, 0);
+    }
+    const int nt = min(max(n_raw, 0), a.T);
+    if (t >= nt) {                                     // a token beyond the valid count: its rows
+      __builtin_amdgcn_s_waitcnt(0);
+      if (threadIdx.x < ROWS && r0 + (int)threadIdx.x < H) {
+        const size_t o = (size_t)t * H + r0 + threadIdx.x;
+        if (!a.accumulate) a.y[o] = 0.0f;
+        if (a.y_bf16) a.y_bf16[o] = 0;
+      }
+      return;
     }
     if (n_groups > 0) load_group(wave);
     __builtin_amdgcn_s_waitcnt(0);                     // the LDS copies have landed
