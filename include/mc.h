@@ -208,7 +208,7 @@ int mc_cache_install(const mc_cache* c, const int32_t* flat, int32_t n, hipStrea
  *   pool  device slot banks (pool->n = S)
  *   fill_flat, fill_slot, n_fill: as written by slot_cache_lookup_evict (device)
  * Entries with a flat id outside [0, host->n) or a slot outside [0, pool->n) are
- * skipped.  kcap = capacity of the lists.
+ * skipped.  kcap = capacity of the lists, 0..65535 (MC_EINVAL otherwise).
  */
 int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
                   const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap, hipStream_t s);

@@ -85,6 +85,15 @@ def test_validation_errors_do_not_need_a_gpu():
     assert "multiples of 64" in L.last_error()
     b.H = 64
     assert lib.moe_experts_decode(ids, ids, w, 1, 2, None, C.byref(b), None, ids, 0, w, 0, None, None, None) == L.MC_EINVAL
+    # fill lists longer than the fill grid's entry dimension
+    big = (C.c_uint8 * 64)()
+    addr = (C.addressof(big) + 15) // 16 * 16
+    fb = L.Banks()
+    fb.fmt, fb.H, fb.I, fb.n = L.MC_MXFP4, 64, 64, 4
+    fb.gate_up = fb.gate_up_scale = fb.down = fb.down_scale = addr
+    assert lib.mc_fill_slots(C.byref(fb), C.byref(fb), ids, ids, ids, 65536, None) == L.MC_EINVAL
+    assert "kcap" in L.last_error()
+    assert lib.mc_fill_slots(C.byref(fb), C.byref(fb), ids, ids, ids, -1, None) == L.MC_EINVAL
     assert lib.mc_host_pool_create(0, None) is None
 
 
