@@ -93,6 +93,10 @@ __device__ __forceinline__ int route_count(const int32_t* n_tok, int T, int k) {
   return nt * k;
 }
 
+// Routes a wave reads per batch, in 64-route groups: every id load of a batch is issued
+// before the first compare, so a wave waits once per batch instead of once per group.
+constexpr int kSortBatch = 8;
+
 // 1. per-expert route counts, per wave quarter (ballot + popcount, no atomics)
 __global__ void __launch_bounds__(256)
 sort_count_kernel(const int32_t* __restrict__ ids, int T, int k, const int32_t* __restrict__ n_tok,
@@ -101,10 +105,15 @@ sort_count_kernel(const int32_t* __restrict__ ids, int T, int k, const int32_t* 
   const int nr = route_count(n_tok, T, k);
   const int q = (nr + 3) / 4, r0 = wave * q, r1 = min(nr, r0 + q);
   int c = 0;
-  for (int base = r0; base < r1; base += 64) {
-    const int r = base + lane;
-    const bool hit = r < r1 && ids[r] == e;
-    c += __popcll(__ballot(hit));
+  for (int base = r0; base < r1; base += 64 * kSortBatch) {
+    int v[kSortBatch];                       // a batch of ids in flight before the first compare
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {
+      const int r = base + 64 * u + lane;
+      v[u] = r < r1 ? ids[r] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) c += __popcll(__ballot(v[u] == e));
   }
   __shared__ int s_c[4];
   if (lane == 0) {
@@ -154,12 +163,20 @@ sort_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, const int32_t
   const int q = (nr + 3) / 4, r0 = wave * q, r1 = min(nr, r0 + q);
   int pos = offsets[e];
   for (int w = 0; w < wave; ++w) pos += counts4[e * 4 + w];
-  for (int base = r0; base < r1; base += 64) {
-    const int r = base + lane;
-    const bool hit = r < r1 && ids[r] == e;
-    const uint64_t m = __ballot(hit);
-    if (hit) perm[pos + __popcll(m & ((1ull << lane) - 1ull))] = r;
-    pos += __popcll(m);
+  for (int base = r0; base < r1; base += 64 * kSortBatch) {
+    int v[kSortBatch];
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {
+      const int r = base + 64 * u + lane;
+      v[u] = r < r1 ? ids[r] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {              // groups in route order: stable
+      const bool hit = v[u] == e;
+      const uint64_t m = __ballot(hit);
+      if (hit) perm[pos + __popcll(m & ((1ull << lane) - 1ull))] = base + 64 * u + lane;
+      pos += __popcll(m);
+    }
   }
 }
 
@@ -476,6 +493,7 @@ prefill_gemm_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------- combine
 
 // y[t][c] = bf16_rne(sum over valid routes j of Yr[t*k + j][c]), j ascending
+constexpr int kCombineMaxK = 8;     // up to this k, a thread's k row reads are in flight together
 __global__ void __launch_bounds__(256)
 prefill_combine_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int H,
                        const int32_t* __restrict__ n_tok, const float* __restrict__ yr,
@@ -486,7 +504,25 @@ prefill_combine_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int
        i += (int64_t)gridDim.x * blockDim.x) {
     const int t = (int)(i * 4 / H), c = (int)(i * 4 % H);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < nt) {
+    if (t < nt && k <= kCombineMaxK) {
+      // every route row of the token is read at once (rows of invalid routes too: they
+      // lie inside yr and are then skipped), then summed in route order
+      int idv[kCombineMaxK];
+      float4 v[kCombineMaxK];
+#pragma unroll
+      for (int j = 0; j < kCombineMaxK; ++j) idv[j] = j < k ? ids[t * k + j] : -1;
+#pragma unroll
+      for (int j = 0; j < kCombineMaxK; ++j)        // j >= k re-reads row 0 (no branch)
+        v[j] = *reinterpret_cast<const float4*>(yr + ((size_t)t * k + (j < k ? j : 0)) * H + c);
+#pragma unroll
+      for (int j = 0; j < kCombineMaxK; ++j) {
+        if (idv[j] < 0 || idv[j] >= E) continue;
+        s.x += v[j].x;
+        s.y += v[j].y;
+        s.z += v[j].z;
+        s.w += v[j].w;
+      }
+    } else if (t < nt) {
       for (int j = 0; j < k; ++j) {
         const int id = ids[t * k + j];
         if (id < 0 || id >= E) continue;
