@@ -12,6 +12,9 @@
 // mc_host_experts on the worker pool, i.e. exactly the two paths a hybrid decode layer
 // runs.  The overlapped run sizes both sides from their stand-alone rates so that they
 // take about the same time.
+#include <math.h>
+
+#include <algorithm>
 #include <chrono>
 #include <thread>
 #include <vector>
@@ -62,36 +65,54 @@ extern "C" int mc_bandwidth_profile(const mc_banks* host, const mc_banks* pool, 
   MC_REQUIRE(seconds > 0.0 && seconds <= 60.0, "mc_bandwidth_profile: seconds=%g not in (0, 60]", seconds);
   MC_REQUIRE(threshold > 0.0, "mc_bandwidth_profile: threshold=%g must be > 0", threshold);
   const int n = n_experts, H = host->H;
-  const double bytes = (double)bank_bytes(host->fmt, H, host->I).total() * n;
+  const double expert_bytes = (double)bank_bytes(host->fmt, H, host->I).total();
+  const double bytes = expert_bytes * n;
+  // Each call reads n experts of a window of W host entries and the next call the n
+  // after them, so both paths stream from host DRAM as in a decode step: a few experts
+  // read over and over would stay in the CPU's last-level cache and overstate the host
+  // kernel.  W covers at least 1 GiB (or the whole host pool).
+  int64_t W = (int64_t)ceil(1073741824.0 / expert_bytes);
+  W = std::min<int64_t>(std::max<int64_t>(W, n), host->n);
 
-  // device fill list: entries 0..n-1 -> slots 0..n-1
+  // device lists: flat ids [W + n] (entry j = j mod W, so any window of n is contiguous),
+  // slots [n] = 0..n-1, count [1] = n
   DevLists dl;
-  MC_HIP(hipMalloc((void**)&dl.p, sizeof(int32_t) * (2 * (size_t)n + 1)));
+  const size_t n_list = (size_t)W + 2 * (size_t)n + 1;
+  MC_HIP(hipMalloc((void**)&dl.p, sizeof(int32_t) * n_list));
+  int32_t* d_flat = dl.p;
+  int32_t* d_slot = dl.p + W + n;
+  int32_t* d_count = d_slot + n;
   {
-    std::vector<int32_t> h(2 * (size_t)n + 1);
-    for (int i = 0; i < n; ++i) h[i] = h[n + i] = i;
-    h[2 * n] = n;
+    std::vector<int32_t> h(n_list);
+    for (int64_t j = 0; j < W + n; ++j) h[j] = (int32_t)(j % W);
+    for (int i = 0; i < n; ++i) h[W + n + i] = i;
+    h[W + 2 * n] = n;
     MC_HIP(hipMemcpy(dl.p, h.data(), h.size() * sizeof(int32_t), hipMemcpyHostToDevice));
   }
-  // host branch inputs: one token routed to the n experts of "layer 0"
+  // host branch inputs: one token routed to n experts of the window ("layer 0" spans
+  // the whole host pool, so an id is a flat id)
   std::vector<uint16_t> x(H, 0x3F80);            // bf16 1.0
   std::vector<int32_t> ids(n);
   std::vector<float> w(n, 1.0f / n), y(H, 0.0f);
-  for (int i = 0; i < n; ++i) ids[i] = i;
+  int64_t fill_calls = 0, cpu_calls = 0;
 
   Events ev;
   MC_HIP(hipEventCreate(&ev.a));
   MC_HIP(hipEventCreate(&ev.b));
   auto fills = [&](int reps) -> int {
     for (int r = 0; r < reps; ++r) {
-      int e = mc_fill_slots(host, pool, dl.p, dl.p + n, dl.p + 2 * n, n, s);
+      const int64_t off = (fill_calls++ * n) % W;
+      int e = mc_fill_slots(host, pool, d_flat + off, d_slot, d_count, n, s);
       if (e != MC_OK) return e;
     }
     return MC_OK;
   };
   auto cpu = [&](int reps) -> int {
     for (int r = 0; r < reps; ++r) {
-      int e = mc_host_experts(workers, x.data(), ids.data(), w.data(), 1, n, 0, n, host, y.data());
+      const int64_t off = (cpu_calls++ * n) % W;
+      for (int i = 0; i < n; ++i) ids[i] = (int32_t)((off + i) % W);
+      int e = mc_host_experts(workers, x.data(), ids.data(), w.data(), 1, n, 0, (int32_t)host->n, host,
+                              y.data());
       if (e != MC_OK) return e;
     }
     return MC_OK;
@@ -152,6 +173,6 @@ extern "C" int mc_bandwidth_profile(const mc_banks* host, const mc_banks* pool, 
   out->cpu_ov_gbs = bytes * rcpu / t_cpu_ov * 1e-9;
   out->frac_q16 = mc_fetch_fraction_q16(out->pcie_gbs, out->cpu_gbs, out->pcie_ov_gbs, out->cpu_ov_gbs);
   out->hybrid = mc_recommend_backend(out->cpu_gbs, out->pcie_gbs, threshold);
-  out->expert_bytes = bytes / n;
+  out->expert_bytes = expert_bytes;
   return MC_OK;
 }

@@ -50,6 +50,29 @@ static std::vector<StageEntry> g_stages;
 
 // ------------------------------------------------------------------ worker pool
 
+// Hand-offs between the calling thread and the workers spin before they block: a
+// layer's host branch runs two parallel passes a few hundred microseconds apart, and a
+// condition-variable wake-up costs tens of microseconds per thread.  The spin first
+// pauses, then yields the core (other runnable threads, such as the one launching GPU
+// work, still get it), and blocks after kSpinUs.
+constexpr int kSpinUs = 200;
+
+template <class Pred>
+static bool spin_until(Pred done) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0;; ++i) {
+    if (done()) return true;
+    if (i < 256) {
+      _mm_pause();
+    } else {
+      if ((i & 15) == 0 &&
+          std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(kSpinUs))
+        return false;
+      sched_yield();
+    }
+  }
+}
+
 struct mc_host_pool {
   std::vector<std::thread> threads;
   std::mutex mu, pf_mu;
@@ -58,9 +81,10 @@ struct mc_host_pool {
   const std::function<void(int)>* fn = nullptr;
   std::atomic<int> next{0};
   int n_tasks = 0;
-  int generation = 0;
-  int acked = 0;
+  std::atomic<int> generation{0};
+  std::atomic<int> acked{0};
   bool stop = false;
+  std::atomic<bool> stop_flag{false};
   // dispatcher of the hybrid stages (the host branch)
   std::thread driver;
   std::atomic<bool> driver_stop{false};
@@ -68,20 +92,24 @@ struct mc_host_pool {
   void worker_loop() {
     int seen = 0;
     for (;;) {
+      spin_until([&] {
+        return stop_flag.load(std::memory_order_acquire) ||
+               generation.load(std::memory_order_acquire) != seen;
+      });
       const std::function<void(int)>* f;
       int n;
       {
         std::unique_lock<std::mutex> lk(mu);
-        cv_work.wait(lk, [&] { return stop || generation != seen; });
+        cv_work.wait(lk, [&] { return stop || generation.load() != seen; });
         if (stop) return;
-        seen = generation;
+        seen = generation.load();
         f = fn;
         n = n_tasks;
       }
       for (int i; (i = next.fetch_add(1)) < n;) (*f)(i);
-      {
+      if (acked.fetch_add(1, std::memory_order_acq_rel) + 1 == (int)threads.size()) {
         std::lock_guard<std::mutex> lk(mu);
-        if (++acked == (int)threads.size()) cv_done.notify_all();
+        cv_done.notify_all();
       }
     }
   }
@@ -100,13 +128,17 @@ struct mc_host_pool {
       fn = &f;
       n_tasks = n;
       next.store(0);
-      acked = 0;
-      ++generation;
+      acked.store(0);
+      generation.fetch_add(1, std::memory_order_acq_rel);
     }
     cv_work.notify_all();
     for (int i; (i = next.fetch_add(1)) < n;) f(i);
-    std::unique_lock<std::mutex> lk(mu);
-    cv_done.wait(lk, [&] { return acked == (int)threads.size(); });
+    const int nw = (int)threads.size();
+    if (!spin_until([&] { return acked.load(std::memory_order_acquire) == nw; })) {
+      std::unique_lock<std::mutex> lk(mu);
+      cv_done.wait(lk, [&] { return acked.load() == nw; });
+    }
+    std::lock_guard<std::mutex> lk(mu);
     fn = nullptr;
   }
 
@@ -197,6 +229,7 @@ extern "C" void mc_host_pool_destroy(mc_host_pool* p) {
   {
     std::lock_guard<std::mutex> lk(p->mu);
     p->stop = true;
+    p->stop_flag.store(true, std::memory_order_release);
   }
   p->cv_work.notify_all();
   for (auto& t : p->threads) t.join();
@@ -233,7 +266,14 @@ static bool init_table() {
 }
 static bool g_table_ok = init_table();
 
-static inline float e8m0(uint8_t X) { return ldexpf(1.0f, (int)X - 127); }
+// e8m0 scale byte -> 2^(X - 127), from a table built once (X = 255 never occurs)
+static float g_e8m0[256];
+static bool init_e8m0() {
+  for (int X = 0; X < 256; ++X) g_e8m0[X] = ldexpf(1.0f, X - 127);
+  return true;
+}
+static bool g_e8m0_ok = init_e8m0();
+static inline float e8m0(uint8_t X) { return g_e8m0[X]; }
 static inline float bf16f(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;

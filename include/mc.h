@@ -375,9 +375,12 @@ int mc_host_experts(mc_host_pool* pool, const void* x_bf16, const int32_t* ids, 
 /*
  * Start-up bandwidth profile ([wanger] "第一层带宽比：选后端" and "实测版本：overlap 带宽取代
  * 假设").  Measures the two paths a hybrid decode layer runs, on this machine:
- *   pcie_gbs     the fill kernel (mc_fill_slots) copying host entries [0, n) into pool
- *                slots [0, n), alone (bytes of the n experts per second)
- *   cpu_gbs      mc_host_experts for one token routed to those n experts, alone
+ *   pcie_gbs     the fill kernel (mc_fill_slots) copying n host entries into pool slots
+ *                [0, n) per call, alone (bytes of the n experts per second)
+ *   cpu_gbs      mc_host_experts for one token routed to n host entries per call, alone
+ * Successive calls of both paths take the next n entries of a window of
+ * W = min(host->n, max(n, ceil(1 GiB / expert bytes))) entries, so they read host DRAM
+ * as a decode step does rather than the CPU's last-level cache.
  *   pcie_ov_gbs, cpu_ov_gbs  the same two while both run at once, each sized from its
  *                stand-alone rate to take about seconds/2
  *   frac_q16     mc_fetch_fraction_q16(pcie_gbs, cpu_gbs, pcie_ov_gbs, cpu_ov_gbs)
