@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 def test_bandwidth_profile_qwen_shaped():
     from expert_cache_offloaded_amd import HostPool, bandwidth_profile
     from expert_cache_offloaded_amd import _lib as L
-    cfg = synth.CONFIGS["qwen_decode"].with_(L=1, E=6)
+    cfg = synth.CONFIGS["qwen_decode"].with_(L=1, E=24)
     host_np = synth.host_pool(cfg)
     host_t = pinned_banks(cfg, host_np)
     pool_t = empty_device_banks(cfg, 8)
@@ -30,11 +30,14 @@ def test_bandwidth_profile_qwen_shaped():
     ref = fetch_fraction_q16(prof["pcie_gbs"], prof["cpu_gbs"], prof["pcie_ov_gbs"], prof["cpu_ov_gbs"])
     assert abs(int(prof["frac_q16"]) - ref) <= 1
     assert prof["backend"] == recommend_backend(prof["cpu_gbs"], prof["pcie_gbs"], 2.0)
-    # the fills it ran left the host entries in slots 0..5
-    for name, arr in pool_t.items():
-        got = arr.cpu()
+    # each call moves on to the next 6 of the 24 host entries (the window is the whole
+    # pool here): the last call left entries off .. off+5 in slots 0..5, one off for all
+    got = {name: arr.cpu() for name, arr in pool_t.items()}
+    offs = [o for o in range(0, 24, 6) if torch.equal(got["gate_up"][0], t_of(host_np["gate_up"][o]))]
+    assert len(offs) == 1, offs
+    for name in got:
         for i in range(6):
-            assert torch.equal(got[i], t_of(host_np[name][i])), (name, i)
+            assert torch.equal(got[name][i], t_of(host_np[name][offs[0] + i])), (name, i)
 
 
 def test_bandwidth_profile_rejects_bad_arguments():
