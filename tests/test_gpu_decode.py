@@ -87,19 +87,23 @@ def _run_decode(cfg, case, nt=None):
 
 
 CASES = [
-    # name, config, T, slots, host fraction, shared
-    ("tiny-bf16", "tiny", 4, 8, 0.25, False),
-    ("qwen-mxfp4-bs1", "qwen_decode", 1, 24, 0.0, True),
-    ("qwen-mxfp4-bs1-split", "qwen_decode", 1, 24, 0.4, True),
-    ("zipf-mxfp4-bs4", "zipf_decode", 4, 40, 0.1, False),
-    ("zipf-mxfp4-bs16", "zipf_decode", 16, 130, 0.1, False),
-    ("dsv4-mxfp4-bs1", "dsv4_hybrid", 1, 8, 0.3, False),
+    # name, config, T, slots, host fraction, shared, shape overrides
+    ("tiny-bf16", "tiny", 4, 8, 0.25, False, {}),
+    ("qwen-mxfp4-bs1", "qwen_decode", 1, 24, 0.0, True, {}),
+    ("qwen-mxfp4-bs1-split", "qwen_decode", 1, 24, 0.4, True, {}),
+    ("zipf-mxfp4-bs4", "zipf_decode", 4, 40, 0.1, False, {}),
+    ("zipf-mxfp4-bs16", "zipf_decode", 16, 130, 0.1, False, {}),
+    ("dsv4-mxfp4-bs1", "dsv4_hybrid", 1, 8, 0.3, False, {}),
+    # bf16 weights past the tiny shape: two 16-B chunks per lane in gate_up and down rows
+    # of 128 chunks (64 lanes x 2), then four chunks per lane in gate_up
+    ("bf16-h1024-i1024-bs3", "tiny", 3, 20, 0.2, True, dict(E=16, k=4, H=1024, I=1024)),
+    ("bf16-h2048-i512-bs1", "tiny", 1, 12, 0.0, False, dict(E=12, k=3, H=2048, I=512)),
 ]
 
 
-@pytest.mark.parametrize("name,cname,T,n_slots,hf,shared", CASES)
-def test_decode_matches_oracle(name, cname, T, n_slots, hf, shared):
-    cfg = synth.CONFIGS[cname].with_(L=2)
+@pytest.mark.parametrize("name,cname,T,n_slots,hf,shared,shape", CASES)
+def test_decode_matches_oracle(name, cname, T, n_slots, hf, shared, shape):
+    cfg = synth.CONFIGS[cname].with_(L=2, **shape)
     case = _resident_case(cfg, T, n_slots, hf, seed=zlib.crc32(name.encode()) % 1000, shared=shared)
     y, yb = _run_decode(cfg, case)
     assert rel_l2(y, case["ref"]) <= 1e-4, name              # fp32 partial (diagnostic bar)
