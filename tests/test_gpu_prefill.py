@@ -56,7 +56,9 @@ def _run_prefill(cfg, x_bits, ids, w, banks_dev, E, n_tok=None):
 
 
 @pytest.mark.parametrize("T,E,k,H,I,n_tok", [(200, 8, 2, 256, 128, None), (333, 16, 6, 512, 256, None),
-                                             (97, 8, 3, 256, 256, 41), (1, 4, 2, 256, 128, None)])
+                                             (97, 8, 3, 256, 256, 41), (1, 4, 2, 256, 128, None),
+                                             # k at and past the combine's batched-read limit (8)
+                                             (150, 16, 8, 256, 128, None), (90, 16, 10, 256, 128, 70)])
 def test_prefill_small_layers(T, E, k, H, I, n_tok):
     cfg = synth.CONFIGS["prefill"].with_(L=1, E=E, k=k, H=H, I=I, T=T)
     banks = _layer(cfg, E)
