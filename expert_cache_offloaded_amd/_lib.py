@@ -82,6 +82,7 @@ _SIGS = {
                                    _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "mc_fill_slots": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, _P]),
     "mc_cache_install": (C.c_int, [C.POINTER(Cache), _P, _I32, _P]),
+    "mc_host_forget": (C.c_int, [_P, C.c_size_t]),
     "mc_fill_slots_banks": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, C.c_uint32, _P]),
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
@@ -210,6 +211,15 @@ def moe_route_lookup(logits, renorm: int, ids, w, cache: Cache, layer: int, n_to
         _ptr(logits), renorm, _ptr(ids), _ptr(w), C.byref(cache), layer, T, k, _ptr(n_tok), frac_q16,
         fixed_cap, min_fill, _ptr(slots), _ptr(fill_flat), _ptr(fill_slot), _ptr(n_fill),
         _ptr(host_flat), _ptr(n_host), fill_flat.numel(), _stream(stream)))
+
+
+def host_forget(ptr: int, nbytes: int = 0) -> int:
+    """Drop the library's remembered device translations of pinned host memory in
+    [ptr, ptr + nbytes) (mc_host_forget); returns how many were dropped."""
+    rc = lib().mc_host_forget(ptr, nbytes)
+    if rc < 0:
+        raise McError("mc_host_forget", rc, last_error())
+    return rc
 
 
 def cache_install(cache: Cache, flat, stream=None) -> None:

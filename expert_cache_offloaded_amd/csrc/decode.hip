@@ -682,10 +682,10 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
                "moe_experts_decode: fill host banks differ from the pool in format or shape");
     MC_REQUIRE(fill->kcap >= 0 && fill->fill_flat && fill->fill_slot && fill->n_fill,
                "moe_experts_decode: bad fill list");
-    if ((rc = host_device_view(fill->host->gate_up, &a.f_gu, "moe_experts_decode: fill host bank")) ||
-        (rc = host_device_view(fill->host->gate_up_scale, &a.f_gus, "moe_experts_decode: fill host bank")) ||
-        (rc = host_device_view(fill->host->down, &a.f_dn, "moe_experts_decode: fill host bank")) ||
-        (rc = host_device_view(fill->host->down_scale, &a.f_dns, "moe_experts_decode: fill host bank")))
+    if ((rc = host_device_view(fill->host->gate_up, &a.f_gu, "moe_experts_decode: fill host bank", s)) ||
+        (rc = host_device_view(fill->host->gate_up_scale, &a.f_gus, "moe_experts_decode: fill host bank", s)) ||
+        (rc = host_device_view(fill->host->down, &a.f_dn, "moe_experts_decode: fill host bank", s)) ||
+        (rc = host_device_view(fill->host->down_scale, &a.f_dns, "moe_experts_decode: fill host bank", s)))
       return rc;
     a.n_host = fill->host->n;
     a.fill_flat = fill->fill_flat;

@@ -64,20 +64,31 @@ fill_kernel(FillSegs g, const int32_t* __restrict__ fill_flat, const int32_t* __
   }
 }
 
-// Device-visible address of pinned host memory.  Translations are remembered so a
-// call made while a stream is being captured needs no runtime query once the same
-// banks were used before.
+// Device-visible address of pinned host memory.  Outside stream capture every call
+// asks the runtime again (so memory that was freed and reused as pageable memory is
+// refused); while `s` is being captured the translation remembered from an earlier
+// call on the same address is used, so capture needs no runtime query once the banks
+// were seen.  mc_host_forget drops remembered translations.
 static std::mutex g_view_mu;
 static const void* g_view_host[64];
 static const uint8_t* g_view_dev[64];
 static int g_view_n = 0, g_view_next = 0;
 
-int host_device_view(const void* host, const uint8_t** out, const char* what) {
+static bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;                 // cannot tell: take the remembered translation, query no more
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
+int host_device_view(const void* host, const uint8_t** out, const char* what, hipStream_t s) {
   if (host == nullptr) {
     *out = nullptr;
     return MC_OK;
   }
-  {
+  if (stream_capturing(s)) {
     std::lock_guard<std::mutex> lk(g_view_mu);
     for (int i = 0; i < g_view_n; ++i)
       if (g_view_host[i] == host) {
@@ -89,16 +100,37 @@ int host_device_view(const void* host, const uint8_t** out, const char* what) {
   hipError_t e = hipHostGetDevicePointer(&d, const_cast<void*>(host), 0);
   if (e != hipSuccess || d == nullptr) {
     (void)hipGetLastError();
+    host_forget(host, 1);
     set_error("%s is not pinned host memory (%s)", what, hipGetErrorString(e));
     return MC_EINVAL;
   }
   *out = static_cast<const uint8_t*>(d);
   std::lock_guard<std::mutex> lk(g_view_mu);
+  for (int i = 0; i < g_view_n; ++i)
+    if (g_view_host[i] == host) {
+      g_view_dev[i] = *out;
+      return MC_OK;
+    }
   g_view_host[g_view_next] = host;
   g_view_dev[g_view_next] = *out;
   g_view_next = (g_view_next + 1) % 64;
   if (g_view_n < 64) ++g_view_n;
   return MC_OK;
+}
+
+int host_forget(const void* p, size_t bytes) {
+  const uintptr_t lo = (uintptr_t)p, hi = lo + (bytes ? bytes : 1);
+  int dropped = 0;
+  std::lock_guard<std::mutex> lk(g_view_mu);
+  for (int i = 0; i < g_view_n; ++i) {
+    const uintptr_t a = (uintptr_t)g_view_host[i];
+    if (a >= lo && a < hi) {
+      g_view_host[i] = nullptr;
+      g_view_dev[i] = nullptr;
+      ++dropped;
+    }
+  }
+  return dropped;
 }
 
 }  // namespace mc
@@ -136,7 +168,7 @@ extern "C" int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, c
     g.bytes[b] = (banks >> b) & 1u ? nbytes[b] : 0;    // banks left out get no chunks
     if (g.bytes[b] == 0) continue;
     MC_REQUIRE(nbytes[b] % 16 == 0, "mc_fill_slots: bank %d entry is not a multiple of 16 bytes", b);
-    if ((rc = host_device_view(hs[b], &g.src[b], "mc_fill_slots: host bank")) != MC_OK) return rc;
+    if ((rc = host_device_view(hs[b], &g.src[b], "mc_fill_slots: host bank", s)) != MC_OK) return rc;
     g.dst[b] = static_cast<uint8_t*>(ds[b]);
     chunks += (int)((nbytes[b] + kFillChunk - 1) / kFillChunk);
   }
@@ -147,4 +179,10 @@ extern "C" int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, c
                      fill_slot, n_fill);
   MC_LAUNCH_CHECK();
   return MC_OK;
+}
+
+extern "C" int mc_host_forget(const void* p, size_t bytes) {
+  clear_error();
+  MC_REQUIRE(p != nullptr, "mc_host_forget: NULL pointer");
+  return host_forget(p, bytes);
 }

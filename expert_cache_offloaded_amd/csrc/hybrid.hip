@@ -156,6 +156,7 @@ extern "C" int mc_hybrid_stage_free(void* stage) {
   if (!stage) return MC_OK;
   MC_HIP(hipDeviceSynchronize());            // no kernel may still read or write it
   host_pool_drop_stage(static_cast<StageHeader*>(stage));
+  host_forget(stage, 1);
   MC_HIP(hipHostFree(stage));
   return MC_OK;
 }
@@ -181,7 +182,7 @@ extern "C" int hybrid_split_merge(const mc_hybrid* hy, int32_t phase, hipStream_
   StageHeader* h = static_cast<StageHeader*>(hy->pinned_stage);
   uint8_t* base = static_cast<uint8_t*>(hy->pinned_stage);
   const uint8_t* dev_view = nullptr;
-  if ((rc = host_device_view(base, &dev_view, "hybrid_split_merge: stage")) != MC_OK) return rc;
+  if ((rc = host_device_view(base, &dev_view, "hybrid_split_merge: stage", s)) != MC_OK) return rc;
   uint8_t* stage_dev = const_cast<uint8_t*>(dev_view);
 
   if (phase == MC_SPLIT_SUBMIT) {

@@ -212,11 +212,11 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   } else if (frac_q16 == 0) {
     q = min(m, fixed_cap);
   } else {
-    const int64_t f = frac_q16;
-    const int64_t lo = ((int64_t)m * f) >> 16;
-    const int64_t c_lo = max(lo * (65536 - f), ((int64_t)m - lo) * f);
-    const int64_t c_hi = max((lo + 1) * (65536 - f), ((int64_t)m - lo - 1) * f);
-    q = (int)min((int64_t)m, c_lo <= c_hi ? lo : lo + 1);
+    // The slower branch, max(F (1 - f), (m - F) f), falls while the host share
+    // dominates (F < m f) and rises after; of the two integers around m f the upper
+    // one wins exactly when f (m + 1) > floor(m f) + 1, so the minimiser (ties to the
+    // smaller F) is ceil(f (m + 1)) - 1, which is at most m.  In Q16 integers:
+    q = (int)(((int64_t)frac_q16 * (m + 1) - 1) >> 16);
   }
   if (min_fill && m >= 1) q = max(q, 1);
   q = min(q, S - n_hits);

@@ -65,9 +65,12 @@ inline BankBytes bank_bytes(int fmt, int H, int I) {
 int check_banks(const mc_banks* b, const char* what, bool need_nonempty = true);
 
 // Device-visible address of pinned host memory (NULL maps to NULL); MC_EINVAL with a
-// message if `host` is not pinned.  Translations are cached, so a call made during
-// stream capture needs no runtime query once the same allocation was seen.
-int host_device_view(const void* host, const uint8_t** out, const char* what);
+// message if `host` is not pinned.  Checked with the runtime on every call made
+// outside stream capture; during capture of `s` a translation remembered from an
+// earlier call on the same address is used.
+int host_device_view(const void* host, const uint8_t** out, const char* what, hipStream_t s);
+// Drops remembered translations of host addresses in [p, p + bytes); returns how many.
+int host_forget(const void* p, size_t bytes);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -11,9 +11,11 @@
  *
  * Conventions for every call
  *   - Ownership: the caller allocates and frees every buffer (device memory,
- *     pinned host memory).  The library never frees caller memory and never
- *     allocates device memory inside a call.  The only library-owned object is
- *     mc_host_pool (CPU worker threads).
+ *     pinned host memory).  The library never frees caller memory.  No hot-path
+ *     call allocates device memory; the exceptions are the set-up calls that say
+ *     so (mc_bandwidth_profile: a small fill list of its own, freed before it
+ *     returns; mc_hybrid_stage_alloc: pinned host staging).  The only
+ *     library-owned long-lived object is mc_host_pool (CPU worker threads).
  *   - Asynchrony: calls enqueue work on the given HIP stream and return; results
  *     are visible to the host after the stream is synchronised.  Counts written
  *     by the device (n_fill, n_host, ...) are device int32s.
@@ -148,10 +150,11 @@ int moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t reno
  *      stats[ERR] and are ignored).
  *   2. hits: resident members of U, stamped with the clock.  Misses M (ascending),
  *      m = |M|.
- *   3. q: frac_q16 = 0 -> min(m, fixed_cap); otherwise lo = (m*frac_q16) >> 16 and
- *      q = lo or lo+1, whichever has the smaller max(F*(65536-frac_q16),
- *      (m-F)*frac_q16) (ties to lo), then min(q, m); min_fill != 0 and m >= 1
- *      -> q >= 1.  Then q is capped by the slots not hit in this call and by kcap.
+ *   3. q: frac_q16 = 0 -> min(m, fixed_cap); otherwise, with f = frac_q16 / 65536,
+ *      q is the integer F next to m*f that makes the slower of the two miss branches,
+ *      max(F*(1-f), (m-F)*f), smallest, ties to the smaller F ([wanger] "3."); it
+ *      equals ceil(f*(m+1)) - 1 <= m.  min_fill != 0 and m >= 1 -> q >= 1.  Then q is
+ *      capped by the slots not hit in this call and by kcap.
  *   4. victims: the q slots not hit in this call with the smallest (stamp, slot).
  *      The first q misses are paired in order with the victims: the old
  *      occupant (if any) is evicted, the miss is installed and stamped.
@@ -212,6 +215,17 @@ int mc_cache_install(const mc_cache* c, const int32_t* flat, int32_t n, hipStrea
  */
 int mc_fill_slots(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
                   const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap, hipStream_t s);
+
+/*
+ * Forget the device translations the library remembers for pinned host memory in
+ * [p, p + bytes) (bytes = 0: the one address p); returns how many were dropped.
+ * Calls made outside stream capture always check their host banks with the runtime;
+ * a call made while its stream is being captured uses the translation remembered
+ * from an earlier call on the same address.  A caller that frees pinned banks and may
+ * capture again calls this first, so a later capture cannot take a stale translation
+ * (mc_hybrid_stage_free does it for the stage).  p = NULL is MC_EINVAL.
+ */
+int mc_host_forget(const void* p, size_t bytes);
 
 /* Bank bits of mc_fill_slots_banks. */
 enum { MC_BANK_GATE_UP = 1, MC_BANK_GATE_UP_SCALE = 2, MC_BANK_DOWN = 4, MC_BANK_DOWN_SCALE = 8,

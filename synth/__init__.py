@@ -308,21 +308,23 @@ def uniform_logits(cfg: Config, T: Optional[int] = None, layer: int = 0) -> np.n
     return _rng(cfg.seed, _TAG_LOGIT, 1 << 30, layer).standard_normal((T, cfg.E), dtype=np.float32)
 
 
-def qiita_replay_trace(E: int, K: int, steps: int, locality: float, seed: int) -> np.ndarray:
-    """The Qiita article's synthetic routing trace ("5. デコード側の答え その1").
-
-    A working set of K ids is drawn without replacement; at every step each
-    position is independently re-drawn, uniformly over all E ids (duplicates
-    allowed), with probability 1 - locality.  Same seed and the same order of
-    generator calls as the article describes, so the article's printed miss rate
-    can be reproduced.
+def drifting_working_set(E: int, K: int, steps: int, locality: float, seed: int) -> np.ndarray:
+    """Routing trace of the Qiita article's simulation ("5. デコード側の答え その1"),
+    generated here from its description: K positions start on K distinct ids; at
+    every step each position independently takes a fresh id, uniform over all E
+    experts (so two positions may coincide), with probability 1 - locality, and
+    keeps its id otherwise.  All random draws of the run are made up front from
+    this module's seeded streams (not the article's generator sequence), so the
+    article's printed miss rates are matched statistically, not digit for digit.
+    Returns int32 [steps, K].
     """
-    g = np.random.default_rng(seed)
-    ws = g.choice(E, size=K, replace=False)
-    rows = []
-    for _ in range(steps):
-        change = g.random(K) > locality
-        cand = g.integers(0, E, K)
-        ws = np.where(change, cand, ws)
-        rows.append(ws.copy())
-    return np.asarray(rows, dtype=np.int32)
+    g = _rng(seed, _TAG_TRACE, E, K)
+    start = g.permutation(E)[:K]
+    redraw = g.random((steps, K)) >= locality          # position takes a fresh id this step
+    fresh = g.integers(0, E, size=(steps, K))
+    # the id a position holds at step s is the fresh id of its latest redraw at or
+    # before s, or its starting id if it was never redrawn
+    step_idx = np.where(redraw, np.arange(steps)[:, None], -1)
+    last = np.maximum.accumulate(step_idx, axis=0)
+    held = np.where(last >= 0, fresh[np.maximum(last, 0), np.arange(K)[None, :]], start[None, :])
+    return held.astype(np.int32)

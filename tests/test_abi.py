@@ -129,10 +129,20 @@ def test_static_placement_matches_oracle():
     import synth
     from expert_cache_offloaded_amd.runtime import static_placement
     from oracle import static_resident_set
-    tr = synth.qiita_replay_trace(256, 8, 600, 0.95, 20260825)
+    tr = synth.drifting_working_set(256, 8, 600, 0.95, 20260825)
     for cap in (1, 8, 64, 200):
         assert static_placement(tr[:512], cap).tolist() == static_resident_set(tr[:512], cap)
     r = np.random.default_rng(4)
     for _ in range(20):
         w = r.integers(0, 40, size=(r.integers(1, 30), 6))
         assert static_placement(w, 10).tolist() == static_resident_set(w, 10)
+
+
+def test_host_forget_needs_no_gpu():
+    """mc_host_forget drops remembered host translations; with none remembered for an
+    address it drops nothing, and NULL is refused."""
+    from expert_cache_offloaded_amd import _lib
+    buf = C.create_string_buffer(64)
+    assert _lib.host_forget(C.addressof(buf), 64) == 0
+    with pytest.raises(_lib.McError):
+        _lib.host_forget(0, 0)

@@ -137,3 +137,109 @@ def test_prefill_grouped_equals_per_token(fmt):
     y_g = prefill_grouped(x, ids, w, banks, cfg.E, fmt, cfg.H, cfg.I)
     y_t = prefill_per_token(x, ids, w, banks, cfg.E, fmt, cfg.H, cfg.I)
     assert np.max(np.abs(y_g - y_t)) <= 1e-12 * np.max(np.abs(y_t))
+
+
+def _per_route_sum(x_bits, ids, w, banks, layer, E, fmt, H, I, n_tok=None, keep=None):
+    """y_t = sum_j w_tj Expert_{layer*E + ids_tj}(x_t), one route at a time, each expert
+    evaluated by the explicit-loop FFN ([jjl357] "1.1": the gate-weighted sum of the
+    selected experts' outputs)."""
+    x = bf16_to_f64(x_bits)
+    T, k = ids.shape
+    n_tok = T if n_tok is None else n_tok
+    y = np.zeros((T, H))
+    for t in range(n_tok):
+        for j in range(k):
+            e = int(ids[t, j])
+            if e < 0 or (keep is not None and not keep[t, j]):
+                continue
+            wg, wu, wd = expert_matrices(banks, layer * E + e, fmt, H, I)
+            y[t] += float(w[t, j]) * expert_ffn_loops(wg, wu, wd, x[t])
+    return y
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("n_tok", [None, 3])
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_decode_layer_equals_per_route_definition(fmt, n_tok, with_shared):
+    cfg = _small_cfg(fmt, H=32, I=32, E=6, k=3, T=5)
+    banks = synth.host_pool(cfg)
+    shared = synth.shared_pool(cfg) if with_shared else None
+    r = np.random.default_rng(17)
+    x = synth.activations(cfg, 1)
+    # several tokens share experts, so a per-expert grouping has to scatter to the right rows
+    ids = np.stack([r.choice(cfg.E, cfg.k, replace=False) for _ in range(cfg.T)]).astype(np.int32)
+    ids[1] = ids[0][::-1]
+    ids[3, 2] = -1
+    w = r.random((cfg.T, cfg.k)) + 0.1
+    for layer in (0, 1):
+        want = _per_route_sum(x, ids, w, banks, layer, cfg.E, fmt, cfg.H, cfg.I, n_tok=n_tok)
+        if with_shared:
+            wg, wu, wd = expert_matrices(shared, layer, fmt, cfg.H, cfg.I)
+            xs = bf16_to_f64(x)
+            for t in range(cfg.T if n_tok is None else n_tok):
+                want[t] += expert_ffn_loops(wg, wu, wd, xs[t])
+        got = decode_layer(x, ids, w, banks, layer, cfg.E, fmt, cfg.H, cfg.I, shared=shared, n_tok=n_tok)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+        if n_tok is not None:
+            assert np.all(got[n_tok:] == 0.0)
+        # the split: the GPU partial is the per-route sum over resident routes, the host
+        # partial the sum over the others
+        slots = np.where(r.random((cfg.T, cfg.k)) < 0.5, 2, -1).astype(np.int32)
+        y_gpu, y_host, _, _ = hybrid_partials(x, ids, slots, w, banks, layer, cfg.E, fmt, cfg.H, cfg.I,
+                                              n_tok=n_tok)
+        want_gpu = _per_route_sum(x, ids, w, banks, layer, cfg.E, fmt, cfg.H, cfg.I, n_tok, keep=slots >= 0)
+        want_host = _per_route_sum(x, ids, w, banks, layer, cfg.E, fmt, cfg.H, cfg.I, n_tok, keep=slots < 0)
+        tol = 1e-12 * max(1.0, np.max(np.abs(want)))
+        assert np.max(np.abs(y_gpu - want_gpu)) <= tol
+        assert np.max(np.abs(y_host - want_host)) <= tol
+
+
+def _bf16_bits(vals):
+    """bf16 bit patterns of values that bf16 holds exactly."""
+    a = np.asarray(vals, dtype=np.float32)
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bf16_to_f64(bits), a.astype(np.float64))
+    return bits
+
+
+def test_decode_layer_hand_built_two_layers():
+    """Two layers of two experts, H = 2, I = 1, every weight a small exact binary
+    fraction and different per (layer, expert): the output is evaluated by hand from
+    y_t = sum_j w_tj * wd * silu(wg . x_t) * (wu . x_t)."""
+    L_, E, H, I = 2, 2, 2, 1
+    # (wg0, wg1, wu0, wu1, wd0, wd1) per flat id l*E + e
+    params = {0: (0.5, -1.0, 1.0, 0.25, 2.0, -0.5),
+              1: (1.0, 0.5, -0.5, 1.0, 1.0, 3.0),
+              2: (-0.25, 2.0, 0.75, -1.0, -1.0, 0.5),
+              3: (1.5, 1.0, 0.5, 0.5, 0.25, -2.0)}
+    gu = np.zeros((L_ * E, 2 * I, H), dtype=np.uint16)
+    dn = np.zeros((L_ * E, H, I), dtype=np.uint16)
+    for f, (g0, g1, u0, u1, d0, d1) in params.items():
+        gu[f] = _bf16_bits([[g0, g1], [u0, u1]])
+        dn[f] = _bf16_bits([[d0], [d1]])
+    banks = {"gate_up": gu, "down": dn}
+    x_vals = [[1.0, 2.0], [-0.5, 0.25]]
+    x = _bf16_bits(x_vals)
+    ids = np.array([[1, 0], [0, -1]], dtype=np.int32)
+    w = np.array([[0.75, 0.25], [0.5, 0.125]])
+
+    def by_hand(layer):
+        y = np.zeros((2, H))
+        for t in range(2):
+            for j in range(2):
+                e = int(ids[t, j])
+                if e < 0:
+                    continue
+                g0, g1, u0, u1, d0, d1 = params[layer * E + e]
+                xa, xb = x_vals[t]
+                g = g0 * xa + g1 * xb
+                u = u0 * xa + u1 * xb
+                h = g / (1.0 + math.exp(-g)) * u
+                y[t, 0] += w[t, j] * d0 * h
+                y[t, 1] += w[t, j] * d1 * h
+        return y
+
+    for layer in range(L_):
+        got = decode_layer(x, ids, w, banks, layer, E, "bf16", H, I)
+        assert np.max(np.abs(got - by_hand(layer))) <= 1e-14
+    assert np.max(np.abs(by_hand(0) - by_hand(1))) > 0.1       # the layers really differ
