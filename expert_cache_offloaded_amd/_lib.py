@@ -84,7 +84,7 @@ _SIGS = {
     "mc_cache_install": (C.c_int, [C.POINTER(Cache), _P, _I32, _P]),
     "mc_host_forget": (C.c_int, [_P, C.c_size_t]),
     "mc_fill_slots_banks": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _P, _P, _I32, C.c_uint32, _P]),
-    "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32]),
+    "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
                                      _P, C.c_size_t, _P, _I32, _P, _P, C.POINTER(FillList)]),
     "mc_prefill_sort_routes": (C.c_int, [_P, _I32, _I32, _P, _I32, _P, C.c_size_t, _P, _P, _P, _P]),
@@ -240,8 +240,8 @@ def fill_slots(host: Banks, pool: Banks, fill_flat, fill_slot, n_fill, stream=No
                                                 _stream(stream)))
 
 
-def decode_ws_bytes(T: int, k: int, I: int) -> int:
-    return int(lib().moe_experts_decode_ws_bytes(T, k, I))
+def decode_ws_bytes(T: int, k: int, H: int, I: int) -> int:
+    return int(lib().moe_experts_decode_ws_bytes(T, k, H, I))
 
 
 def make_fill_list(host: Banks, fill_flat, fill_slot, n_fill, gate_up_only: bool = False,

@@ -5,108 +5,54 @@
 // and [wanger] "代码全链路": the GPU runs hits + fills; host-computed routes arrive
 // with slot -1 (or gate 0) and are skipped.
 //
-// Decode is a GEMV that streams ~0.53 B of MXFP4 weight per multiply-add, so it is
-// bound by HBM bandwidth; at batch 1 a layer moves only ~15 MB, so what matters is
-// having every weight load of a wave in flight at once (no branch or conversion
-// between a load and the next one).  Two kernels, no cross-workgroup waiting:
-//   gate_up: workgroup = (unit, 4 WR intermediate rows); a unit is one distinct slot of
-//      the call, run by the grid column of the first route that holds it, or the
-//      shared expert.  Each wave owns WR gate rows and the WR matching up rows; lane
-//      l reads the 16-byte chunks l, l+64, ... of every row (one coalesced 1 KiB
-//      row slice per load instruction), keeps them in registers and reuses them for
-//      every token that routes to the unit.  Dot
-//      products run on packed bf16 (MXFP4 -> bf16 is exact) with fp32 accumulation;
-//      h = silu(g) * u is written in fp32 per route.
-//   down: workgroup = (ROWS hidden rows, one token), over every route of the token.
-//      The token's h vectors are staged in LDS; each wave takes every fourth route, loads all of
-//      its rows first, then computes; the waves' partial sums meet in LDS and are
-//      added in a fixed order, so every output element is written once (no atomics,
-//      run-to-run identical).  The same pass writes the bf16 output when asked.
+// Decode streams ~0.53 B of MXFP4 weight per multiply-add, so it is bound by HBM
+// bandwidth, and every weight must be dequantised exactly once whatever the batch.
+// Both passes therefore run on the matrix cores: the expert's weight rows are the
+// MFMA's N side (16 rows per tile, MXFP4 -> bf16 dequantised exactly), the tokens its
+// M side, and K runs in steps of 128 in which each lane owns one whole 32-element MX
+// block (16 B of codes + 1 scale byte) of its row; the activation operand is read in
+// the same permuted K order.  A unit is one distinct slot of the call (run by the grid
+// column of the first route that holds it) or the shared expert.
+//   gate_up: workgroup = (unit, 16 intermediate rows); the four waves split H, each
+//      loading its gate and up fragments for all of its K steps at once, and the four
+//      products meet in LDS in a fixed order.  The unit's tokens, 16 at a time, are the
+//      MFMA rows.  h = silu(g) * u is stored as two bf16 halves (hi = bf16(h), lo =
+//      bf16(h - hi): 16 significant bits, the fp32 value to within 2^-17).
+//   down, one token: workgroup = 16 hidden rows over every route of the token (no
+//      cross-workgroup sum); the waves split I.  The hi and lo halves of a route's h are
+//      two MFMA rows of one product, added after it.  The token's h vectors are staged in
+//      LDS by DMA while the weight loads are in flight.
+//   down, several tokens: workgroup = (unit, 64 hidden rows); each wave owns a 16-row
+//      tile over all of I, loaded once; the unit's routes (hi and lo rows, 8 routes per
+//      product) are staged in LDS a batch at a time.  Each route's gated partial is
+//      stored, and the last workgroup of a row block to arrive (one arrival counter per
+//      row block) adds the partials of every token in route order (j = 0 .. k-1, then
+//      the shared expert), so each output element is one fixed-order sum (no float
+//      atomics, run-to-run identical).
 // Fill-through: when the call carries the lookup's fill list, a unit whose slot is
-// being filled reads its rows from the pinned host entry instead (over the host
-// link) and stores them into the slot from the registers that hold them, so the
-// fill and the expert pass are one stream of loads.  gate_up records each route's
-// host source in the workspace; down reads it there.
+// being filled reads its fragments from the pinned host entry instead (over the host
+// link) and stores them into the slot from the registers that hold them, so the fill
+// and the expert pass are one stream of loads.
+#include <algorithm>
+
 #include "mc_common.h"
 
 namespace mc {
 
 constexpr int kThreads = 256;
-// gate_up: WR intermediate rows per wave (WR gate + WR up rows), 4 WR per workgroup;
-// down: ROWS hidden rows per workgroup.  Chosen per call: single-token calls take the
-// smaller gate_up tile (more workgroups for few units), batched calls the larger down
-// tile (a token's h staged once for more rows).
-constexpr int kB_RoutesPerWave = 3;          // down: routes a wave holds in registers at once
 constexpr int kMaxRoutes = 1024;
 constexpr int kMaxTok = 64;
-constexpr int kB_LdsBytes = 64 * 1024;
-
-// ---------------------------------------------------------------- chunk dots
+constexpr int kKS = 128;                     // K elements per step (4 MFMAs of 32)
+constexpr int kHLdsBytes = 32 * 1024;        // down (several tokens): LDS for a batch of h
+constexpr int kRouteTile = 8;                // routes per down product (hi + lo rows)
+constexpr int kUnitRows = 64;                // down (several tokens): rows per workgroup
+constexpr int kCntStride = 16;               // uint32 words between arrival counters (64 B)
+constexpr int kTok1LdsBytes = 64 * 1024;    // down (one token): LDS for all of the token's h
 
 // 16-byte weight load marked non-temporal: every weight byte of a call is used once,
 // and the same form serves HBM slots and pinned host entries (fill-through).
-__device__ __forceinline__ uint4 stream_load16(const uint4* p) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// x pairs: packed bf16 pairs of the chunk's activations.
-// MXFP4 chunk: 32 elements, 16 B codes, one e8m0 scale; x: 16 dwords.
-__device__ __forceinline__ float dot_chunk_mx(const uint4& w, float scale, const uint32_t* xp,
-                                              float acc) {
-  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc = dot2_bf16(fp4x2_to_bf16x2<0>(d[q], scale), xp[4 * q + 0], acc);
-    acc = dot2_bf16(fp4x2_to_bf16x2<1>(d[q], scale), xp[4 * q + 1], acc);
-    acc = dot2_bf16(fp4x2_to_bf16x2<2>(d[q], scale), xp[4 * q + 2], acc);
-    acc = dot2_bf16(fp4x2_to_bf16x2<3>(d[q], scale), xp[4 * q + 3], acc);
-  }
-  return acc;
-}
-
-// bf16 chunk: 8 elements; x: 4 dwords.
-__device__ __forceinline__ float dot_chunk_bf(const uint4& w, const uint32_t* xp, float acc) {
-  acc = dot2_bf16(w.x, xp[0], acc);
-  acc = dot2_bf16(w.y, xp[1], acc);
-  acc = dot2_bf16(w.z, xp[2], acc);
-  acc = dot2_bf16(w.w, xp[3], acc);
-  return acc;
-}
-
-// fp32 activations (h): MXFP4 chunk of 32 weights against 32 floats.
-__device__ __forceinline__ float dot_chunk_mx_f32(const uint4& w, float scale, const float* h,
-                                                  float acc) {
-  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x2_t a = fp4x2_to_f32x2<0>(d[q], scale);
-    f32x2_t b = fp4x2_to_f32x2<1>(d[q], scale);
-    f32x2_t c = fp4x2_to_f32x2<2>(d[q], scale);
-    f32x2_t e = fp4x2_to_f32x2<3>(d[q], scale);
-    acc = fmaf(a.x, h[8 * q + 0], acc);
-    acc = fmaf(a.y, h[8 * q + 1], acc);
-    acc = fmaf(b.x, h[8 * q + 2], acc);
-    acc = fmaf(b.y, h[8 * q + 3], acc);
-    acc = fmaf(c.x, h[8 * q + 4], acc);
-    acc = fmaf(c.y, h[8 * q + 5], acc);
-    acc = fmaf(e.x, h[8 * q + 6], acc);
-    acc = fmaf(e.y, h[8 * q + 7], acc);
-  }
-  return acc;
-}
-
-__device__ __forceinline__ float dot_chunk_bf_f32(const uint4& w, const float* h, float acc) {
-  acc = fmaf(bf16_lo(w.x), h[0], acc);
-  acc = fmaf(bf16_hi(w.x), h[1], acc);
-  acc = fmaf(bf16_lo(w.y), h[2], acc);
-  acc = fmaf(bf16_hi(w.y), h[3], acc);
-  acc = fmaf(bf16_lo(w.z), h[4], acc);
-  acc = fmaf(bf16_hi(w.z), h[5], acc);
-  acc = fmaf(bf16_lo(w.w), h[6], acc);
-  acc = fmaf(bf16_hi(w.w), h[7], acc);
-  return acc;
+__device__ __forceinline__ u32x4_t stream_load16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
 struct DecodeArgs {
@@ -124,8 +70,15 @@ struct DecodeArgs {
   const uint8_t* sh_gus;
   const uint8_t* sh_dn;
   const uint8_t* sh_dns;
-  float* h_route;             // [T*k][I]
-  float* h_shared;            // [T][I]
+  // vector v: route v (v < T*k) or the shared expert of token v - T*k
+  float* h32;                 // [T*k + T][I] fp32 h (one-token path)
+  uint16_t* h_hi;             // [T*k + T][I] bf16(h)
+  uint16_t* h_lo;             // [T*k + T][I] bf16(h - hi)
+  float* part;                // [T*k + T][H] gated partial outputs (several-token down)
+  int32_t* rsrc;              // [T*k] host entry a route's unit reads (fill-through), -1 = slot
+  uint32_t* cnt;              // [n_cnt * kCntStride] arrival counters of the down row blocks
+  int32_t n_cnt;
+  int32_t tb;                 // several-token down: routes per LDS batch
   float* y;                   // [T][H]
   uint16_t* y_bf16;           // [T][H] or null
   int32_t accumulate;
@@ -140,8 +93,9 @@ struct DecodeArgs {
   const int32_t* fill_slot;
   const int32_t* n_fill;
   int32_t kcap;
-  int32_t* rsrc;              // [T*k] host flat id a route's weights come from, -1 = slot
 };
+
+// ---------------------------------------------------------------- units
 
 // Host entry that fills `slot` in this call, or -1 (wave-uniform; lanes search the
 // list 64 entries at a time).
@@ -175,69 +129,371 @@ __device__ __forceinline__ uint64_t routes_with_slot(const DecodeArgs& a, int ba
   return __ballot(j < end && pool_slot(a, j) == slot);
 }
 
-// ---------------------------------------------------------------- gate_up kernel
-
-template <int FMT, int CPL, int WR>
-__global__ void __launch_bounds__(kThreads)
-gate_up_kernel(DecodeArgs a) {
-  // column u < T*k: route u's slot, when no earlier route of the call holds it (the
-  // first route of a unit); column T*k: the shared expert
-  // The unit's slot, the slots of its window of 64 routes and the valid count are read
-  // in one round trip (every route index below T*k is readable, valid or not), so the
-  // weight loads wait behind a single dependent read.
-  const int u = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Whether grid column u runs a unit, and its slot.  Column u < T*k runs route u's slot
+// when no earlier route of the call holds it; column T*k is the shared expert (runs
+// when any token is valid).  The column's slot, the slots of its window of 64 routes
+// and the valid count are read in one round trip (every route index below T*k is
+// readable, valid or not), so the weight loads wait behind a single dependent read.
+// Wave-uniform; every wave of the workgroup gets the same answer.
+__device__ __forceinline__ bool column_unit(const DecodeArgs& a, int u, int& slot, int& win_slot,
+                                            int& nt, int& nr) {
+  const int lane = threadIdx.x & 63;
   const int n_all = a.T * a.k;
   const bool shared_unit = a.has_shared && u == n_all;
   const int wbase = u & ~63;
-  int slot_raw = -1, win_slot = -1;
+  int slot_raw = -1;
+  win_slot = -1;
   if (!shared_unit) {
     slot_raw = a.slots[u];
     if (wbase + lane < n_all) win_slot = a.slots[wbase + lane];
   }
-  const int nt = valid_tokens(a);
-  const int nr = nt * a.k;
-  int slot = -1;
-  if (shared_unit) {
-    if (nt == 0) return;
-  } else {
-    if (u >= nr) return;
-    slot = (slot_raw >= 0 && slot_raw < a.n_pool) ? slot_raw : -1;
-    if (slot < 0) return;
-    if (__ballot(wbase + lane < u && win_slot == slot)) return;
-    for (int base = 0; base < wbase; base += 64)
-      if (routes_with_slot(a, base, u, slot)) return;
+  nt = valid_tokens(a);
+  nr = nt * a.k;
+  slot = -1;
+  if (shared_unit) return nt > 0;
+  if (u >= nr) return false;
+  slot = (slot_raw >= 0 && slot_raw < a.n_pool) ? slot_raw : -1;
+  if (slot < 0) return false;
+  if (__ballot(wbase + lane < u && win_slot == slot)) return false;
+  for (int base = 0; base < wbase; base += 64)
+    if (routes_with_slot(a, base, u, slot)) return false;
+  return true;
+}
+
+// The unit's vectors in route order into LDS (the shared expert: every valid token);
+// run by one wave, returns the count on every lane of it.
+__device__ __forceinline__ int unit_vectors(const DecodeArgs& a, int u, int slot, int win_slot, int nt,
+                                            int nr, int32_t* s_vec) {
+  const int lane = threadIdx.x & 63;
+  const int n_all = a.T * a.k;
+  if (a.has_shared && u == n_all) {
+    for (int t = lane; t < nt; t += 64) s_vec[t] = n_all + t;
+    return nt;
   }
+  int n = 0, base = u & ~63;
+  uint64_t m = __ballot(base + lane >= u && base + lane < nr && win_slot == slot);
+  while (true) {
+    while (!m && base + 64 < nr) {
+      base += 64;
+      m = routes_with_slot(a, base, nr, slot);
+    }
+    if (!m) break;
+    if ((m >> lane) & 1)
+      s_vec[n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0))] =
+          base + lane;
+    n += __builtin_popcountll(m);
+    m = 0;
+  }
+  return n;
+}
 
-  const int H = a.H, I = a.I;
-  const int i0 = blockIdx.y * (4 * WR) + wave * WR;   // first intermediate row
-  constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;             // elements per 16-B chunk
-  const int n_chunks = H / ELEMS;
+// ---------------------------------------------------------------- MFMA fragments
+//
+// Weight fragment of one 16-row tile and one K step: lane l owns row (l & 15) and the
+// 32-element block 4 * step + (l >> 4) of it: 16 B of MXFP4 codes + its scale byte, or
+// 64 B of bf16.  The four MFMAs of the step consume elements 8 ks .. 8 ks + 7 of every
+// lane's block (ks = 0..3), so the activation operand of lane l holds, for its token
+// row (l & 15), elements 128 step + 32 (l >> 4) + 8 ks .. + 7.
+
+template <int FMT>
+struct WFrag {
+  u32x4_t v[FMT == MC_MXFP4 ? 1 : 4];
+  uint32_t s;
+};
+
+template <int FMT>
+__device__ __forceinline__ void wfrag_load(WFrag<FMT>& f, const uint8_t* row, const uint8_t* srow, int blk,
+                                           bool ok) {
+  const int b = ok ? blk : 0;
+  if (FMT == MC_MXFP4) {
+    f.v[0] = stream_load16(row + (size_t)b * 16);
+    f.s = srow[b];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f.v[q] = stream_load16(row + (size_t)b * 64 + q * 16);
+    f.s = 0;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void wfrag_store(const WFrag<FMT>& f, uint8_t* row, uint8_t* srow, int blk) {
+  if (FMT == MC_MXFP4) {
+    *reinterpret_cast<u32x4_t*>(row + (size_t)blk * 16) = f.v[0];
+    srow[blk] = (uint8_t)f.s;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(row + (size_t)blk * 64 + q * 16) = f.v[q];
+  }
+}
+
+// B operand of MFMA ks (an invalid block contributes zeros)
+template <int FMT>
+__device__ __forceinline__ bf16x8_t wfrag_op(const WFrag<FMT>& f, int ks, bool ok) {
+  if (!ok) return bf16x8_t{};
+  if (FMT == MC_MXFP4) return fp4x8_bf16(f.v[0][ks], e8m0_to_f32(f.s));
+  return __builtin_bit_cast(bf16x8_t, f.v[ks]);
+}
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ---------------------------------------------------------------- gate_up kernel
+
+template <int FMT, int SPW>   // SPW: K steps per wave
+__global__ void __launch_bounds__(kThreads)
+gate_up_kernel(DecodeArgs a) {
+  __shared__ f32x4_t s_red[4][2][64];            // per-wave gate / up products
+  __shared__ int32_t s_vec[kMaxRoutes];
+  __shared__ int32_t s_n;
+  // the several-token down pass's arrival counters start at zero in every call
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < a.n_cnt; i += kThreads) a.cnt[i * kCntStride] = 0u;
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, n_all = a.T * a.k;
+  const bool shared_unit = a.has_shared && u == n_all;
+  int slot, win_slot, nt, nr;
+  if (!column_unit(a, u, slot, win_slot, nt, nr)) return;
+
   const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)H / 2 : (size_t)H * 2;
-
+  const size_t per_gu = 2 * (size_t)I * row_bytes, per_gus = (size_t)2 * I * H / 32;
   const uint8_t* gu;
   const uint8_t* gus = nullptr;
-  uint8_t* wb_gu = nullptr;        // fill-through: the slot entry the rows are stored to
-  uint8_t* wb_gus = nullptr;
+  uint8_t* wb = nullptr;                         // fill-through: slot entry the fragments go to
+  uint8_t* wbs = nullptr;
   int64_t src = -1;
   if (shared_unit) {
     gu = a.sh_gu;
     gus = a.sh_gus;
   } else {
-    const size_t per_gu = 2 * (size_t)I * row_bytes, per_gus = (size_t)2 * I * H / 32;
     gu = a.gu + (size_t)slot * per_gu;
     if (FMT == MC_MXFP4) gus = a.gus + (size_t)slot * per_gus;
     if (a.f_gu) src = fill_source(a, slot);
     if (src >= 0) {
-      wb_gu = const_cast<uint8_t*>(gu);
-      wb_gus = const_cast<uint8_t*>(gus);
+      wb = const_cast<uint8_t*>(gu);
+      wbs = const_cast<uint8_t*>(gus);
       gu = a.f_gu + (size_t)src * per_gu;
       if (FMT == MC_MXFP4) gus = a.f_gus + (size_t)src * per_gus;
     }
   }
+  const int i0 = blockIdx.y * 16;                // first intermediate row of the tile
+  const int rl = lane & 15, g4 = lane >> 4;
+  const int n_blk = H / 32;
+  const uint8_t* grow = gu + (size_t)(i0 + rl) * row_bytes;
+  const uint8_t* urow = gu + (size_t)(I + i0 + rl) * row_bytes;
+  const uint8_t* gsrow = FMT == MC_MXFP4 ? gus + (size_t)(i0 + rl) * (H / 32) : nullptr;
+  const uint8_t* usrow = FMT == MC_MXFP4 ? gus + (size_t)(I + i0 + rl) * (H / 32) : nullptr;
 
-  // all loads of the wave's 8 rows first (chunk index clamped; out-of-row lanes are
-  // zeroed after the loads), scale bytes kept raw until every load is issued
+  // every weight load of the wave first
+  WFrag<FMT> fg[SPW], fu[SPW];
+  bool okb[SPW];
+  int blk[SPW];
+#pragma unroll
+  for (int q = 0; q < SPW; ++q) {
+    blk[q] = 4 * (wave * SPW + q) + g4;
+    okb[q] = blk[q] < n_blk;
+    wfrag_load<FMT>(fg[q], grow, gsrow, blk[q], okb[q]);
+    wfrag_load<FMT>(fu[q], urow, usrow, blk[q], okb[q]);
+  }
+  if (wave == 0) {
+    const int n = unit_vectors(a, u, slot, win_slot, nt, nr, s_vec);
+    if (lane == 0) s_n = n;
+  }
+  __syncthreads();
+  const int n_vec = s_n;
+  if (!shared_unit && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < n_vec; i += kThreads) a.rsrc[s_vec[i]] = (int32_t)src;
+
+  for (int b0 = 0; b0 < n_vec; b0 += 16) {
+    const int nb = min(16, n_vec - b0);
+    // activation rows: the token of vector b0 + rl
+    const bool row_ok = rl < nb;
+    const int vec = row_ok ? s_vec[b0 + rl] : 0;
+    const int tok = vec < n_all ? vec / a.k : vec - n_all;
+    const uint16_t* xrow = a.x + (size_t)tok * H;
+    f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+      u32x4_t xa[4];
+      const bool ok = okb[q] && row_ok;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        xa[ks] = ok ? *reinterpret_cast<const u32x4_t*>(xrow + (size_t)blk[q] * 32 + 8 * ks) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[ks]);
+        accg = mfma(av, wfrag_op<FMT>(fg[q], ks, okb[q]), accg);
+        accu = mfma(av, wfrag_op<FMT>(fu[q], ks, okb[q]), accu);
+      }
+    }
+    s_red[wave][0][lane] = accg;
+    s_red[wave][1][lane] = accu;
+    __syncthreads();
+    if (wave == 0) {
+      const f32x4_t g = ((s_red[0][0][lane] + s_red[1][0][lane]) + s_red[2][0][lane]) + s_red[3][0][lane];
+      const f32x4_t up = ((s_red[0][1][lane] + s_red[1][1][lane]) + s_red[2][1][lane]) + s_red[3][1][lane];
+      // D[token row 4 g4 + j][weight row rl]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 4 * g4 + j;
+        if (m < nb) {
+          const float h = silu(g[j]) * up[j];
+          const uint16_t hi = f32_to_bf16_rne(h);
+          const size_t o = (size_t)s_vec[b0 + m] * I + i0 + rl;
+          a.h_hi[o] = hi;
+          a.h_lo[o] = f32_to_bf16_rne(h - bf16_val(hi));
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // fill-through: the fragments read from the host go into the slot
+  if (wb) {
+#pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+      if (!okb[q]) continue;
+      wfrag_store<FMT>(fg[q], wb + (size_t)(i0 + rl) * row_bytes,
+                       FMT == MC_MXFP4 ? wbs + (size_t)(i0 + rl) * (H / 32) : nullptr, blk[q]);
+      wfrag_store<FMT>(fu[q], wb + (size_t)(I + i0 + rl) * row_bytes,
+                       FMT == MC_MXFP4 ? wbs + (size_t)(I + i0 + rl) * (H / 32) : nullptr, blk[q]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- h staging
+
+// XOR applied to the 16-byte chunks of an LDS row of h (rows of I bf16).
+__device__ __forceinline__ int h_cmask(int I) { return (I / 8) % 16 == 0 ? 15 : 7; }
+
+// LDS rows of h: row R = 2 b + half (half 0 = hi, 1 = lo) of the b-th staged vector,
+// I bf16 each; 16-byte chunk c of row R sits at chunk c ^ (R & cmask), so the 16 rows
+// an operand read touches fall in different banks.  Copied by DMA (global_load_lds,
+// 1 KiB per wave instruction, the LDS area rounded up to whole KiB): LDS position is
+// fixed per lane, so each lane fetches the global chunk that belongs there.
+__device__ __forceinline__ void stage_h(const DecodeArgs& a, const int32_t* vecs, int nvec, uint16_t* s_hv,
+                                        int wave, int lane) {
+  const int I = a.I;
+  const int cpr = I / 8, cmask = h_cmask(I);
+  const int total = 2 * nvec * cpr;
+  for (int ch = wave; ch * 64 < total; ch += 4) {
+    int p = ch * 64 + lane;
+    if (p >= total) p = total - 1;               // tail lanes re-read a valid chunk
+    const int R = p / cpr, c = (p % cpr) ^ (R & cmask);
+    const uint16_t* src = (R & 1 ? a.h_lo : a.h_hi) + (size_t)vecs[R >> 1] * I + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(s_hv + ch * 512), 16, 0,
+                                     0);
+  }
+}
+
+// Activation operand of MFMA ks in block `blk`: row R of the staged h.
+__device__ __forceinline__ bf16x8_t h_op(const uint16_t* s_hv, int R, int blk, int ks, int I) {
+  const int c = (blk * 4 + ks) ^ (R & h_cmask(I));
+  return *reinterpret_cast<const bf16x8_t*>(s_hv + (size_t)R * I + c * 8);
+}
+
+// ---------------------------------------------------------------- one token
+//
+// At batch 1 a layer's weights are streamed once and each lane's work per 16-byte
+// chunk is a handful of instructions, so what decides the time is that every load of
+// the grid is in flight in a single round of resident workgroups.  Both one-token
+// kernels read whole row slices (lane l takes 16-byte chunks l, l + 64, ... of a row:
+// one coalesced 1 KiB piece per load instruction) straight into registers and keep
+// their register count low enough for the whole grid to be resident at once.
+
+// x pairs: packed bf16 pairs of the chunk's activations.
+// MXFP4 chunk: 32 elements, 16 B codes, one e8m0 scale; x: 16 dwords.
+__device__ __forceinline__ float dot_chunk_mx(const u32x4_t& w, float scale, const uint32_t* xp, float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = dot2_bf16(fp4x2_to_bf16x2<0>(w[q], scale), xp[4 * q + 0], acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<1>(w[q], scale), xp[4 * q + 1], acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<2>(w[q], scale), xp[4 * q + 2], acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<3>(w[q], scale), xp[4 * q + 3], acc);
+  }
+  return acc;
+}
+
+// bf16 chunk: 8 elements; x: 4 dwords.
+__device__ __forceinline__ float dot_chunk_bf(const u32x4_t& w, const uint32_t* xp, float acc) {
+  acc = dot2_bf16(w[0], xp[0], acc);
+  acc = dot2_bf16(w[1], xp[1], acc);
+  acc = dot2_bf16(w[2], xp[2], acc);
+  acc = dot2_bf16(w[3], xp[3], acc);
+  return acc;
+}
+
+// fp32 activations (h): MXFP4 chunk of 32 weights against 32 floats.
+__device__ __forceinline__ float dot_chunk_mx_f32(const u32x4_t& w, float scale, const float* h, float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x2_t p0 = fp4x2_to_f32x2<0>(w[q], scale);
+    f32x2_t p1 = fp4x2_to_f32x2<1>(w[q], scale);
+    f32x2_t p2 = fp4x2_to_f32x2<2>(w[q], scale);
+    f32x2_t p3 = fp4x2_to_f32x2<3>(w[q], scale);
+    acc = fmaf(p0.x, h[8 * q + 0], acc);
+    acc = fmaf(p0.y, h[8 * q + 1], acc);
+    acc = fmaf(p1.x, h[8 * q + 2], acc);
+    acc = fmaf(p1.y, h[8 * q + 3], acc);
+    acc = fmaf(p2.x, h[8 * q + 4], acc);
+    acc = fmaf(p2.y, h[8 * q + 5], acc);
+    acc = fmaf(p3.x, h[8 * q + 6], acc);
+    acc = fmaf(p3.y, h[8 * q + 7], acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float dot_chunk_bf_f32(const u32x4_t& w, const float* h, float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fmaf(bf16_lo(w[q]), h[2 * q], acc);
+    acc = fmaf(bf16_hi(w[q]), h[2 * q + 1], acc);
+  }
+  return acc;
+}
+
+// gate_up for one token: workgroup = (route column, 8 intermediate rows); each wave
+// owns 2 gate rows and the 2 matching up rows of the route's slot (or of the shared
+// expert).  Every route with a valid slot runs (a slot named twice by the token is read
+// twice, which only a malformed id list can cause).
+template <int FMT, int CPL>
+__global__ void __launch_bounds__(kThreads)
+gate_up_tok1_kernel(DecodeArgs a) {
+  const int u = blockIdx.x, k = a.k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool shared_unit = a.has_shared && u == k;
+  const int slot_raw = shared_unit ? -1 : a.slots[u];
+  if (valid_tokens(a) == 0) return;
+  const int slot = (slot_raw >= 0 && slot_raw < a.n_pool) ? slot_raw : -1;
+  if (!shared_unit && slot < 0) return;
+  const int H = a.H, I = a.I;
+  constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;              // elements per 16-B chunk
+  const int n_chunks = H / ELEMS;
+  const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)H / 2 : (size_t)H * 2;
+  const size_t per_gu = 2 * (size_t)I * row_bytes, per_gus = (size_t)2 * I * H / 32;
+  const uint8_t* gu;
+  const uint8_t* gus = nullptr;
+  uint8_t* wb = nullptr;
+  uint8_t* wbs = nullptr;
+  int64_t src = -1;
+  if (shared_unit) {
+    gu = a.sh_gu;
+    gus = a.sh_gus;
+  } else {
+    gu = a.gu + (size_t)slot * per_gu;
+    if (FMT == MC_MXFP4) gus = a.gus + (size_t)slot * per_gus;
+    if (a.f_gu) src = fill_source(a, slot);
+    if (src >= 0) {
+      wb = const_cast<uint8_t*>(gu);
+      wbs = const_cast<uint8_t*>(gus);
+      gu = a.f_gu + (size_t)src * per_gu;
+      if (FMT == MC_MXFP4) gus = a.f_gus + (size_t)src * per_gus;
+    }
+    if (blockIdx.y == 0 && threadIdx.x == 0) a.rsrc[u] = (int32_t)src;
+  }
+  const int i0 = blockIdx.y * 8 + wave * 2;
   int cq[CPL];
   bool okq[CPL];
 #pragma unroll
@@ -246,115 +502,76 @@ gate_up_kernel(DecodeArgs a) {
     okq[q] = c < n_chunks;
     cq[q] = okq[q] ? c : n_chunks - 1;
   }
-  uint4 wv[2 * WR][CPL];
-  uint32_t sb[2 * WR][CPL];
+  // all loads of the wave's 4 rows first, the scale bytes kept raw until every load is issued
+  u32x4_t wv[4][CPL];
+  uint32_t sb[4][CPL];
 #pragma unroll
-  for (int r = 0; r < 2 * WR; ++r) {
-    const int row = r < WR ? i0 + r : I + i0 + (r - WR);
-    const uint4* rp = reinterpret_cast<const uint4*>(gu + (size_t)row * row_bytes);
+  for (int r = 0; r < 4; ++r) {
+    const int row = r < 2 ? i0 + r : I + i0 + r - 2;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      wv[r][q] = stream_load16(rp + cq[q]);
+      wv[r][q] = stream_load16(gu + (size_t)row * row_bytes + (size_t)cq[q] * 16);
       if (FMT == MC_MXFP4) sb[r][q] = gus[(size_t)row * (H / 32) + cq[q]];
     }
   }
-
-  // the unit's routes in route order: a mask per 64 routes, the next one fetched when
-  // this one runs out (the shared expert takes every valid token in turn)
-  int base = wbase, t_next = 0;
-  uint64_t unit_routes =
-      shared_unit ? 0 : __ballot(wbase + lane >= u && wbase + lane < nr && win_slot == slot);
-  while (true) {
-    int t, route;
-    if (shared_unit) {
-      if (t_next >= nt) break;
-      t = t_next++;
-      route = -1;
-    } else {
-      while (!unit_routes && base + 64 < nr) {
-        base += 64;
-        unit_routes = routes_with_slot(a, base, nr, slot);
-      }
-      if (!unit_routes) break;
-      route = base + __builtin_ctzll(unit_routes);
-      unit_routes &= unit_routes - 1;
-      t = route / a.k;
-      if (blockIdx.y == 0 && threadIdx.x == 0) a.rsrc[route] = (int32_t)src;
-    }
-    const uint32_t* xrow = reinterpret_cast<const uint32_t*>(a.x + (size_t)t * H);
-    uint32_t xp[CPL][ELEMS / 2];
+  const uint16_t* xrow = a.x;                                  // the one token
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const uint4* xs = reinterpret_cast<const uint4*>(xrow + (size_t)cq[q] * (ELEMS / 2));
+  for (int q = 0; q < CPL; ++q) {
+    uint32_t xp[ELEMS / 2];
+    const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(xrow + (size_t)cq[q] * ELEMS);
 #pragma unroll
-      for (int v = 0; v < ELEMS / 8; ++v) {
-        const uint4 xx = xs[v];
-        xp[q][4 * v + 0] = xx.x;
-        xp[q][4 * v + 1] = xx.y;
-        xp[q][4 * v + 2] = xx.z;
-        xp[q][4 * v + 3] = xx.w;
-      }
-    }
-    float acc[2 * WR];
-#pragma unroll
-    for (int r = 0; r < 2 * WR; ++r) {
-      acc[r] = 0.0f;
-#pragma unroll
-      for (int q = 0; q < CPL; ++q) {
-        const uint4 wq = okq[q] ? wv[r][q] : make_uint4(0, 0, 0, 0);
-        if (FMT == MC_MXFP4)
-          acc[r] = dot_chunk_mx(wq, e8m0_to_f32(sb[r][q]), xp[q], acc[r]);
-        else
-          acc[r] = dot_chunk_bf(wq, xp[q], acc[r]);
-      }
+    for (int v = 0; v < ELEMS / 8; ++v) {
+      const u32x4_t xx = xs[v];
+      xp[4 * v + 0] = xx[0];
+      xp[4 * v + 1] = xx[1];
+      xp[4 * v + 2] = xx[2];
+      xp[4 * v + 3] = xx[3];
     }
 #pragma unroll
-    for (int r = 0; r < 2 * WR; ++r) acc[r] = wave_sum(acc[r]);
-    if (lane < WR) {
-      float g = acc[0], up = acc[WR];
-#pragma unroll
-      for (int r = 1; r < WR; ++r)
-        if (lane == r) {
-          g = acc[r];
-          up = acc[WR + r];
-        }
-      float* dst = shared_unit ? a.h_shared + (size_t)t * I : a.h_route + (size_t)route * I;
-      dst[i0 + lane] = silu(g) * up;
+    for (int r = 0; r < 4; ++r) {
+      const u32x4_t wq = okq[q] ? wv[r][q] : u32x4_t{0, 0, 0, 0};
+      acc[r] = FMT == MC_MXFP4 ? dot_chunk_mx(wq, e8m0_to_f32(sb[r][q]), xp, acc[r]) : dot_chunk_bf(wq, xp, acc[r]);
     }
   }
-  // fill-through: the rows this wave read from the host go into the slot
-  if (wb_gu) {
 #pragma unroll
-    for (int r = 0; r < 2 * WR; ++r) {
-      const int row = r < WR ? i0 + r : I + i0 + (r - WR);
+  for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane < 2) {
+    const float g = lane == 0 ? acc[0] : acc[1];
+    const float up = lane == 0 ? acc[2] : acc[3];
+    a.h32[(size_t)u * I + i0 + lane] = silu(g) * up;
+  }
+  if (wb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = r < 2 ? i0 + r : I + i0 + r - 2;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
         if (!okq[q]) continue;
-        reinterpret_cast<uint4*>(wb_gu + (size_t)row * row_bytes)[cq[q]] = wv[r][q];
-        if (FMT == MC_MXFP4) wb_gus[(size_t)row * (H / 32) + cq[q]] = (uint8_t)sb[r][q];
+        *reinterpret_cast<u32x4_t*>(wb + (size_t)row * row_bytes + (size_t)cq[q] * 16) = wv[r][q];
+        if (FMT == MC_MXFP4) wbs[(size_t)row * (H / 32) + cq[q]] = (uint8_t)sb[r][q];
       }
     }
   }
 }
 
-// ---------------------------------------------------------------- down kernel
+// down for one token: workgroup = ROWS hidden rows over every route of the token.  The
+// token's h vectors are staged in LDS; each wave takes every fourth route, loads all of
+// its rows first, then computes; the waves' partial sums meet in LDS and are added in
+// a fixed order, so every output element is written once (no atomics, run-to-run
+// identical), together with the bf16 output when asked.
+constexpr int kRoutesPerWave = 3;          // routes a wave holds in registers at once
 
 template <int FMT, int LPR, int CPLB, int ROWS>
 __global__ void __launch_bounds__(kThreads)
-down_kernel(DecodeArgs a) {
-  extern __shared__ float s_h[];                 // [k + 1][I]: one token's route vectors (swizzled)
+down_tok1_kernel(DecodeArgs a) {
+  extern __shared__ float s_h[];                 // [k + 1][I]: the token's h vectors (swizzled)
   __shared__ float s_part[4][ROWS];
-  const int t = blockIdx.y;
   const int H = a.H, I = a.I, k = a.k;
   const int r0 = blockIdx.x * ROWS;
-  // The valid count, the accumulated y and the token's h vectors are read before the
-  // first wait; the wave's slots and gates and then its weight rows follow once the token
-  // is known to be valid (with no count given, at once), so the rows wait behind one
-  // dependent read.
   const int n_raw = a.n_tok ? *a.n_tok : a.T;
   float y_old = 0.0f;                            // the value accumulated into
-  if (a.accumulate && threadIdx.x < ROWS && r0 + (int)threadIdx.x < H)
-    y_old = a.y[(size_t)t * H + r0 + threadIdx.x];
+  if (a.accumulate && threadIdx.x < ROWS && r0 + (int)threadIdx.x < H) y_old = a.y[r0 + threadIdx.x];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;
   constexpr int E4 = ELEMS / 4;                              // float4 of h per chunk
@@ -366,7 +583,7 @@ down_kernel(DecodeArgs a) {
   const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)I / 2 : (size_t)I * 2;
   const size_t per = (size_t)H * row_bytes;
   const size_t per_s = (size_t)H * I / 32;
-  const int nvec = k + a.has_shared;                         // routes (+ shared) of a token
+  const int nvec = k + a.has_shared;
 
   int cq[CPLB];
   bool okq[CPLB];
@@ -380,49 +597,41 @@ down_kernel(DecodeArgs a) {
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) rowp[p] = min(r0 + row_sub + RPP * p, H - 1);
 
-  constexpr int kGroup = 4 * kB_RoutesPerWave;             // routes covered by one round
+  constexpr int kGroup = 4 * kRoutesPerWave;
   const int n_groups = (nvec + kGroup - 1) / kGroup;
-
-  uint4 wv[kB_RoutesPerWave][PASSES][CPLB];
-  uint32_t sb[kB_RoutesPerWave][PASSES][CPLB];
-  float gate[kB_RoutesPerWave];
-  uint8_t* wb[kB_RoutesPerWave];           // fill-through: slot entry to store the rows to
-  uint8_t* wbs[kB_RoutesPerWave];
-  // the wave's routes v0, v0+4, v0+8: gates and all row loads
+  u32x4_t wv[kRoutesPerWave][PASSES][CPLB];
+  uint32_t sb[kRoutesPerWave][PASSES][CPLB];
+  float gate[kRoutesPerWave];
+  int wsl[kRoutesPerWave];                   // fill-through: slot the rows are stored to, or -1
+  // the wave's routes v0, v0+4, v0+8: slots, gates and host sources in one round trip
+  // (route index clamped into the token's routes), then the rows that depend on them
   auto load_group = [&](int v0) {
-    // the routes' slots, gates and host sources first, all in flight together (route
-    // index clamped into the token's routes), then the rows that depend on them
-    int s_raw[kB_RoutesPerWave], src_raw[kB_RoutesPerWave];
-    float g_raw[kB_RoutesPerWave];
-    if (k > 0) {
+    int s_raw[kRoutesPerWave], src_raw[kRoutesPerWave];
+    float g_raw[kRoutesPerWave];
 #pragma unroll
-      for (int j = 0; j < kB_RoutesPerWave; ++j) {
-        const int r = t * k + min(v0 + 4 * j, k - 1);
-        s_raw[j] = a.slots[r];
-        g_raw[j] = a.w[r];
-        src_raw[j] = a.f_dn ? a.rsrc[r] : -1;
-      }
+    for (int j = 0; j < kRoutesPerWave; ++j) {
+      const int r = min(v0 + 4 * j, k - 1);
+      s_raw[j] = a.slots[r];
+      g_raw[j] = a.w[r];
+      src_raw[j] = a.f_dn ? a.rsrc[r] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kB_RoutesPerWave; ++j) {
+    for (int j = 0; j < kRoutesPerWave; ++j) {
       const int v = v0 + 4 * j;
       const uint8_t* dn = a.dn;            // any readable address when there is nothing to read
       const uint8_t* dns = a.dns;
       gate[j] = 0.0f;
-      wb[j] = nullptr;
-      wbs[j] = nullptr;
+      wsl[j] = -1;
       if (v < k) {
         const int s = (s_raw[j] >= 0 && s_raw[j] < a.n_pool) ? s_raw[j] : -1;
         if (s >= 0) {
           dn = a.dn + (size_t)s * per;
           if (FMT == MC_MXFP4) dns = a.dns + (size_t)s * per_s;
           gate[j] = g_raw[j];
-          const int src = src_raw[j] < a.n_host ? src_raw[j] : -1;
-          if (src >= 0) {
-            wb[j] = const_cast<uint8_t*>(dn);
-            wbs[j] = const_cast<uint8_t*>(dns);
-            dn = a.f_dn + (size_t)src * per;
-            if (FMT == MC_MXFP4) dns = a.f_dns + (size_t)src * per_s;
+          if (src_raw[j] >= 0 && src_raw[j] < a.n_host) {
+            wsl[j] = s;
+            dn = a.f_dn + (size_t)src_raw[j] * per;
+            if (FMT == MC_MXFP4) dns = a.f_dns + (size_t)src_raw[j] * per_s;
           }
         }
       } else if (v == k && a.has_shared) {
@@ -434,150 +643,302 @@ down_kernel(DecodeArgs a) {
       for (int p = 0; p < PASSES; ++p)
 #pragma unroll
         for (int q = 0; q < CPLB; ++q) {
-          wv[j][p][q] = stream_load16(reinterpret_cast<const uint4*>(dn + (size_t)rowp[p] * row_bytes) + cq[q]);
+          wv[j][p][q] = stream_load16(dn + (size_t)rowp[p] * row_bytes + (size_t)cq[q] * 16);
           if (FMT == MC_MXFP4) sb[j][p][q] = dns[(size_t)rowp[p] * (I / 32) + cq[q]];
         }
     }
   };
 
-  {
-    // h of this token straight into LDS (global_load_lds, 1 KiB per wave instruction),
-    // then the first route group's rows: both sets of loads are in flight together.
-    // Float4 e of chunk c sits at LDS float4 c * E4 + (e ^ (c & (E4 - 1))): the lanes
-    // of a row, which read the same e of consecutive chunks, hit different banks, and
-    // each chunk still comes from one contiguous piece of global memory.
-    const int n4 = nvec * I / 4, r4 = I / 4;
-    for (int ch = wave; ch * 64 < n4; ch += 4) {
-      int i4 = ch * 64 + lane;
-      if (i4 >= n4) i4 = n4 - 1;                       // tail lanes re-read a valid vector
-      const int v = i4 / r4, sl = i4 % r4, c = sl / E4;
-      const int e = (c * E4 + ((sl % E4) ^ (c & (E4 - 1)))) * 4;
-      const float* src = v < k ? a.h_route + ((size_t)t * k + v) * I : a.h_shared + (size_t)t * I;
-      __builtin_amdgcn_global_load_lds(src + e, (__attribute__((address_space(3))) void*)(s_h + ch * 256),
-                                       16, 0, 0);
+  // h of this token straight into LDS (global_load_lds, 1 KiB per wave instruction),
+  // then the first route group's rows: both sets of loads are in flight together.
+  // Float4 e of chunk c sits at LDS float4 c * E4 + (e ^ (c & (E4 - 1))): the lanes of a
+  // row, which read the same e of consecutive chunks, hit different banks, and each
+  // chunk still comes from one contiguous piece of global memory.
+  const int n4 = nvec * I / 4, r4 = I / 4;
+  for (int ch = wave; ch * 64 < n4; ch += 4) {
+    int i4 = ch * 64 + lane;
+    if (i4 >= n4) i4 = n4 - 1;                       // tail lanes re-read a valid vector
+    const int v = i4 / r4, sl = i4 % r4, c = sl / E4;
+    const int e = (c * E4 + ((sl % E4) ^ (c & (E4 - 1)))) * 4;
+    __builtin_amdgcn_global_load_lds(a.h32 + (size_t)v * I + e,
+                                     (__attribute__((address_space(3))) void*)(s_h + ch * 256), 16, 0, 0);
+  }
+  const int nt = min(max(n_raw, 0), a.T);
+  if (nt == 0) {                                     // no valid token: the rows are zero
+    __builtin_amdgcn_s_waitcnt(0);
+    if (threadIdx.x < ROWS && r0 + (int)threadIdx.x < H) {
+      if (!a.accumulate) a.y[r0 + threadIdx.x] = 0.0f;
+      if (a.y_bf16) a.y_bf16[r0 + threadIdx.x] = 0;
     }
-    const int nt = min(max(n_raw, 0), a.T);
-    if (t >= nt) {                                     // a token beyond the valid count: its rows
-      __builtin_amdgcn_s_waitcnt(0);
-      if (threadIdx.x < ROWS && r0 + (int)threadIdx.x < H) {
-        const size_t o = (size_t)t * H + r0 + threadIdx.x;
-        if (!a.accumulate) a.y[o] = 0.0f;
-        if (a.y_bf16) a.y_bf16[o] = 0;
-      }
-      return;
-    }
-    if (n_groups > 0) load_group(wave);
-    __builtin_amdgcn_s_waitcnt(0);                     // the LDS copies have landed
-    __syncthreads();
+    return;
+  }
+  if (n_groups > 0) load_group(wave);
+  __builtin_amdgcn_s_waitcnt(0);                     // the LDS copies have landed
+  __syncthreads();
 
-    float acc[PASSES];
+  float acc[PASSES];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) acc[p] = 0.0f;
-    for (int g = 0; g < n_groups; ++g) {
-      const int v0 = wave + g * kGroup;
-      if (g > 0) load_group(v0);
+  for (int p = 0; p < PASSES; ++p) acc[p] = 0.0f;
+  for (int g = 0; g < n_groups; ++g) {
+    const int v0 = wave + g * kGroup;
+    if (g > 0) load_group(v0);
 #pragma unroll
-      for (int j = 0; j < kB_RoutesPerWave; ++j) {
-        const int v = v0 + 4 * j;
-        if (v >= nvec || gate[j] == 0.0f) continue;
+    for (int j = 0; j < kRoutesPerWave; ++j) {
+      const int v = v0 + 4 * j;
+      if (v >= nvec || gate[j] == 0.0f) continue;
 #pragma unroll
-        for (int q = 0; q < CPLB; ++q) {
-          float hv[ELEMS];
-          const float4* hs = reinterpret_cast<const float4*>(s_h + (size_t)v * I) + cq[q] * E4;
-          const int sw = cq[q] & (E4 - 1);
+      for (int q = 0; q < CPLB; ++q) {
+        float hv[ELEMS];
+        const float4* hs = reinterpret_cast<const float4*>(s_h + (size_t)v * I) + cq[q] * E4;
+        const int sw = cq[q] & (E4 - 1);
 #pragma unroll
-          for (int e = 0; e < E4; ++e) {
-            const float4 f = hs[e ^ sw];
-            hv[4 * e + 0] = f.x;
-            hv[4 * e + 1] = f.y;
-            hv[4 * e + 2] = f.z;
-            hv[4 * e + 3] = f.w;
-          }
-#pragma unroll
-          for (int p = 0; p < PASSES; ++p) {
-            const uint4 wq = okq[q] ? wv[j][p][q] : make_uint4(0, 0, 0, 0);
-            const float part = FMT == MC_MXFP4
-                                   ? dot_chunk_mx_f32(wq, e8m0_to_f32(sb[j][p][q]), hv, 0.0f)
-                                   : dot_chunk_bf_f32(wq, hv, 0.0f);
-            acc[p] = fmaf(gate[j], part, acc[p]);
-          }
+        for (int e = 0; e < E4; ++e) {
+          const float4 f = hs[e ^ sw];
+          hv[4 * e + 0] = f.x;
+          hv[4 * e + 1] = f.y;
+          hv[4 * e + 2] = f.z;
+          hv[4 * e + 3] = f.w;
         }
-      }
-      // fill-through: rows read from the host go into the slot (rows of this block)
-#pragma unroll
-      for (int j = 0; j < kB_RoutesPerWave; ++j) {
-        if (!wb[j]) continue;
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
-          const int rl = row_sub + RPP * p, row = r0 + rl;
-          if (rl >= ROWS || row >= H) continue;
-#pragma unroll
-          for (int q = 0; q < CPLB; ++q) {
-            if (!okq[q]) continue;
-            reinterpret_cast<uint4*>(wb[j] + (size_t)row * row_bytes)[cq[q]] = wv[j][p][q];
-            if (FMT == MC_MXFP4) wbs[j][(size_t)row * (I / 32) + cq[q]] = (uint8_t)sb[j][p][q];
-          }
+          const u32x4_t wq = okq[q] ? wv[j][p][q] : u32x4_t{0, 0, 0, 0};
+          const float part = FMT == MC_MXFP4 ? dot_chunk_mx_f32(wq, e8m0_to_f32(sb[j][p][q]), hv, 0.0f)
+                                             : dot_chunk_bf_f32(wq, hv, 0.0f);
+          acc[p] = fmaf(gate[j], part, acc[p]);
         }
       }
     }
+    // fill-through: rows read from the host go into the slot (rows of this block)
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const float sum = group_sum(acc[p], LPR);
-      const int rl = row_sub + RPP * p;
-      if (c_lane == 0 && lane_rows && rl < ROWS) s_part[wave][rl] = sum;
-    }
-    __syncthreads();
-    if (threadIdx.x < ROWS) {
-      const int row = r0 + threadIdx.x;
-      float v = ((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
-                s_part[3][threadIdx.x];
-      float* yp = a.y + (size_t)t * H + row;
-      if (a.accumulate) v += y_old;
-      *yp = v;
-      if (a.y_bf16) a.y_bf16[(size_t)t * H + row] = f32_to_bf16_rne(v);
+    for (int j = 0; j < kRoutesPerWave; ++j) {
+      if (wsl[j] < 0) continue;
+      uint8_t* wb = const_cast<uint8_t*>(a.dn) + (size_t)wsl[j] * per;
+      uint8_t* wbs = FMT == MC_MXFP4 ? const_cast<uint8_t*>(a.dns) + (size_t)wsl[j] * per_s : nullptr;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int rl = row_sub + RPP * p, row = r0 + rl;
+        if (rl >= ROWS || row >= H) continue;
+#pragma unroll
+        for (int q = 0; q < CPLB; ++q) {
+          if (!okq[q]) continue;
+          *reinterpret_cast<u32x4_t*>(wb + (size_t)row * row_bytes + (size_t)cq[q] * 16) = wv[j][p][q];
+          if (FMT == MC_MXFP4) wbs[(size_t)row * (I / 32) + cq[q]] = (uint8_t)sb[j][p][q];
+        }
+      }
     }
   }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const float sum = group_sum(acc[p], LPR);
+    const int rl = row_sub + RPP * p;
+    if (c_lane == 0 && lane_rows && rl < ROWS) s_part[wave][rl] = sum;
+  }
+  __syncthreads();
+  if (threadIdx.x < ROWS) {
+    const int row = r0 + threadIdx.x;
+    if (row < H) {
+      float v = ((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
+                s_part[3][threadIdx.x];
+      if (a.accumulate) v += y_old;
+      a.y[row] = v;
+      if (a.y_bf16) a.y_bf16[row] = f32_to_bf16_rne(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down, several tokens
+
+// Store visible to the other XCDs once this wave's stores have completed (coherent
+// write, no L2 write-back needed); read of such a value.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int FMT, int NSTEP>   // NSTEP: K steps covering all of I
+__global__ void __launch_bounds__(kThreads)
+down_unit_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_hv[];   // [2 tb][I]
+  __shared__ int32_t s_vec[kMaxRoutes];
+  __shared__ float s_gate[kMaxRoutes];
+  __shared__ int32_t s_n;
+  __shared__ uint32_t s_last;
+  const int u = blockIdx.x, rb = blockIdx.y;
+  const int H = a.H, I = a.I, k = a.k, n_all = a.T * k;
+  const int r0 = rb * kUnitRows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane & 15, g4 = lane >> 4;
+  const bool shared_unit = a.has_shared && u == n_all;
+  const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)I / 2 : (size_t)I * 2;
+  const size_t per = (size_t)H * row_bytes, per_s = (size_t)H * I / 32;
+  const int n_blk = I / 32;
+
+  int slot, win_slot, nt, nr;
+  if (column_unit(a, u, slot, win_slot, nt, nr)) {
+    const uint8_t* dn;
+    const uint8_t* dns = nullptr;
+    uint8_t* wb = nullptr;
+    uint8_t* wbs = nullptr;
+    if (shared_unit) {
+      dn = a.sh_dn;
+      dns = a.sh_dns;
+    } else {
+      dn = a.dn + (size_t)slot * per;
+      if (FMT == MC_MXFP4) dns = a.dns + (size_t)slot * per_s;
+      const int64_t src = a.f_dn ? fill_source(a, slot) : -1;
+      if (src >= 0) {
+        wb = const_cast<uint8_t*>(dn);
+        wbs = const_cast<uint8_t*>(dns);
+        dn = a.f_dn + (size_t)src * per;
+        if (FMT == MC_MXFP4) dns = a.f_dns + (size_t)src * per_s;
+      }
+    }
+    // the wave's 16-row tile over all of I, loaded once
+    const int prow = r0 + wave * 16 + rl;
+    const int row = min(prow, H - 1);
+    const uint8_t* wrow = dn + (size_t)row * row_bytes;
+    const uint8_t* srow = FMT == MC_MXFP4 ? dns + (size_t)row * (I / 32) : nullptr;
+    WFrag<FMT> f[NSTEP];
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      const int blk = 4 * s + g4;
+      wfrag_load<FMT>(f[s], wrow, srow, blk, blk < n_blk);
+    }
+    if (wave == 0) {
+      const int n = unit_vectors(a, u, slot, win_slot, nt, nr, s_vec);
+      for (int i = lane; i < n; i += 64) s_gate[i] = s_vec[i] < n_all ? a.w[s_vec[i]] : 1.0f;
+      if (lane == 0) s_n = n;
+    }
+    __syncthreads();
+    const int n_vec = s_n;
+    for (int b0 = 0; b0 < n_vec; b0 += a.tb) {
+      const int nb = min(a.tb, n_vec - b0);
+      stage_h(a, s_vec + b0, nb, s_hv, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0);                   // the LDS copies (and the rows) have landed
+      __syncthreads();
+      for (int t0 = 0; t0 < nb; t0 += kRouteTile) {
+        // product row R = 2 i + half for route t0 + i of the batch
+        const int R = 2 * t0 + rl;
+        const bool ok_r = R < 2 * nb;
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+          const int blk = 4 * s + g4;
+          const bool ok = blk < n_blk;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8_t av = (ok_r && ok) ? h_op(s_hv, R, blk, ks, I) : bf16x8_t{};
+            d = mfma(av, wfrag_op<FMT>(f[s], ks, ok), d);
+          }
+        }
+        // lane holds D[4 g4 + j][rl]: route t0 + 2 g4 (j = 0, 1) and t0 + 2 g4 + 1 (j = 2, 3)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = t0 + 2 * g4 + e;
+          if (i < nb && prow < H)
+            store_coherent(a.part + (size_t)s_vec[b0 + i] * H + prow,
+                           s_gate[b0 + i] * (d[2 * e] + d[2 * e + 1]));
+        }
+      }
+      __syncthreads();                                 // the batch's LDS is free again
+    }
+    if (wb && prow < H) {
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        const int blk = 4 * s + g4;
+        if (blk < n_blk)
+          wfrag_store<FMT>(f[s], wb + (size_t)prow * row_bytes,
+                           FMT == MC_MXFP4 ? wbs + (size_t)prow * (I / 32) : nullptr, blk);
+      }
+    }
+  }
+
+  // arrival: every column arrives once per row block; the last one sums the partials
+  __builtin_amdgcn_s_waitcnt(0);                       // this wave's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(a.cnt + (size_t)rb * kCntStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  nt = valid_tokens(a);
+  for (int i = threadIdx.x; i < a.T * kUnitRows; i += kThreads) {
+    const int t = i / kUnitRows, row = r0 + i % kUnitRows;
+    if (row >= H) continue;
+    const size_t o = (size_t)t * H + row;
+    if (t >= nt) {                                   // a token beyond the valid count
+      if (!a.accumulate) a.y[o] = 0.0f;
+      if (a.y_bf16) a.y_bf16[o] = 0;
+      continue;
+    }
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int r = t * k + j;
+      const int sl = a.slots[r];
+      const float v = load_coherent(a.part + (size_t)r * H + row);
+      sum += (sl >= 0 && sl < a.n_pool) ? v : 0.0f;
+    }
+    if (a.has_shared) sum += load_coherent(a.part + (size_t)(n_all + t) * H + row);
+    if (a.accumulate) sum = a.y[o] + sum;
+    a.y[o] = sum;
+    if (a.y_bf16) a.y_bf16[o] = f32_to_bf16_rne(sum);
+  }
+  if (threadIdx.x == 0) a.cnt[(size_t)rb * kCntStride] = 0u;
 }
 
 // ---------------------------------------------------------------- dispatch
 
-template <int FMT, int WR>
-static void launch_gate_up_w(const DecodeArgs& a, int cpl, dim3 grid, hipStream_t s) {
-  switch (cpl) {
-    case 1: hipLaunchKernelGGL((gate_up_kernel<FMT, 1, WR>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gate_up_kernel<FMT, 2, WR>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((gate_up_kernel<FMT, 4, WR>), grid, dim3(kThreads), 0, s, a); break;
+template <int FMT>
+static bool launch_gate_up(const DecodeArgs& a, int spw, dim3 grid, hipStream_t s) {
+  switch (spw) {
+    case 1: hipLaunchKernelGGL((gate_up_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((gate_up_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((gate_up_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a); return true;
+    case 8: hipLaunchKernelGGL((gate_up_kernel<FMT, 8>), grid, dim3(kThreads), 0, s, a); return true;
+    default: return false;
   }
 }
 
 template <int FMT>
-static void launch_gate_up(const DecodeArgs& a, int cpl, int wr, dim3 grid, hipStream_t s) {
-  if (wr == 2) launch_gate_up_w<FMT, 2>(a, cpl, grid, s);
-  else launch_gate_up_w<FMT, 4>(a, cpl, grid, s);
+static bool launch_gate_up_tok1(const DecodeArgs& a, int cpl, dim3 grid, hipStream_t s) {
+  switch (cpl) {
+    case 1: hipLaunchKernelGGL((gate_up_tok1_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((gate_up_tok1_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((gate_up_tok1_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a); return true;
+    default: return false;
+  }
 }
 
-template <int FMT, int LPR, int ROWS>
-static void launch_down_l(const DecodeArgs& a, int cplb, dim3 grid, size_t lds, hipStream_t s) {
-  if (cplb == 1)
-    hipLaunchKernelGGL((down_kernel<FMT, LPR, 1, ROWS>), grid, dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL((down_kernel<FMT, LPR, 2, ROWS>), grid, dim3(kThreads), lds, s, a);
+template <int FMT, int LPR>
+static bool launch_down_tok1_l(const DecodeArgs& a, int cplb, dim3 grid, size_t lds, hipStream_t s) {
+  if (cplb == 1) hipLaunchKernelGGL((down_tok1_kernel<FMT, LPR, 1, 8>), grid, dim3(kThreads), lds, s, a);
+  else if (cplb == 2) hipLaunchKernelGGL((down_tok1_kernel<FMT, LPR, 2, 8>), grid, dim3(kThreads), lds, s, a);
+  else return false;
+  return true;
 }
 
-// rows = 16 only with lpr 4 or 16 (the 64-lane row form keeps 8)
 template <int FMT>
-static void launch_down(const DecodeArgs& a, int lpr, int cplb, int rows, dim3 grid, size_t lds,
-                        hipStream_t s) {
+static bool launch_down_tok1(const DecodeArgs& a, int lpr, int cplb, dim3 grid, size_t lds, hipStream_t s) {
   switch (lpr) {
-    case 4:
-      if (rows == 16) launch_down_l<FMT, 4, 16>(a, cplb, grid, lds, s);
-      else launch_down_l<FMT, 4, 8>(a, cplb, grid, lds, s);
-      break;
-    case 16:
-      if (rows == 16) launch_down_l<FMT, 16, 16>(a, cplb, grid, lds, s);
-      else launch_down_l<FMT, 16, 8>(a, cplb, grid, lds, s);
-      break;
-    default: launch_down_l<FMT, 64, 8>(a, cplb, grid, lds, s); break;
+    case 4: return launch_down_tok1_l<FMT, 4>(a, cplb, grid, lds, s);
+    case 16: return launch_down_tok1_l<FMT, 16>(a, cplb, grid, lds, s);
+    default: return launch_down_tok1_l<FMT, 64>(a, cplb, grid, lds, s);
+  }
+}
+
+template <int FMT>
+static bool launch_down_unit(const DecodeArgs& a, int nstep, dim3 grid, size_t lds, hipStream_t s) {
+  switch (nstep) {
+    case 1: hipLaunchKernelGGL((down_unit_kernel<FMT, 1>), grid, dim3(kThreads), lds, s, a); return true;
+    case 2: hipLaunchKernelGGL((down_unit_kernel<FMT, 2>), grid, dim3(kThreads), lds, s, a); return true;
+    case 4: hipLaunchKernelGGL((down_unit_kernel<FMT, 4>), grid, dim3(kThreads), lds, s, a); return true;
+    case 8: hipLaunchKernelGGL((down_unit_kernel<FMT, 8>), grid, dim3(kThreads), lds, s, a); return true;
+    case 16: hipLaunchKernelGGL((down_unit_kernel<FMT, 16>), grid, dim3(kThreads), lds, s, a); return true;
+    default: return false;
   }
 }
 
@@ -587,19 +948,27 @@ static int pow2_at_least(int v) {
   return p;
 }
 
+static size_t round_kib(size_t b) { return (b + 1023) & ~(size_t)1023; }
+
 }  // namespace mc
 
 using namespace mc;
 
-// workspace: h of every route [T*k][I] and of the shared expert [T][I] (fp32), then
-// the routes' fill-through sources [T*k] (int32)
-static size_t ws_h_bytes(int32_t T, int32_t k, int32_t I) {
-  return ((size_t)T * k + (size_t)T) * (size_t)I * sizeof(float);
+// workspace: h as bf16 hi and lo halves of every vector [T*k + T][I] each (the
+// one-token path keeps fp32 h [T*k + T][I] in the same bytes), the gated partial
+// outputs [T*k + T][H] (fp32), the routes' fill-through sources [T*k] (int32), then the
+// several-token down pass's arrival counters
+static size_t ws_vec(int32_t T, int32_t k) { return (size_t)T * k + (size_t)T; }
+static size_t ws_h_bytes(int32_t T, int32_t k, int32_t I) { return ws_vec(T, k) * (size_t)I * 2; }
+static size_t ws_part_bytes(int32_t T, int32_t k, int32_t H) { return ws_vec(T, k) * (size_t)H * 4; }
+static size_t ws_rsrc_bytes(int32_t T, int32_t k) { return (((size_t)T * k * 4) + 15) & ~(size_t)15; }
+static size_t ws_cnt_bytes(int32_t H) {
+  return (size_t)((H + kUnitRows - 1) / kUnitRows) * kCntStride * sizeof(uint32_t);
 }
 
-extern "C" size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I) {
-  if (T < 0 || k < 0 || I < 0) return 0;
-  return ws_h_bytes(T, k, I) + (size_t)T * k * sizeof(int32_t);
+extern "C" size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t H, int32_t I) {
+  if (T < 0 || k < 0 || H < 0 || I < 0) return 0;
+  return 2 * ws_h_bytes(T, k, I) + ws_part_bytes(T, k, H) + ws_rsrc_bytes(T, k) + ws_cnt_bytes(H);
 }
 
 extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w,
@@ -622,30 +991,29 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
   MC_REQUIRE(accumulate == 0 || accumulate == 1, "moe_experts_decode: accumulate=%d", accumulate);
   if (T == 0) return MC_OK;
   MC_REQUIRE(x_bf16 && slots && w && y_acc && ws, "moe_experts_decode: NULL pointer");
-  MC_REQUIRE(ws_bytes >= moe_experts_decode_ws_bytes(T, k, pool->I),
+  MC_REQUIRE(ws_bytes >= moe_experts_decode_ws_bytes(T, k, pool->H, pool->I),
              "moe_experts_decode: workspace %zu < %zu bytes", ws_bytes,
-             moe_experts_decode_ws_bytes(T, k, pool->I));
+             moe_experts_decode_ws_bytes(T, k, pool->H, pool->I));
   MC_REQUIRE((uintptr_t)x_bf16 % 16 == 0 && (uintptr_t)ws % 16 == 0,
              "moe_experts_decode: x and ws must be 16-byte aligned");
   const int H = pool->H, I = pool->I, fmt = pool->fmt;
-  const int elems = fmt == MC_MXFP4 ? 32 : 8;
-  const int cpl = pow2_at_least((H / elems + 63) / 64);
-  if (cpl > 4) {
-    set_error("moe_experts_decode: H=%d too large", H);
-    return MC_EUNSUPPORTED;
-  }
-  const int chunks_b = I / elems;
-  const int lpr = chunks_b <= 4 ? 4 : (chunks_b <= 16 ? 16 : 64);
-  const int cplb = pow2_at_least((chunks_b + lpr - 1) / lpr);
-  if (cplb > 2) {
-    set_error("moe_experts_decode: I=%d too large", I);
-    return MC_EUNSUPPORTED;
-  }
   const int has_shared = shared ? 1 : 0;
-  const size_t lds = ((size_t)(k + has_shared) * I * sizeof(float) + 1023) & ~(size_t)1023;
-  if (lds > (size_t)kB_LdsBytes) {
-    set_error("moe_experts_decode: (k+1)*I*4 = %zu bytes of staged activations exceed %d", lds,
-              kB_LdsBytes);
+  // one token: dot-product kernels over whole row slices; several: MFMA kernels
+  const int elems = fmt == MC_MXFP4 ? 32 : 8;
+  const int cpl1 = pow2_at_least((H / elems + 63) / 64);
+  const int chunks_b = I / elems;
+  const int lpr1 = chunks_b <= 4 ? 4 : (chunks_b <= 16 ? 16 : 64);
+  const int cplb1 = pow2_at_least((chunks_b + lpr1 - 1) / lpr1);
+  const size_t lds1 = ((size_t)(k + has_shared) * I * sizeof(float) + 1023) & ~(size_t)1023;
+  // K steps of 128: the several-token gate_up splits H's steps over its 4 waves
+  const int nstep_gu = (H + kKS - 1) / kKS, nstep_dn = (I + kKS - 1) / kKS;
+  const int spw_gu = pow2_at_least((nstep_gu + 3) / 4);
+  const int tb = (int)std::min<size_t>(std::min<size_t>(64, (size_t)T * k + 1), kHLdsBytes / ((size_t)I * 4));
+  const size_t ldsn = round_kib((size_t)2 * tb * I * 2);
+  const bool tile_ok = T == 1 ? (cpl1 <= 4 && cplb1 <= 2 && lds1 <= (size_t)kTok1LdsBytes)
+                              : (spw_gu <= 8 && tb >= 1 && pow2_at_least(nstep_dn) <= 16);
+  if (!tile_ok) {
+    set_error("moe_experts_decode: H=%d I=%d k=%d T=%d is beyond this build's tiles", H, I, k, T);
     return MC_EUNSUPPORTED;
   }
 
@@ -669,13 +1037,20 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
     a.sh_dn = static_cast<const uint8_t*>(shared->down);
     a.sh_dns = static_cast<const uint8_t*>(shared->down_scale);
   }
-  a.h_route = static_cast<float*>(ws);
-  a.h_shared = a.h_route + (size_t)T * k * I;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  a.h32 = reinterpret_cast<float*>(wsb);
+  a.h_hi = reinterpret_cast<uint16_t*>(wsb);
+  a.h_lo = reinterpret_cast<uint16_t*>(wsb + ws_h_bytes(T, k, I));
+  a.part = reinterpret_cast<float*>(wsb + 2 * ws_h_bytes(T, k, I));
+  a.rsrc = reinterpret_cast<int32_t*>(wsb + 2 * ws_h_bytes(T, k, I) + ws_part_bytes(T, k, H));
+  a.cnt = reinterpret_cast<uint32_t*>(wsb + 2 * ws_h_bytes(T, k, I) + ws_part_bytes(T, k, H) +
+                                      ws_rsrc_bytes(T, k));
+  a.n_cnt = T == 1 ? 0 : (H + kUnitRows - 1) / kUnitRows;
+  a.tb = tb;
   a.y = y_acc;
   a.y_bf16 = static_cast<uint16_t*>(y_bf16);
   a.accumulate = accumulate;
   a.has_shared = has_shared;
-  a.rsrc = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + ws_h_bytes(T, k, I));
   if (fill) {
     if ((rc = check_banks(fill->host, "moe_experts_decode fill host")) != MC_OK) return rc;
     MC_REQUIRE(fill->host->fmt == fmt && fill->host->H == H && fill->host->I == I,
@@ -698,20 +1073,35 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
     if (a.kcap == 0) a.f_gu = a.f_dn = nullptr;
   }
 
-  const int wr = T == 1 ? 2 : 4;
-  const int rows = (T >= 4 && lpr != 64) ? 16 : 8;
-  dim3 grid_a(T * k + has_shared, I / (4 * wr));
-  if (fmt == MC_MXFP4)
-    launch_gate_up<MC_MXFP4>(a, cpl, wr, grid_a, s);
-  else
-    launch_gate_up<MC_BF16>(a, cpl, wr, grid_a, s);
+  bool ok_a, ok_b;
+  if (T == 1) {
+    const dim3 grid_a(k + has_shared, I / 8);
+    ok_a = fmt == MC_MXFP4 ? launch_gate_up_tok1<MC_MXFP4>(a, cpl1, grid_a, s)
+                           : launch_gate_up_tok1<MC_BF16>(a, cpl1, grid_a, s);
+  } else {
+    const dim3 grid_a(T * k + has_shared, I / 16);
+    ok_a = fmt == MC_MXFP4 ? launch_gate_up<MC_MXFP4>(a, spw_gu, grid_a, s)
+                           : launch_gate_up<MC_BF16>(a, spw_gu, grid_a, s);
+  }
+  if (!ok_a) {
+    set_error("moe_experts_decode: no gate_up tile for H=%d", H);
+    return MC_EUNSUPPORTED;
+  }
   MC_LAUNCH_CHECK();
   if (fill && fill->down_after) MC_HIP(hipStreamWaitEvent(s, fill->down_after, 0));
-  dim3 grid_b((H + rows - 1) / rows, T);
-  if (fmt == MC_MXFP4)
-    launch_down<MC_MXFP4>(a, lpr, cplb, rows, grid_b, lds, s);
-  else
-    launch_down<MC_BF16>(a, lpr, cplb, rows, grid_b, lds, s);
+  if (T == 1) {
+    const dim3 grid_b((H + 7) / 8);
+    ok_b = fmt == MC_MXFP4 ? launch_down_tok1<MC_MXFP4>(a, lpr1, cplb1, grid_b, lds1, s)
+                           : launch_down_tok1<MC_BF16>(a, lpr1, cplb1, grid_b, lds1, s);
+  } else {
+    const dim3 grid_b(T * k + has_shared, (H + kUnitRows - 1) / kUnitRows);
+    ok_b = fmt == MC_MXFP4 ? launch_down_unit<MC_MXFP4>(a, pow2_at_least(nstep_dn), grid_b, ldsn, s)
+                           : launch_down_unit<MC_BF16>(a, pow2_at_least(nstep_dn), grid_b, ldsn, s);
+  }
+  if (!ok_b) {
+    set_error("moe_experts_decode: no down tile for I=%d", I);
+    return MC_EUNSUPPORTED;
+  }
   MC_LAUNCH_CHECK();
   return MC_OK;
 }

@@ -76,6 +76,9 @@ int host_forget(const void* p, size_t bytes);
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // e8m0 exponent byte -> fp32 scale 2^(X-127) (X = 0 gives 2^-127, a subnormal).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t X) {
@@ -92,6 +95,18 @@ __device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t v, float scale) {
 template <int SEL>
 __device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t v, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, SEL);
+}
+
+// 8 consecutive MXFP4 elements (one dword of codes) -> bf16x8, scaled (exact).
+__device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t v, float s) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

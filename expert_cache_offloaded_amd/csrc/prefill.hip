@@ -33,11 +33,8 @@
 
 namespace mc {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kP_BM = 64;          // rows per tile
 constexpr int kP_KS = 128;         // K per pipeline step
@@ -225,18 +222,7 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return (b & 7) * per + (b >> 3);
 }
 
-// 8 consecutive MXFP4 elements (one dword of codes) -> bf16x8 / f16x8, scaled.
-__device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t v, float s) {
-  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0);
-  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1);
-  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2);
-  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3);
-  bf16x8_t r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
+// 8 consecutive MXFP4 elements (one dword of codes) -> f16x8, scaled.
 __device__ __forceinline__ f16x8_t fp4x8_f16(uint32_t v, float s) {
   const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 0);
   const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, s, 1);

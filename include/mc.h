@@ -269,9 +269,10 @@ typedef struct {
 } mc_fill_list;
 
 /*
- * Workspace bytes of moe_experts_decode for up to T tokens x k routes.
+ * Workspace bytes of moe_experts_decode for up to T tokens x k routes of experts with
+ * hidden size H and intermediate size I.
  */
-size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I);
+size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t H, int32_t I);
 
 /*
  * Slot-indirected SwiGLU experts and gated combine on the GPU
@@ -288,16 +289,18 @@ size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t I);
  *              so a layer with no host branch needs no separate rounding pass.
  *   pool       device slot banks; shared: NULL or a device bank whose entry 0 is the
  *              layer's shared expert (same fmt, H, I).
- *   ws         device workspace of moe_experts_decode_ws_bytes(T, k, I) bytes (the
- *              gate_up results h and each route's weight source), 16-byte aligned;
- *              one workspace per call in flight.
+ *   ws         device workspace of moe_experts_decode_ws_bytes(T, k, H, I) bytes (the
+ *              gate_up results h, each route's gated partial output and the down pass's
+ *              arrival counters), 16-byte aligned; one workspace per call in flight (two
+ *              calls that overlap on one workspace race).
  *   fill       NULL (every routed slot is resident), or the fill list of this call's
  *              lookup (mc_fill_list): those slots are read from the host and written
- *              in the same pass, so no separate mc_fill_slots is needed.  With T > 1 a
- *              filled expert's down rows are read from the host once per token that
- *              routes to it.
- * Two kernel launches (gate_up + SwiGLU, then down + combine).  Needs H % 64 == 0,
- * I % 64 == 0, T <= 64, T*k <= 1024, (k + 1) * I * 4 <= 64 KiB.
+ *              in the same pass, so no separate mc_fill_slots is needed.
+ * Two kernel launches, both unit-major (a unit = one distinct slot, or the shared
+ * expert): gate_up + SwiGLU, then down, where each unit's rows produce every route's
+ * gated partial for a block of rows and the last unit to finish a block adds the
+ * partials of each token in route order (a fixed order: results are run-to-run
+ * identical).  Needs H % 64 == 0, I % 64 == 0, T <= 64, T*k <= 1024.
  */
 int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w, int32_t T,
                        int32_t k, const int32_t* n_tok, const mc_banks* pool,

@@ -67,7 +67,7 @@ def _run_decode(cfg, case, nt=None):
     x = t_of(case["x"]).cuda()
     slots = torch.from_numpy(case["slots"]).cuda()
     w = torch.from_numpy(case["w"]).cuda()
-    ws = torch.zeros(decode_ws_bytes(T, cfg.k, cfg.I) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(decode_ws_bytes(T, cfg.k, cfg.H, cfg.I) // 4, dtype=torch.float32, device="cuda")
     y = torch.full((T, cfg.H), 7.0, dtype=torch.float32, device="cuda")    # overwritten
     ntt = None
     if nt is not None:
