@@ -87,6 +87,9 @@ _SIGS = {
     "moe_experts_decode_ws_bytes": (C.c_size_t, [_I32, _I32, _I32, _I32]),
     "moe_experts_decode": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
                                      _P, C.c_size_t, _P, _I32, _P, _P, C.POINTER(FillList)]),
+    "moe_experts_decode_noalloc": (C.c_int, [_P, _P, _P, _I32, _I32, _P, C.POINTER(Banks), C.POINTER(Banks),
+                                             _P, _I32, _P, _P, C.POINTER(FillList)]),
+    "moe_experts_decode_noalloc_max_bytes": (C.c_size_t, []),
     "mc_prefill_sort_routes": (C.c_int, [_P, _I32, _I32, _P, _I32, _P, C.c_size_t, _P, _P, _P, _P]),
     "moe_experts_prefill_ws_bytes": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "moe_experts_prefill": (C.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, C.POINTER(Banks), _P, C.c_size_t,
@@ -270,6 +273,20 @@ def moe_experts_decode(x, slots, w, n_tok, pool: Banks, shared: Optional[Banks],
         _ptr(y_acc), accumulate, _ptr(y_bf16), _stream(stream),
         C.byref(fill) if fill is not None else None))
 
+
+def moe_experts_decode_noalloc(x, slots, w, n_tok, pool: Banks, shared: Optional[Banks], y_acc,
+                               accumulate: int = 1, y_bf16=None, stream=None,
+                               fill: Optional[FillList] = None) -> None:
+    """moe_experts_decode with the library's own scratch array as workspace (no allocation)."""
+    T, k = slots.shape
+    _check("moe_experts_decode_noalloc", lib().moe_experts_decode_noalloc(
+        _ptr(x), _ptr(slots), _ptr(w), T, k, _ptr(n_tok), C.byref(pool),
+        C.byref(shared) if shared is not None else None, _ptr(y_acc), accumulate, _ptr(y_bf16),
+        _stream(stream), C.byref(fill) if fill is not None else None))
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(lib().moe_experts_decode_noalloc_max_bytes())
 
 
 def finish_bf16(y_acc, n_tok, y_bf16, stream=None) -> None:

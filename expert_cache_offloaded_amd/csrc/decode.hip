@@ -34,6 +34,7 @@
 // link) and stores them into the slot from the registers that hold them, so the fill
 // and the expert pass are one stream of loads.
 #include <algorithm>
+#include <mutex>
 
 #include "mc_common.h"
 
@@ -971,12 +972,10 @@ extern "C" size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t H, i
   return 2 * ws_h_bytes(T, k, I) + ws_part_bytes(T, k, H) + ws_rsrc_bytes(T, k) + ws_cnt_bytes(H);
 }
 
-extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w,
-                                  int32_t T, int32_t k, const int32_t* n_tok,
-                                  const mc_banks* pool, const mc_banks* shared, void* ws,
-                                  size_t ws_bytes, float* y_acc, int32_t accumulate, void* y_bf16,
-                                  hipStream_t s, const mc_fill_list* fill) {
-  clear_error();
+static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w, int32_t T, int32_t k,
+                       const int32_t* n_tok, const mc_banks* pool, const mc_banks* shared, void* ws,
+                       size_t ws_bytes, float* y_acc, int32_t accumulate, void* y_bf16, hipStream_t s,
+                       const mc_fill_list* fill) {
   int rc;
   if ((rc = check_banks(pool, "moe_experts_decode pool")) != MC_OK) return rc;
   if (shared) {
@@ -1104,4 +1103,75 @@ extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, cons
   }
   MC_LAUNCH_CHECK();
   return MC_OK;
+}
+
+extern "C" int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w,
+                                  int32_t T, int32_t k, const int32_t* n_tok,
+                                  const mc_banks* pool, const mc_banks* shared, void* ws,
+                                  size_t ws_bytes, float* y_acc, int32_t accumulate, void* y_bf16,
+                                  hipStream_t s, const mc_fill_list* fill) {
+  clear_error();
+  return decode_impl(x_bf16, slots, w, T, k, n_tok, pool, shared, ws, ws_bytes, y_acc, accumulate, y_bf16, s,
+                     fill);
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+//
+// The workspace of moe_experts_decode_noalloc lives in this file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (in host code it is only a stand-in for the symbol): the device
+// address of each GPU's copy is looked up once, with that GPU current, and kept.
+// Every call on a GPU shares that GPU's copy and leaves the last call's contents in it;
+// no part of it needs to start at zero (the kernels write every word they later read,
+// and the arrival counters are cleared by the first kernel of each call), and calls that
+// overlap on one GPU race on it.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// Device address of this GPU's scratch array (looked up on the first call per GPU).
+static int scratch_for_current_device(void** out) {
+  int dev = -1;
+  MC_HIP(hipGetDevice(&dev));
+  MC_REQUIRE(dev >= 0 && dev < kMaxDevices, "moe_experts_decode_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    MC_REQUIRE(p != nullptr, "moe_experts_decode_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MC_OK;
+}
+
+extern "C" size_t moe_experts_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int moe_experts_decode_noalloc(const void* x_bf16, const int32_t* slots, const float* w,
+                                          int32_t T, int32_t k, const int32_t* n_tok,
+                                          const mc_banks* pool, const mc_banks* shared, float* y_acc,
+                                          int32_t accumulate, void* y_bf16, hipStream_t s,
+                                          const mc_fill_list* fill) {
+  clear_error();
+  int rc;
+  if ((rc = check_banks(pool, "moe_experts_decode_noalloc pool")) != MC_OK) return rc;
+  MC_REQUIRE(T >= 0 && k >= 1, "moe_experts_decode_noalloc: T=%d k=%d", T, k);
+  const size_t need = moe_experts_decode_ws_bytes(T, k, pool->H, pool->I);
+  if (need > kScratchBytes) {
+    set_error("moe_experts_decode_noalloc: T=%d k=%d H=%d I=%d needs %zu bytes of workspace, beyond the "
+              "%zu-byte scratch array (use moe_experts_decode with a workspace)",
+              T, k, pool->H, pool->I, need, kScratchBytes);
+    return MC_ENOMEM;
+  }
+  if (T == 0) return decode_impl(x_bf16, slots, w, T, k, n_tok, pool, shared, nullptr, 0, y_acc, accumulate,
+                                 y_bf16, s, fill);
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws)) != MC_OK) return rc;
+  return decode_impl(x_bf16, slots, w, T, k, n_tok, pool, shared, ws, kScratchBytes, y_acc, accumulate, y_bf16,
+                     s, fill);
 }

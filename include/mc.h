@@ -308,6 +308,27 @@ int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w,
                        int32_t accumulate, void* y_bf16, hipStream_t s, const mc_fill_list* fill);
 
 
+/*
+ * moe_experts_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under hipGraph capture that must not call hipMalloc, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results and
+ * kernels as moe_experts_decode; the workspace is a file-scope device array of the
+ * library, moe_experts_decode_noalloc_max_bytes() bytes (4 MiB) per GPU, held until the
+ * process ends.  Nothing is allocated by the call (no hipMalloc, no allocating library
+ * routine); the array's device address is looked up once per GPU on its first call.
+ * A call whose moe_experts_decode_ws_bytes(T, k, H, I) exceeds the array returns
+ * MC_ENOMEM with a message (nothing is enqueued).  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents (no part of it needs clearing):
+ * calls that overlap on one GPU — on two streams, or from two threads — race and must
+ * be ordered by the caller.
+ */
+int moe_experts_decode_noalloc(const void* x_bf16, const int32_t* slots, const float* w, int32_t T,
+                               int32_t k, const int32_t* n_tok, const mc_banks* pool,
+                               const mc_banks* shared, float* y_acc, int32_t accumulate,
+                               void* y_bf16, hipStream_t s, const mc_fill_list* fill);
+/* Size of the array moe_experts_decode_noalloc works in (bytes). */
+size_t moe_experts_decode_noalloc_max_bytes(void);
+
 /* ------------------------------------------------------------------------- */
 /* Prefill                                                                   */
 /* ------------------------------------------------------------------------- */

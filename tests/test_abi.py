@@ -146,3 +146,22 @@ def test_host_forget_needs_no_gpu():
     assert _lib.host_forget(C.addressof(buf), 64) == 0
     with pytest.raises(_lib.McError):
         _lib.host_forget(0, 0)
+
+
+def test_noalloc_rejects_oversized_calls_without_a_gpu():
+    """moe_experts_decode_noalloc checks the workspace a call needs against its scratch
+    array before anything is enqueued: a call beyond it fails with MC_ENOMEM."""
+    from expert_cache_offloaded_amd import _lib
+    lib = _lib.lib()
+    assert lib.moe_experts_decode_noalloc_max_bytes() == 4 << 20
+    buf = C.create_string_buffer(4096 + 16)
+    base = (C.addressof(buf) + 15) & ~15
+    b = _lib.Banks()
+    b.fmt, b.H, b.I, b.n = _lib.MC_MXFP4, 4096, 2048, 1
+    b.gate_up = b.gate_up_scale = b.down = b.down_scale = base
+    need = lib.moe_experts_decode_ws_bytes(64, 16, 4096, 2048)
+    assert need > 4 << 20
+    rc = lib.moe_experts_decode_noalloc(base, base, base, 64, 16, None, C.byref(b), None, base, 0, None,
+                                        None, None)
+    assert rc == _lib.MC_ENOMEM
+    assert "scratch array" in _lib.last_error()
