@@ -94,6 +94,7 @@ _SIGS = {
     "moe_experts_prefill_ws_bytes": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "moe_experts_prefill": (C.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, C.POINTER(Banks), _P, C.c_size_t,
                                       _P, _P, C.POINTER(Prefetch)]),
+    "moe_experts_prefill_status": (C.c_int, [_P, _P, C.POINTER(C.c_uint32)]),
     "mc_host_pool_create": (_P, [_I32, _P]),
     "mc_host_pool_destroy": (None, [_P]),
     "mc_host_experts": (C.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, C.POINTER(Banks), _P]),
@@ -300,6 +301,13 @@ def prefill_sort_routes(ids, n_tok, E: int, ws, counts, offsets, perm, stream=No
     _check("mc_prefill_sort_routes", lib().mc_prefill_sort_routes(
         _ptr(ids), T, k, _ptr(n_tok), E, _ptr(ws), ws.numel() * ws.element_size(), _ptr(counts),
         _ptr(offsets), _ptr(perm), _stream(stream)))
+
+
+def prefill_status(ws, stream=None):
+    """(rc, status bits) of the last moe_experts_prefill on workspace ws (synchronises)."""
+    st = C.c_uint32(0)
+    rc = lib().moe_experts_prefill_status(_ptr(ws), _stream(stream), C.byref(st))
+    return rc, int(st.value)
 
 
 def prefill_ws_bytes(T: int, k: int, E: int, H: int, I: int) -> int:

@@ -45,7 +45,12 @@ constexpr int kP_LdsRow = kP_KS + 8;   // padded LDS row (elements)
 constexpr int kP_MaxE = 1024;
 constexpr int kP_MaxK = 8192;      // largest H or I (sizes the generic kernel's scale table)
 
+// Status bits of a prefill call (the workspace's first word, cleared by the call's first
+// kernel): an h value beyond the fp16 range (it became +-inf in the down GEMM's input).
+constexpr uint32_t kStatusHOverflow = 1u;
+
 struct PrefillWs {
+  uint32_t* status;     // [1] kStatus* bits of the last call
   int32_t* counts;      // [E]
   int32_t* counts4;     // [E][4] per-wave counts
   int32_t* offsets;     // [E+1]
@@ -66,6 +71,8 @@ static size_t ws_layout(int T, int k, int E, int H, int I, PrefillWs* w, uint8_t
   };
   const size_t nr = (size_t)T * k;
   uint8_t* p;
+  p = take(sizeof(uint32_t));
+  if (w) w->status = (uint32_t*)p;
   p = take((size_t)E * 4);
   if (w) w->counts = (int32_t*)p;
   p = take((size_t)E * 16);
@@ -97,7 +104,9 @@ constexpr int kSortBatch = 8;
 // 1. per-expert route counts, per wave quarter (ballot + popcount, no atomics)
 __global__ void __launch_bounds__(256)
 sort_count_kernel(const int32_t* __restrict__ ids, int T, int k, const int32_t* __restrict__ n_tok,
-                  int E, int32_t* __restrict__ counts, int32_t* __restrict__ counts4) {
+                  int E, int32_t* __restrict__ counts, int32_t* __restrict__ counts4,
+                  uint32_t* __restrict__ status) {
+  if (status && blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
   const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nr = route_count(n_tok, T, k);
   const int q = (nr + 3) / 4, r0 = wave * q, r1 = min(nr, r0 + q);
@@ -267,6 +276,7 @@ prefill_gemm_kernel(PrefillArgs a) {
   constexpr int SROW = scale_row_bytes(NSTEPS);
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kP_StageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sS[kP_Threads * SROW];
+  __shared__ int s_shift[kP_Threads];            // down: power-of-two shift of each weight row
   int e, row0, nrows, nb;
   if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -328,6 +338,7 @@ prefill_gemm_kernel(PrefillArgs a) {
   // is placed in scratch memory
   GemmStage st0, st1, st2;
   u32x4_t ar0[4], ar1[4], ar2[4];
+  int shf[4] = {0, 0, 0, 0};                     // down: the shift of the lane's 4 weight rows
   auto issue_a = [&](int s, u32x4_t* ar) {
     const int k0 = s * kP_KS;
 #pragma unroll
@@ -357,7 +368,7 @@ prefill_gemm_kernel(PrefillArgs a) {
       // would wait for that load within the step that issued it
       uint32_t raw = g.s[nt];
       asm volatile("" : "+v"(raw));
-      sc[nt] = e8m0_to_f32(raw);
+      sc[nt] = MODE == 0 ? e8m0_to_f32(raw) : ldexpf(1.0f, (int)raw - 127 - shf[nt]);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -416,15 +427,40 @@ prefill_gemm_kernel(PrefillArgs a) {
   {
     uint8_t* dst = sS + tid * SROW;
     const int swt = ((tid & 15) * SROW) >> 8;
+    uint32_t xmin = 255, xmax = 0;               // the row's smallest and largest block exponent
+    auto minmax4 = [&](uint32_t v) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t x = (v >> (8 * b)) & 0xFFu;
+        xmin = min(xmin, x);
+        xmax = max(xmax, x);
+      }
+    };
     if ((nsteps & 3) == 0) {
-      for (int c = 0; c < (nsteps >> 2); ++c)
-        *reinterpret_cast<u32x4_t*>(dst + ((c ^ swt) << 4)) =
-            *reinterpret_cast<const u32x4_t*>(srow_g + c * 16);
+      for (int c = 0; c < (nsteps >> 2); ++c) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(srow_g + c * 16);
+        *reinterpret_cast<u32x4_t*>(dst + ((c ^ swt) << 4)) = v;
+        if (MODE == 1) {
+          minmax4(v[0]);
+          minmax4(v[1]);
+          minmax4(v[2]);
+          minmax4(v[3]);
+        }
+      }
     } else {
-      for (int d = 0; d < nsteps; ++d)
-        *reinterpret_cast<uint32_t*>(dst + (((d >> 2) ^ swt) << 4) + ((d & 3) << 2)) =
-            *reinterpret_cast<const uint32_t*>(srow_g + d * 4);
+      for (int d = 0; d < nsteps; ++d) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(srow_g + d * 4);
+        *reinterpret_cast<uint32_t*>(dst + (((d >> 2) ^ swt) << 4) + ((d & 3) << 2)) = v;
+        if (MODE == 1) minmax4(v);
+      }
     }
+    // fp16 holds e2m1 * 2^e exactly for e in [-23, 13]; a row with a block outside is
+    // dequantised at 2^-shift (its largest block at 2^13) and its outputs are scaled
+    // back by 2^shift in the epilogue.  Blocks more than 36 binades below the row's
+    // largest one then round in fp16; their share of an output is below 2^-32 of the
+    // largest block's, under the fp32 accumulation's own rounding.
+    if (MODE == 1)
+      s_shift[tid] = ((int)xmin - 127 >= -23 && (int)xmax - 127 <= 13) ? 0 : (int)xmax - 140;
   }
   issue_a(0, ar0);
   issue_w(0, st0);
@@ -435,6 +471,10 @@ prefill_gemm_kernel(PrefillArgs a) {
   if (nsteps > 2) issue_a(2, ar2);
   store_a(ar0, 0);
   __syncthreads();
+  if (MODE == 1) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) shf[nt] = s_shift[wave * 64 + nt * 16 + (lane & 15)];
+  }
   scales(0, st0);
   if (nsteps > 1) scales(1, st1);
   if (NSTEPS > 0) {
@@ -445,7 +485,8 @@ prefill_gemm_kernel(PrefillArgs a) {
   }
 
   if (MODE == 0) {
-    // h = silu(g) * u -> fp16, rows of this tile
+    // h = silu(g) * u -> fp16, rows of this tile; a value beyond fp16's range is flagged
+    bool h_over = false;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -456,9 +497,12 @@ prefill_gemm_kernel(PrefillArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const float g = acc[mt][nt][j], u = acc[mt][nt + 2][j];
-          hrow[c0 + nt * 16 + (lane & 15)] = (_Float16)(silu(g) * u);
+          const _Float16 hv = (_Float16)(silu(g) * u);
+          h_over |= __builtin_isinf((float)hv);
+          hrow[c0 + nt * 16 + (lane & 15)] = hv;
         }
       }
+    if (__ballot(h_over) && lane == 0) atomicOr(a.ws.status, kStatusHOverflow);
   } else {
     // the route's own output row, scaled by its gate
 #pragma unroll
@@ -471,7 +515,7 @@ prefill_gemm_kernel(PrefillArgs a) {
         const float g = a.w[route];
         float* yrow = a.ws.yr + (size_t)route * H;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) yrow[c0 + nt * 16 + (lane & 15)] = g * acc[mt][nt][j];
+        for (int nt = 0; nt < 4; ++nt) yrow[c0 + nt * 16 + (lane & 15)] = ldexpf(g * acc[mt][nt][j], shf[nt]);
       }
   }
 }
@@ -529,7 +573,7 @@ prefill_combine_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int
 static int sort_launch(const int32_t* ids, int T, int k, const int32_t* n_tok, int E,
                        const PrefillWs& w, hipStream_t s) {
   hipLaunchKernelGGL(sort_count_kernel, dim3(E), dim3(256), 0, s, ids, T, k, n_tok, E, w.counts,
-                     w.counts4);
+                     w.counts4, w.status);
   hipLaunchKernelGGL(sort_plan_kernel, dim3(1), dim3(1024), 0, s, E, w.counts, w.offsets,
                      w.mtile_off);
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(E), dim3(256), 0, s, ids, T, k, n_tok, E, w.counts4,
@@ -658,5 +702,23 @@ extern "C" int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)gc), dim3(256), 0, s, ids, T, k, E, H,
                      n_tok, pw.yr, static_cast<uint16_t*>(y_bf16));
   MC_LAUNCH_CHECK();
+  return MC_OK;
+}
+
+extern "C" int moe_experts_prefill_status(const void* ws, hipStream_t s, uint32_t* status) {
+  clear_error();
+  MC_REQUIRE(ws && status, "moe_experts_prefill_status: NULL pointer");
+  MC_REQUIRE((uintptr_t)ws % 16 == 0, "moe_experts_prefill_status: ws must be 16-byte aligned");
+  MC_HIP(hipStreamSynchronize(s));
+  PrefillWs pw{};
+  ws_layout(0, 1, 1, 0, 0, &pw, const_cast<uint8_t*>(static_cast<const uint8_t*>(ws)));
+  uint32_t v = 0;
+  MC_HIP(hipMemcpy(&v, pw.status, sizeof v, hipMemcpyDeviceToHost));
+  *status = v;
+  if (v & kStatusHOverflow) {
+    set_error("moe_experts_prefill: an activation h = silu(g) * u exceeded the fp16 range of the down "
+              "GEMM's input (the affected outputs are not exact)");
+    return MC_EDEVICE;
+  }
   return MC_OK;
 }

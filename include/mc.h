@@ -371,9 +371,15 @@ size_t moe_experts_prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, 
  * Prefill MoE layer over a resident layer buffer (entry e = expert e of the layer):
  *   y[t] = bf16_rne( sum_j w[t][j] * Expert_{ids[t][j]}(x[t]) )   for t < *n_tok (else 0)
  * computed as a stable token sort by expert, a grouped gate_up GEMM with the SwiGLU
- * epilogue (bf16 MFMA; MXFP4 -> bf16 is exact), a grouped down GEMM (fp16 h and
- * MXFP4 -> fp16 weights, exact for block exponents X-127 in [-23, 13]; fp16 MFMA),
- * fp32 accumulation, and a fixed-order sum of each token's k gated route outputs.
+ * epilogue (bf16 MFMA; MXFP4 -> bf16 is exact), a grouped down GEMM (fp16 MFMA on fp16
+ * h and MXFP4 -> fp16 weights), fp32 accumulation, and a fixed-order sum of each token's
+ * k gated route outputs.  W_down is consumed exactly: a row whose block exponents X-127
+ * leave fp16's exact range [-23, 13] is dequantised at a power-of-two offset that the
+ * epilogue undoes (blocks more than 36 binades below the row's largest then round, a
+ * share of the output below the fp32 accumulation's own rounding).  h is held in fp16:
+ * a value beyond +-65504 becomes +-inf and is recorded in the workspace's status word
+ * (moe_experts_prefill_status); values below fp16's normal range keep an absolute
+ * error under 2^-25.
  * If next != NULL the next layer's prefetch (see mc_prefetch) is enqueued first on
  * its own stream, so it overlaps this layer's compute.
  *   x bf16 [T][H], ids int32 [T][k] (expert-in-layer; invalid ids contribute nothing),
@@ -384,6 +390,13 @@ int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const float* w, 
                         int32_t k, const int32_t* n_tok, int32_t E, const mc_banks* layer_buf,
                         void* ws, size_t ws_bytes, void* y_bf16, hipStream_t s,
                         const mc_prefetch* next);
+
+/*
+ * Status of the last moe_experts_prefill call made with workspace ws: waits for stream
+ * s, then *status = the call's status bits (1: an h value exceeded the fp16 range).
+ * Returns MC_EDEVICE with a message when a bit is set, MC_OK otherwise.  Synchronous.
+ */
+int moe_experts_prefill_status(const void* ws, hipStream_t s, uint32_t* status);
 
 /* ------------------------------------------------------------------------- */
 /* Hybrid split / merge and the host branch                                  */

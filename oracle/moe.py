@@ -29,7 +29,8 @@ from .formats import bf16_to_f64, expert_matrices
 
 
 def _silu(z: np.ndarray) -> np.ndarray:
-    return z / (1.0 + np.exp(-z))
+    with np.errstate(over="ignore"):          # exp(-z) -> inf for z << 0 gives the limit -0
+        return z / (1.0 + np.exp(-z))
 
 
 def expert_ffn(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, x: np.ndarray) -> np.ndarray:

@@ -180,6 +180,26 @@ def expert_weights(cfg: Config, flat: int, tag: int = _TAG_ROUTED) -> Dict[str, 
     return {"gate_up": gu, "gate_up_scale": gus, "down": dn, "down_scale": dns}
 
 
+def exponent_variant(cfg: Config, flat: int, gu_bases: Sequence[int], dn_bases: Sequence[int],
+                     spread: int = 2, tag: int = _TAG_ROUTED) -> Dict[str, np.ndarray]:
+    """An MXFP4 expert whose block exponents sit at chosen places of the e8m0 range
+    (inputs for tests of the format's edges, not a workload).  The codes are those of
+    ``expert_weights``; row r of the gate_up bank takes the base exponent
+    gu_bases[r % len(gu_bases)], row r of the down bank dn_bases[r % len(dn_bases)], and
+    each 32-element block of a row gets X - 127 = base - d with d uniform in [0, spread]
+    (seeded), X clamped to [0, 254]."""
+    if cfg.fmt != "mxfp4":
+        raise ValueError("exponent_variant needs MXFP4 experts")
+    w = expert_weights(cfg, flat, tag)
+    r = _rng(cfg.seed, tag, flat, 7)
+    for name, bases in (("gate_up_scale", gu_bases), ("down_scale", dn_bases)):
+        rows, blocks = w[name].shape
+        base = np.array([bases[i % len(bases)] for i in range(rows)], dtype=np.int64)[:, None]
+        x = 127 + base - r.integers(0, spread + 1, size=(rows, blocks))
+        w[name] = np.clip(x, 0, 254).astype(np.uint8)
+    return w
+
+
 def shared_weights(cfg: Config, layer: int) -> Dict[str, np.ndarray]:
     """The always-on shared expert of one layer (same format and shape as a routed one)."""
     return expert_weights(cfg, layer, tag=_TAG_SHARED)
