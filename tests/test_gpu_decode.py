@@ -209,7 +209,7 @@ def test_tiny_trace_end_to_end(frac, fill_mode):
     hp.close()
 
 
-@pytest.mark.parametrize("ratio,p", [(2.0, 0.5), (3.0, 0.9)])
+@pytest.mark.parametrize("ratio,p", [(1.5, 0.5), (2.0, 0.5), (1.5, 0.9), (3.0, 0.9)])
 def test_dsv4_shaped_hybrid_steps(ratio, p):
     """DeepSeek-V4-Flash expert shapes (H 4096, I 2048, MXFP4, top-6) on a reduced pool of
     E=16 experts x 3 layers, split by q* with B_H/B_P = ratio; y against the unsplit layer."""
