@@ -97,6 +97,7 @@ _SIGS = {
     "moe_experts_prefill_status": (C.c_int, [_P, _P, C.POINTER(C.c_uint32)]),
     "mc_host_pool_create": (_P, [_I32, _P]),
     "mc_host_pool_destroy": (None, [_P]),
+    "mc_host_pool_cpus": (C.c_int32, [_P, _P, _I32]),
     "mc_host_experts": (C.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, C.POINTER(Banks), _P]),
     "mc_bandwidth_profile": (C.c_int, [C.POINTER(Banks), C.POINTER(Banks), _P, _I32, C.c_double, C.c_double,
                                        _P, C.POINTER(BwProfile)]),
@@ -347,6 +348,14 @@ class HostPool:
         if not self.handle:
             raise McError("mc_host_pool_create", -1, last_error())
         self.n_threads = n_threads
+
+    def cpus(self):
+        """The CPU each pool thread is pinned to (-1 = not pinned); thread 0 is the dispatcher."""
+        arr = (C.c_int32 * self.n_threads)()
+        n = lib().mc_host_pool_cpus(self.handle, arr, self.n_threads)
+        if n < 0:
+            raise McError("mc_host_pool_cpus", n, last_error())
+        return list(arr)
 
     def close(self):
         if self.handle:

@@ -88,6 +88,7 @@ struct mc_host_pool {
   // dispatcher of the hybrid stages (the host branch)
   std::thread driver;
   std::atomic<bool> driver_stop{false};
+  std::vector<int> cpus;                 // CPU of thread i (0 = dispatcher), -1 = not pinned
 
   void worker_loop() {
     int seen = 0;
@@ -185,6 +186,71 @@ void mc_host_pool::driver_loop() {
   }
 }
 
+namespace mc {
+
+static int read_int_file(const char* path, int dflt) {
+  FILE* f = fopen(path, "r");
+  if (!f) return dflt;
+  int v = dflt;
+  if (fscanf(f, "%d", &v) != 1) v = dflt;
+  fclose(f);
+  return v;
+}
+
+// Default placement ([jjl357] "8.3": workers pinned to physical cores): the CPUs this
+// process may run on, one hardware thread of each physical core first (the lowest
+// numbered, in (package, core) order), then the cores' further hardware threads.
+// Topology comes from /sys; a CPU without it counts as a core of its own.
+static std::vector<int> physical_core_order() {
+  cpu_set_t allowed;
+  CPU_ZERO(&allowed);
+  std::vector<int> cpus;
+  if (sched_getaffinity(0, sizeof allowed, &allowed) == 0) {
+    for (int c = 0; c < CPU_SETSIZE; ++c)
+      if (CPU_ISSET(c, &allowed)) cpus.push_back(c);
+  }
+  struct Cpu { int pkg, core, cpu; };
+  std::vector<Cpu> info;
+  for (int c : cpus) {
+    char path[128];
+    snprintf(path, sizeof path, "/sys/devices/system/cpu/cpu%d/topology/physical_package_id", c);
+    const int pkg = read_int_file(path, 0);
+    snprintf(path, sizeof path, "/sys/devices/system/cpu/cpu%d/topology/core_id", c);
+    const int core = read_int_file(path, 100000 + c);
+    info.push_back({pkg, core, c});
+  }
+  std::sort(info.begin(), info.end(), [](const Cpu& a, const Cpu& b) {
+    return a.pkg != b.pkg ? a.pkg < b.pkg : (a.core != b.core ? a.core < b.core : a.cpu < b.cpu);
+  });
+  std::vector<int> order;
+  std::vector<bool> used(info.size(), false);
+  for (size_t round = 0; order.size() < info.size(); ++round) {
+    // round r takes the r-th hardware thread of every core that has one
+    size_t i = 0;
+    while (i < info.size()) {
+      size_t j = i;
+      while (j < info.size() && info[j].pkg == info[i].pkg && info[j].core == info[i].core) ++j;
+      if (i + round < j && !used[i + round]) {
+        used[i + round] = true;
+        order.push_back(info[i + round].cpu);
+      }
+      i = j;
+    }
+    if (round > info.size()) break;
+  }
+  return order;
+}
+
+static void pin_thread(std::thread& t, int cpu) {
+  if (cpu < 0) return;
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  CPU_SET(cpu, &set);
+  pthread_setaffinity_np(t.native_handle(), sizeof set, &set);
+}
+
+}  // namespace mc
+
 extern "C" mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* cpu_ids) {
   mc::clear_error();
   if (n_threads < 1 || n_threads > 1024) {
@@ -196,24 +262,34 @@ extern "C" mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* c
     mc::set_error("mc_host_pool_create: out of memory");
     return nullptr;
   }
+  // thread i of the pool (0 = the dispatcher, which also computes; 1.. = workers) runs
+  // on p->cpus[i]: the caller's list, or distinct physical cores of the allowed set
+  p->cpus.assign(n_threads, -1);
+  if (cpu_ids) {
+    for (int i = 0; i < n_threads; ++i) p->cpus[i] = cpu_ids[i];
+  } else {
+    const std::vector<int> order = mc::physical_core_order();
+    for (int i = 0; i < n_threads && !order.empty(); ++i) p->cpus[i] = order[i % order.size()];
+  }
   // the calling thread takes part in parallel_for, so n_threads - 1 workers
   for (int i = 0; i + 1 < n_threads; ++i) {
     p->threads.emplace_back([p] { p->worker_loop(); });
-    if (cpu_ids) {
-      cpu_set_t set;
-      CPU_ZERO(&set);
-      CPU_SET(cpu_ids[i + 1], &set);
-      pthread_setaffinity_np(p->threads.back().native_handle(), sizeof set, &set);
-    }
+    mc::pin_thread(p->threads.back(), p->cpus[i + 1]);
   }
   p->driver = std::thread([p] { p->driver_loop(); });
-  if (cpu_ids) {
-    cpu_set_t set;
-    CPU_ZERO(&set);
-    CPU_SET(cpu_ids[0], &set);
-    pthread_setaffinity_np(p->driver.native_handle(), sizeof set, &set);
-  }
+  mc::pin_thread(p->driver, p->cpus[0]);
   return p;
+}
+
+extern "C" int32_t mc_host_pool_cpus(const mc_host_pool* p, int32_t* cpus, int32_t n) {
+  mc::clear_error();
+  if (!p || (n > 0 && !cpus)) {
+    mc::set_error("mc_host_pool_cpus: NULL pointer");
+    return MC_EINVAL;
+  }
+  const int32_t total = (int32_t)p->cpus.size();
+  for (int32_t i = 0; i < n && i < total; ++i) cpus[i] = p->cpus[i];
+  return total;
 }
 
 extern "C" void mc_host_pool_destroy(mc_host_pool* p) {

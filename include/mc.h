@@ -404,10 +404,17 @@ int moe_experts_prefill_status(const void* ws, hipStream_t s, uint32_t* status);
 
 /* Persistent CPU worker pool ([jjl357] "8.3": persistent C++ workers pinned to cores). */
 typedef struct mc_host_pool mc_host_pool;
-/* n_threads >= 1; cpu_ids: NULL = no pinning, else n_threads core ids. NULL on failure.
- * Besides its workers the pool runs one dispatcher thread that serves the hybrid stages
- * registered with it (see hybrid_split_merge); it polls while calls keep coming. */
+/* n_threads >= 1 compute threads: one dispatcher thread, which serves the hybrid stages
+ * registered with the pool (see hybrid_split_merge; it polls while calls keep coming)
+ * and computes, plus n_threads - 1 workers.  cpu_ids: NULL pins thread i to a distinct
+ * physical core of the CPUs this process may use (one hardware thread per core, in
+ * (package, core) order, further hardware threads only when there are more threads than
+ * cores); else n_threads CPU ids, thread 0 being the dispatcher, -1 leaving a thread
+ * unpinned.  NULL on failure. */
 mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* cpu_ids);
+/* The CPU of each pool thread (-1 = not pinned): writes min(n, n_threads) entries and
+ * returns n_threads (MC_EINVAL for a NULL pool). */
+int32_t mc_host_pool_cpus(const mc_host_pool* p, int32_t* cpus, int32_t n);
 void mc_host_pool_destroy(mc_host_pool* p);
 
 /*

@@ -165,3 +165,33 @@ def test_noalloc_rejects_oversized_calls_without_a_gpu():
                                         None, None)
     assert rc == _lib.MC_ENOMEM
     assert "scratch array" in _lib.last_error()
+
+
+def test_host_pool_pins_physical_cores_by_default():
+    """[jjl357] "8.3": the workers are pinned to physical cores.  With no CPU list the pool's
+    threads take distinct CPUs of this process's affinity set, one per physical core before
+    any second hardware thread; an explicit list is taken as given, -1 leaving a thread free."""
+    import os
+    from expert_cache_offloaded_amd import HostPool
+    allowed = sorted(os.sched_getaffinity(0))
+
+    def core_of(c):
+        try:
+            with open("/sys/devices/system/cpu/cpu%d/topology/core_id" % c) as f:
+                core = int(f.read())
+            with open("/sys/devices/system/cpu/cpu%d/topology/physical_package_id" % c) as f:
+                return (int(f.read()), core)
+        except OSError:
+            return (0, 100000 + c)
+
+    n_cores = len({core_of(c) for c in allowed})
+    n = min(4, len(allowed))
+    p = HostPool(n)
+    cpus = p.cpus()
+    p.close()
+    assert len(cpus) == n and all(c in allowed for c in cpus) and len(set(cpus)) == n
+    if n <= n_cores:
+        assert len({core_of(c) for c in cpus}) == n          # distinct physical cores
+    p = HostPool(2, [allowed[0], -1])
+    assert p.cpus() == [allowed[0], -1]
+    p.close()
