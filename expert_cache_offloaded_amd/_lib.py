@@ -94,6 +94,8 @@ _SIGS = {
     "moe_experts_prefill_ws_bytes": (C.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "moe_experts_prefill": (C.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, C.POINTER(Banks), _P, C.c_size_t,
                                       _P, _P, C.POINTER(Prefetch)]),
+    "moe_experts_prefill_part": (C.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, C.POINTER(Banks), _P, _I32, _P,
+                                           C.c_size_t, _P, _P, _P]),
     "moe_experts_prefill_status": (C.c_int, [_P, _P, C.POINTER(C.c_uint32)]),
     "mc_host_pool_create": (_P, [_I32, _P]),
     "mc_host_pool_destroy": (None, [_P]),
@@ -335,6 +337,18 @@ def moe_experts_prefill(x, ids, w, n_tok, E: int, layer_buf: Banks, ws, y, nxt: 
     _check("moe_experts_prefill", lib().moe_experts_prefill(
         _ptr(x), _ptr(ids), _ptr(w), T, k, _ptr(n_tok), E, C.byref(layer_buf), _ptr(ws),
         ws.numel() * ws.element_size(), _ptr(y), _stream(stream), C.byref(nxt) if nxt is not None else None))
+
+
+PF_SORT, PF_EXPERTS, PF_COMBINE, PF_ALL = 1, 2, 4, 7
+
+
+def moe_experts_prefill_part(x, ids, w, n_tok, E: int, part_buf: Banks, entry_of, steps: int, ws, counts=None,
+                             y=None, stream=None) -> None:
+    """One or more steps of a prefill layer (PF_SORT / PF_EXPERTS / PF_COMBINE) on ws."""
+    T, k = ids.shape
+    _check("moe_experts_prefill_part", lib().moe_experts_prefill_part(
+        _ptr(x), _ptr(ids), _ptr(w), T, k, _ptr(n_tok), E, C.byref(part_buf), _ptr(entry_of), steps, _ptr(ws),
+        ws.numel() * ws.element_size(), _ptr(counts), _ptr(y), _stream(stream)))
 
 
 class HostPool:

@@ -392,23 +392,31 @@ namespace mc {
 
 // ---------------------------------------------------------------- install
 
-// flat[i] -> slot i on a cache that holds no expert: slot_of / id_of set, stamp = the
-// current clock (so the installed experts are the least recent at the next call).  An
+// flat[i] -> slot i on a cache that holds no expert: slot_of / id_of set, stamp = a
+// new clock tick (so the installed experts are more recent than the empty slots and
+// less recent than anything the next call touches).  Id -1 leaves slot i empty.  Another
 // id outside [0, L*E), one already placed (a duplicate in the list) or an occupied slot
-// is skipped and counted in stats[err].
+// is skipped and counted in stats[err].  One workgroup: every lane reads the clock
+// before the barrier, lane 0 advances it after.
 __global__ void __launch_bounds__(256)
 install_kernel(int32_t LE, int32_t S, int32_t* __restrict__ slot_of, int32_t* __restrict__ id_of,
-               int64_t* __restrict__ stamp, const int64_t* __restrict__ clock_p,
+               int64_t* __restrict__ stamp, int64_t* __restrict__ clock_p,
                int64_t* __restrict__ stats, const int32_t* __restrict__ flat, int32_t n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n || i >= S) return;
-  const int f = flat[i];
-  if (id_of[i] != -1 || f < 0 || f >= LE || atomicCAS(&slot_of[f], -1, i) != -1) {
-    atomicAdd(reinterpret_cast<unsigned long long*>(&stats[MC_STAT_ERR]), 1ull);
-    return;
+  const int64_t tick = *clock_p + 1;
+  int errs = 0;
+  for (int i = threadIdx.x; i < n && i < S; i += blockDim.x) {
+    const int f = flat[i];
+    if (f == -1) continue;
+    if (id_of[i] != -1 || f < 0 || f >= LE || atomicCAS(&slot_of[f], -1, i) != -1) {
+      ++errs;
+      continue;
+    }
+    id_of[i] = f;
+    stamp[i] = tick;
   }
-  id_of[i] = f;
-  stamp[i] = *clock_p;
+  if (errs) atomicAdd(reinterpret_cast<unsigned long long*>(&stats[MC_STAT_ERR]), (unsigned long long)errs);
+  __syncthreads();
+  if (threadIdx.x == 0) *clock_p = tick;
 }
 
 }  // namespace mc
@@ -421,7 +429,7 @@ extern "C" int mc_cache_install(const mc_cache* c, const int32_t* flat, int32_t 
   MC_REQUIRE(n >= 0 && n <= c->S, "mc_cache_install: n=%d not in [0, S=%d]", n, c->S);
   if (n == 0) return MC_OK;
   MC_REQUIRE(flat != nullptr, "mc_cache_install: NULL list");
-  hipLaunchKernelGGL(install_kernel, dim3((n + 255) / 256), dim3(256), 0, s, c->L * c->E, c->S,
+  hipLaunchKernelGGL(install_kernel, dim3(1), dim3(256), 0, s, c->L * c->E, c->S,
                      c->slot_of, c->id_of, c->stamp, c->clock, c->stats, flat, n);
   MC_LAUNCH_CHECK();
   return MC_OK;

@@ -198,6 +198,7 @@ struct PrefillArgs {
   const uint8_t* dns;
   PrefillWs ws;
   int32_t n_nb;               // column blocks per expert
+  const int32_t* entry_of;    // [E] buffer entry of expert e (-1: not in this part), or null = e
 };
 
 // Tile of logical id L: expert, row range, column block.  Returns false if L is past
@@ -279,6 +280,8 @@ prefill_gemm_kernel(PrefillArgs a) {
   __shared__ int s_shift[kP_Threads];            // down: power-of-two shift of each weight row
   int e, row0, nrows, nb;
   if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
+  const int eb = a.entry_of ? a.entry_of[e] : e;   // the expert's entry of the layer buffer
+  if (eb < 0) return;                              // computed by another part of the layer
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, I = a.I;
   const int K = MODE == 0 ? H : I;
@@ -309,12 +312,12 @@ prefill_gemm_kernel(PrefillArgs a) {
     const uint8_t* wbase;
     const uint8_t* sbase;
     if (MODE == 0) {
-      wbase = a.gu + (size_t)e * (2 * (size_t)I * row_b);
-      sbase = a.gus + (size_t)e * (2 * (size_t)I * row_s);
+      wbase = a.gu + (size_t)eb * (2 * (size_t)I * row_b);
+      sbase = a.gus + (size_t)eb * (2 * (size_t)I * row_s);
       c0 = nb * kP_GU_Cols + wave * 32;
     } else {
-      wbase = a.dn + (size_t)e * ((size_t)H * row_b);
-      sbase = a.dns + (size_t)e * ((size_t)H * row_s);
+      wbase = a.dn + (size_t)eb * ((size_t)H * row_b);
+      sbase = a.dns + (size_t)eb * ((size_t)H * row_s);
       c0 = nb * kP_DN_Cols + wave * 64;
     }
     // table row tid = wave * 64 + nt * 16 + r holds the scales of weight row wrow(nt, r)
@@ -610,27 +613,88 @@ extern "C" int mc_prefill_sort_routes(const int32_t* ids, int32_t T, int32_t k,
   return sort_launch(ids, T, k, n_tok, E, w, s);
 }
 
+static int check_prefill_args(const char* fn, int32_t T, int32_t k, int32_t E, const mc_banks* buf, size_t ws_bytes,
+                              bool need_n) {
+  int rc;
+  if ((rc = check_banks(buf, fn)) != MC_OK) return rc;
+  MC_REQUIRE(buf->fmt == MC_MXFP4, "%s: MXFP4 experts only", fn);
+  MC_REQUIRE(T >= 0 && k >= 1 && E >= 1 && E <= kP_MaxE && k <= E, "%s: T=%d k=%d E=%d", fn, T, k, E);
+  if (need_n)
+    MC_REQUIRE(buf->n >= E, "%s: layer buffer holds %lld < E=%d experts", fn, (long long)buf->n, E);
+  const int H = buf->H, I = buf->I;
+  MC_REQUIRE(H % kP_DN_Cols == 0 && I % kP_GU_Cols == 0 && H % kP_KS == 0 && I % kP_KS == 0,
+             "%s: H=%d must be a multiple of %d and I=%d of %d", fn, H, kP_DN_Cols, I, kP_GU_Cols);
+  MC_REQUIRE(H <= kP_MaxK && I <= kP_MaxK, "%s: H=%d and I=%d must be <= %d", fn, H, I, kP_MaxK);
+  MC_REQUIRE(ws_bytes >= moe_experts_prefill_ws_bytes(T, k, E, H, I), "%s: workspace %zu < %zu bytes", fn,
+             ws_bytes, moe_experts_prefill_ws_bytes(T, k, E, H, I));
+  return MC_OK;
+}
+
+// The steps of a prefill layer on one workspace: the sort, the grouped GEMMs of the
+// experts in `buf` (all of the layer's experts when entry_of is null), the combine.
+static int prefill_steps(const void* x_bf16, const int32_t* ids, const float* w, int32_t T, int32_t k,
+                         const int32_t* n_tok, int32_t E, const mc_banks* buf, const int32_t* entry_of,
+                         int32_t steps, void* ws, int32_t* counts_out, void* y_bf16, hipStream_t s) {
+  int rc;
+  const int H = buf->H, I = buf->I;
+  PrefillWs pw{};
+  ws_layout(T, k, E, H, I, &pw, static_cast<uint8_t*>(ws));
+  if (steps & MC_PF_SORT) {
+    if ((rc = sort_launch(ids, T, k, n_tok, E, pw, s)) != MC_OK) return rc;
+    if (counts_out) MC_HIP(hipMemcpyAsync(counts_out, pw.counts, (size_t)E * 4, hipMemcpyDeviceToDevice, s));
+  }
+  if (steps & MC_PF_EXPERTS) {
+    PrefillArgs a{};
+    a.x = static_cast<const uint16_t*>(x_bf16);
+    a.w = w;
+    a.T = T;
+    a.k = k;
+    a.E = E;
+    a.H = H;
+    a.I = I;
+    a.gu = static_cast<const uint8_t*>(buf->gate_up);
+    a.gus = static_cast<const uint8_t*>(buf->gate_up_scale);
+    a.dn = static_cast<const uint8_t*>(buf->down);
+    a.dns = static_cast<const uint8_t*>(buf->down_scale);
+    a.ws = pw;
+    a.entry_of = entry_of;
+    // tile count bound: sum_e ceil(n_e / BM) <= T*k / BM + E
+    const int max_mt = (T * k) / kP_BM + E;
+    a.n_nb = I / kP_GU_Cols;
+    int g = max_mt * a.n_nb;
+    g = (g + 7) & ~7;
+    if (H / kP_KS == 32)
+      hipLaunchKernelGGL((prefill_gemm_kernel<0, 32>), dim3(g), dim3(kP_Threads), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_gemm_kernel<0, 0>), dim3(g), dim3(kP_Threads), 0, s, a);
+    MC_LAUNCH_CHECK();
+    a.n_nb = H / kP_DN_Cols;
+    g = max_mt * a.n_nb;
+    g = (g + 7) & ~7;
+    if (I / kP_KS == 16)
+      hipLaunchKernelGGL((prefill_gemm_kernel<1, 16>), dim3(g), dim3(kP_Threads), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_gemm_kernel<1, 0>), dim3(g), dim3(kP_Threads), 0, s, a);
+    MC_LAUNCH_CHECK();
+  }
+  if (steps & MC_PF_COMBINE) {
+    const int64_t n4 = (int64_t)T * H / 4;
+    int64_t gc = (n4 + 255) / 256;
+    if (gc > 8192) gc = 8192;
+    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)gc), dim3(256), 0, s, ids, T, k, E, H, n_tok, pw.yr,
+                       static_cast<uint16_t*>(y_bf16));
+    MC_LAUNCH_CHECK();
+  }
+  return MC_OK;
+}
+
 extern "C" int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const float* w,
                                    int32_t T, int32_t k, const int32_t* n_tok, int32_t E,
                                    const mc_banks* layer_buf, void* ws, size_t ws_bytes,
                                    void* y_bf16, hipStream_t s, const mc_prefetch* next) {
   clear_error();
   int rc;
-  if ((rc = check_banks(layer_buf, "moe_experts_prefill layer_buf")) != MC_OK) return rc;
-  MC_REQUIRE(layer_buf->fmt == MC_MXFP4, "moe_experts_prefill: MXFP4 experts only");
-  MC_REQUIRE(T >= 0 && k >= 1 && E >= 1 && E <= kP_MaxE && k <= E,
-             "moe_experts_prefill: T=%d k=%d E=%d", T, k, E);
-  MC_REQUIRE(layer_buf->n >= E, "moe_experts_prefill: layer buffer holds %lld < E=%d experts",
-             (long long)layer_buf->n, E);
-  const int H = layer_buf->H, I = layer_buf->I;
-  MC_REQUIRE(H % kP_DN_Cols == 0 && I % kP_GU_Cols == 0 && H % kP_KS == 0 && I % kP_KS == 0,
-             "moe_experts_prefill: H=%d must be a multiple of %d and I=%d of %d", H, kP_DN_Cols, I,
-             kP_GU_Cols);
-  MC_REQUIRE(H <= kP_MaxK && I <= kP_MaxK, "moe_experts_prefill: H=%d and I=%d must be <= %d", H, I,
-             kP_MaxK);
-  MC_REQUIRE(ws_bytes >= moe_experts_prefill_ws_bytes(T, k, E, H, I),
-             "moe_experts_prefill: workspace %zu < %zu bytes", ws_bytes,
-             moe_experts_prefill_ws_bytes(T, k, E, H, I));
+  if ((rc = check_prefill_args("moe_experts_prefill", T, k, E, layer_buf, ws_bytes, true)) != MC_OK) return rc;
   MC_REQUIRE(((uintptr_t)x_bf16 | (uintptr_t)ws | (uintptr_t)y_bf16) % 16 == 0,
              "moe_experts_prefill: x, ws and y must be 16-byte aligned");
 
@@ -660,49 +724,25 @@ extern "C" int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const
   }
   if (T == 0) return MC_OK;
   MC_REQUIRE(x_bf16 && ids && w && ws && y_bf16, "moe_experts_prefill: NULL pointer");
+  return prefill_steps(x_bf16, ids, w, T, k, n_tok, E, layer_buf, nullptr, MC_PF_ALL, ws, nullptr, y_bf16, s);
+}
 
-  PrefillWs pw{};
-  ws_layout(T, k, E, H, I, &pw, static_cast<uint8_t*>(ws));
-  if ((rc = sort_launch(ids, T, k, n_tok, E, pw, s)) != MC_OK) return rc;
-
-  PrefillArgs a{};
-  a.x = static_cast<const uint16_t*>(x_bf16);
-  a.w = w;
-  a.T = T;
-  a.k = k;
-  a.E = E;
-  a.H = H;
-  a.I = I;
-  a.gu = static_cast<const uint8_t*>(layer_buf->gate_up);
-  a.gus = static_cast<const uint8_t*>(layer_buf->gate_up_scale);
-  a.dn = static_cast<const uint8_t*>(layer_buf->down);
-  a.dns = static_cast<const uint8_t*>(layer_buf->down_scale);
-  a.ws = pw;
-  // tile count bound: sum_e ceil(n_e / BM) <= T*k / BM + E
-  const int max_mt = (T * k) / kP_BM + E;
-  a.n_nb = I / kP_GU_Cols;
-  int g = max_mt * a.n_nb;
-  g = (g + 7) & ~7;
-  if (H / kP_KS == 32)
-    hipLaunchKernelGGL((prefill_gemm_kernel<0, 32>), dim3(g), dim3(kP_Threads), 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_gemm_kernel<0, 0>), dim3(g), dim3(kP_Threads), 0, s, a);
-  MC_LAUNCH_CHECK();
-  a.n_nb = H / kP_DN_Cols;
-  g = max_mt * a.n_nb;
-  g = (g + 7) & ~7;
-  if (I / kP_KS == 16)
-    hipLaunchKernelGGL((prefill_gemm_kernel<1, 16>), dim3(g), dim3(kP_Threads), 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_gemm_kernel<1, 0>), dim3(g), dim3(kP_Threads), 0, s, a);
-  MC_LAUNCH_CHECK();
-  const int64_t n4 = (int64_t)T * H / 4;
-  int64_t gc = (n4 + 255) / 256;
-  if (gc > 8192) gc = 8192;
-  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)gc), dim3(256), 0, s, ids, T, k, E, H,
-                     n_tok, pw.yr, static_cast<uint16_t*>(y_bf16));
-  MC_LAUNCH_CHECK();
-  return MC_OK;
+extern "C" int moe_experts_prefill_part(const void* x_bf16, const int32_t* ids, const float* w, int32_t T,
+                                        int32_t k, const int32_t* n_tok, int32_t E, const mc_banks* part_buf,
+                                        const int32_t* entry_of, int32_t steps, void* ws, size_t ws_bytes,
+                                        int32_t* counts, void* y_bf16, hipStream_t s) {
+  clear_error();
+  int rc;
+  if ((rc = check_prefill_args("moe_experts_prefill_part", T, k, E, part_buf, ws_bytes, false)) != MC_OK)
+    return rc;
+  MC_REQUIRE(steps != 0 && (steps & ~MC_PF_ALL) == 0, "moe_experts_prefill_part: steps=0x%x", steps);
+  MC_REQUIRE(!(steps & MC_PF_EXPERTS) || entry_of, "moe_experts_prefill_part: the experts step needs entry_of");
+  MC_REQUIRE(((uintptr_t)x_bf16 | (uintptr_t)ws | (uintptr_t)y_bf16) % 16 == 0,
+             "moe_experts_prefill_part: x, ws and y must be 16-byte aligned");
+  if (T == 0) return MC_OK;
+  MC_REQUIRE(x_bf16 && ids && w && ws && (y_bf16 || !(steps & MC_PF_COMBINE)),
+             "moe_experts_prefill_part: NULL pointer");
+  return prefill_steps(x_bf16, ids, w, T, k, n_tok, E, part_buf, entry_of, steps, ws, counts, y_bf16, s);
 }
 
 extern "C" int moe_experts_prefill_status(const void* ws, hipStream_t s, uint32_t* status) {

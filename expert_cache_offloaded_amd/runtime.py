@@ -15,6 +15,7 @@ from __future__ import annotations
 from dataclasses import dataclass
 from typing import Dict, Optional
 
+import numpy as np
 import torch
 
 from . import _lib as L
@@ -232,7 +233,6 @@ def static_placement(warm_ids, cap: int):
     warm-up window (host int array of any shape, one entry per routed id, occurrences
     counted), equal counts in the order of first appearance ([qiita] "5. デコード側の答え
     その1").  Returns int32 ids in rank order, for ``cache_install``."""
-    import numpy as np
     flat = np.asarray(warm_ids, dtype=np.int64).ravel()
     flat = flat[flat >= 0]
     if flat.size == 0:
@@ -243,32 +243,43 @@ def static_placement(warm_ids, cap: int):
 
 
 class PrefillRunner:
-    """Prefill over the decode slot pool ([jjl357] "4.3 为什么不用三缓冲或更大缓存").
+    """Prefill over the decode slot pool ([jjl357] "4.3 为什么不用三缓冲或更大缓存", "4.4").
 
     The layer buffers are slot ranges of the pool itself, so no separate staging
     memory exists and the experts still in them when prefill ends become decode's
     initial cache:
       * S >= 2E: whole-layer double buffer in slots [0, E) and [E, 2E) (layer l + 1
         streams host -> HBM on a copy stream while layer l computes);
-      * E <= S < 2E: one layer buffer in slots [0, E), copy then compute, no overlap
-        (the pages fall back to loading on demand when two layers do not fit);
-      * S < E: not supported here (raises).
+      * S < 2E: two layers do not fit, so each layer loads only its routed experts, on
+        demand, after its routing (the pages' fallback).  The routed experts are taken in
+        groups of G = S // 2 that ping-pong between slots [0, G) and [G, 2G): group g + 1
+        streams in on the copy stream while group g computes (S = 1: one slot, no
+        overlap).  The layer runs as moe_experts_prefill_part steps — sort (which also
+        gives the route counts, read back to the host), the experts of each group, one
+        combine — and its output is bit-identical to the whole-layer call.
     After the last layer the experts left in the buffers are installed in the cache
     (mc_cache_install on the freshly reset tables)."""
 
     def __init__(self, cache: "CacheState", host: "BankSet", pool: "BankSet", T: int, k: int):
         E = cache.E
-        if pool.n < E:
-            raise ValueError("prefill needs at least one layer of slots: E=%d > S=%d" % (E, pool.n))
+        if pool.n < 1:
+            raise ValueError("prefill needs at least one slot")
         self.cache, self.host, self.pool, self.T, self.k = cache, host, pool, T, k
         self.double = pool.n >= 2 * E
-        nb = 2 if self.double else 1
-        self.bufs = [BankSet({n: v[b * E:(b + 1) * E] for n, v in pool.t.items()}, pool.H, pool.I, pool.fmt)
-                     for b in range(nb)]
-        self.ws = torch.empty(L.prefill_ws_bytes(T, k, E, pool.H, pool.I), dtype=torch.uint8,
-                              device=pool.t["gate_up"].device)
-        self.ids = torch.empty((T, k), dtype=torch.int32, device=self.ws.device)
-        self.w = torch.empty((T, k), dtype=torch.float32, device=self.ws.device)
+        dev = pool.t["gate_up"].device
+        if self.double:
+            self.G, nb = E, 2
+        else:
+            self.G, nb = max(1, pool.n // 2), (2 if pool.n >= 2 else 1)
+        self.bufs = [BankSet({n: v[b * self.G:(b + 1) * self.G] for n, v in pool.t.items()}, pool.H, pool.I,
+                             pool.fmt) for b in range(nb)]
+        self.ws = torch.empty(L.prefill_ws_bytes(T, k, E, pool.H, pool.I), dtype=torch.uint8, device=dev)
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        if not self.double:
+            self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+            self.entry_of = torch.empty(((E + self.G - 1) // self.G, E), dtype=torch.int32, device=dev)
+        self.groups = []            # per layer: the expert groups loaded (on-demand mode)
 
     def _copy_layer(self, layer: int, b: int, stream) -> None:
         E = self.cache.E
@@ -276,17 +287,35 @@ class PrefillRunner:
             for n, v in self.bufs[b].t.items():
                 v.copy_(self.host.t[n][layer * E:(layer + 1) * E], non_blocking=True)
 
+    def _copy_group(self, layer: int, experts, b: int, stream) -> None:
+        """Host experts layer*E + experts[j] -> entry j of buffer b, one copy per run of
+        consecutive ids and bank."""
+        E = self.cache.E
+        j = 0
+        with torch.cuda.stream(stream):
+            while j < len(experts):
+                r = j
+                while r + 1 < len(experts) and experts[r + 1] == experts[r] + 1:
+                    r += 1
+                f0 = layer * E + int(experts[j])
+                for n, v in self.bufs[b].t.items():
+                    v[j:r + 1].copy_(self.host.t[n][f0:f0 + r - j + 1], non_blocking=True)
+                j = r + 1
+
     def run(self, logits, x, ys, renorm: int = 1):
         """logits: list of L device fp32 [T, E]; x: device bf16 bits [T, H]; ys: list of L
-        device bf16 [T, H] outputs.  Resets the cache first; returns the installed ids."""
+        device bf16 [T, H] outputs.  Resets the cache first; returns the installed ids
+        (flat id per slot, -1 = left empty)."""
         Lc, E = self.cache.L, self.cache.E
         comp = torch.cuda.current_stream()
         self.cache.reset(comp)
+        nb = len(self.bufs)
+        copy = torch.cuda.Stream()
+        done = [torch.cuda.Event() for _ in range(nb)]
+        free = [torch.cuda.Event() for _ in range(nb)]
+        held = [[] for _ in range(nb)]          # flat ids each buffer holds
+        copy.wait_stream(comp)
         if self.double:
-            copy = torch.cuda.Stream()
-            done = [torch.cuda.Event() for _ in range(2)]
-            free = [torch.cuda.Event() for _ in range(2)]
-            copy.wait_stream(comp)
             self._copy_layer(0, 0, copy)
             done[0].record(copy)
             for layer in range(Lc):
@@ -302,29 +331,44 @@ class PrefillRunner:
                 if nxt is not None:
                     done[1 - b].record(copy)
                 free[b].record(comp)
-            # buffer b holds layer l for the last two layers
-            layer_of = [None, None]
-            for layer in range(max(0, Lc - 2), Lc):
-                layer_of[layer % 2] = layer
+                held[b] = list(range(layer * E, (layer + 1) * E))
         else:
+            self.groups = []
+            G = self.G
             for layer in range(Lc):
-                self._copy_layer(layer, 0, comp)
                 L.moe_route(logits[layer], self.k, renorm, self.ids, self.w, comp)
-                L.moe_experts_prefill(x, self.ids, self.w, None, E, self.bufs[0].desc, self.ws, ys[layer], None,
-                                      comp)
-            layer_of = [Lc - 1]
+                L.moe_experts_prefill_part(x, self.ids, self.w, None, E, self.bufs[0].desc, None, L.PF_SORT,
+                                           self.ws, counts=self.counts, stream=comp)
+                routed = np.nonzero(self.counts.cpu().numpy())[0]      # waits for the sort
+                groups = [routed[i:i + G] for i in range(0, len(routed), G)]
+                self.groups.append(groups)
+                eo = np.full((max(1, len(groups)), E), -1, dtype=np.int32)
+                for g, grp in enumerate(groups):
+                    eo[g, grp] = np.arange(len(grp), dtype=np.int32)
+                self.entry_of[:len(eo)].copy_(torch.from_numpy(eo))
+                # the layer's last group lands in the last buffer, so the residents left
+                # at the end fill a prefix of the pool
+                h0 = len(groups) % 2 if nb == 2 else 0
+                for g, grp in enumerate(groups):
+                    b = (h0 + g) % nb
+                    copy.wait_event(free[b])
+                    self._copy_group(layer, grp, b, copy)
+                    done[b].record(copy)
+                    comp.wait_event(done[b])
+                    L.moe_experts_prefill_part(x, self.ids, self.w, None, E, self.bufs[b].desc, self.entry_of[g],
+                                               L.PF_EXPERTS, self.ws, stream=comp)
+                    free[b].record(comp)
+                    held[b] = [layer * E + int(e) for e in grp]
+                L.moe_experts_prefill_part(x, self.ids, self.w, None, E, self.bufs[0].desc, None, L.PF_COMBINE,
+                                           self.ws, y=ys[layer], stream=comp)
         # the experts left in the buffers become the decode cache
         flats = []
-        for b, layer in enumerate(layer_of):
-            if layer is None:
-                flats.extend([-1] * E)        # an unused buffer: its slots stay empty
-            else:
-                flats.extend(range(layer * E, (layer + 1) * E))
+        for b in range(nb):
+            flats.extend(held[b] + [-1] * (self.G - len(held[b])))
         while flats and flats[-1] == -1:
             flats.pop()
-        fl = torch.tensor(flats, dtype=torch.int32, device=self.ws.device)
-        if len(flats):
-            L.cache_install(self.cache.desc, fl, comp)
+        if flats:
+            L.cache_install(self.cache.desc, torch.tensor(flats, dtype=torch.int32, device=self.ws.device), comp)
         return flats
 
 

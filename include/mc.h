@@ -194,10 +194,11 @@ int moe_route_lookup(const float* logits, int32_t renorm, int32_t* topk_ids, flo
  * (device list).  For a fixed placement chosen ahead of decode — the static and
  * prefill-time placements the pages compare LRU against ([jjl357] "11.2 Expert Cache
  * Locality"; [qiita] "5. デコード側の答え その1") — and for adopting experts whose bytes
- * are already in the slots.  Only the tables change (bytes: mc_fill_slots); stamps are
- * set to the current clock.  The cache must hold no expert in slots [0, n) (right after
- * mc_cache_reset); ids outside [0, L*E), duplicates and occupied slots are skipped and
- * counted in stats[MC_STAT_ERR].  A lookup with fixed_cap = 0, min_fill = 0 and
+ * are already in the slots.  Only the tables change (bytes: mc_fill_slots); the call
+ * advances the clock by one and stamps the installed slots with it, so they are more
+ * recent than the empty slots and less recent than anything a later call touches.  The cache must hold no expert in slots [0, n) (right after
+ * mc_cache_reset); id -1 leaves its slot empty; other ids outside [0, L*E), duplicates
+ * and occupied slots are skipped and counted in stats[MC_STAT_ERR].  A lookup with fixed_cap = 0, min_fill = 0 and
  * frac_q16 = 0 then never fills or evicts, which keeps such a placement fixed.
  */
 int mc_cache_install(const mc_cache* c, const int32_t* flat, int32_t n, hipStream_t s);
@@ -390,6 +391,28 @@ int moe_experts_prefill(const void* x_bf16, const int32_t* ids, const float* w, 
                         int32_t k, const int32_t* n_tok, int32_t E, const mc_banks* layer_buf,
                         void* ws, size_t ws_bytes, void* y_bf16, hipStream_t s,
                         const mc_prefetch* next);
+
+/*
+ * A prefill layer in parts, for a slot pool too small for the whole-layer double buffer
+ * ([jjl357] "4.3" last paragraph, "4.4"; [juhe] "Prefill 为什么不能也按需加载": without
+ * room for two whole layers the engine falls back to loading the routed experts on
+ * demand).  The steps of moe_experts_prefill, run separately on one workspace:
+ *   MC_PF_SORT     the stable token sort of ids (also writes each expert's route count
+ *                  to the device array counts [E] when counts != NULL);
+ *   MC_PF_EXPERTS  the grouped gate_up / SwiGLU / down GEMMs of the experts e with
+ *                  entry_of[e] >= 0 (device int32 [E]), whose weights are entry
+ *                  entry_of[e] of part_buf; each of their routes' gated outputs is kept
+ *                  in the workspace;
+ *   MC_PF_COMBINE  y = bf16 of each token's fixed-order sum over its valid routes.
+ * A layer is one SORT, EXPERTS steps whose parts together cover every routed expert
+ * once, and one COMBINE, in stream order on the same workspace; the result is then
+ * bit-identical to moe_experts_prefill's.  Arguments and limits as moe_experts_prefill.
+ */
+enum { MC_PF_SORT = 1, MC_PF_EXPERTS = 2, MC_PF_COMBINE = 4, MC_PF_ALL = 7 };
+int moe_experts_prefill_part(const void* x_bf16, const int32_t* ids, const float* w, int32_t T,
+                             int32_t k, const int32_t* n_tok, int32_t E, const mc_banks* part_buf,
+                             const int32_t* entry_of, int32_t steps, void* ws, size_t ws_bytes,
+                             int32_t* counts, void* y_bf16, hipStream_t s);
 
 /*
  * Status of the last moe_experts_prefill call made with workspace ws: waits for stream

@@ -172,13 +172,19 @@ class LruOracle:
         self.stats = np.zeros(8, dtype=np.int64)
 
     def install(self, flats) -> None:
-        """A fixed placement made ahead of lookups: flats[i] becomes resident in slot i,
-        stamped with the current clock.  Slots that are occupied, ids out of range and
-        repeated ids are skipped and counted as errors (as the device call does)."""
+        """A fixed placement made ahead of lookups: flats[i] becomes resident in slot i.
+        The install is one clock tick: its slots are stamped with it, so they are more
+        recent than the empty slots (stamp 0) and older than anything a later lookup
+        touches.  Id -1 leaves slot i empty.  Slots that are
+        occupied, other ids out of range and repeated ids are skipped and counted as
+        errors (as the device call does)."""
+        self.clock += 1
         for i, f in enumerate(flats):
             f = int(f)
             if i >= self.S:
                 break
+            if f == -1:
+                continue
             if self.id_of[i] != -1 or f < 0 or f >= self.L * self.E or self.slot_of[f] != -1:
                 self.stats[STAT_ERR] += 1
                 continue

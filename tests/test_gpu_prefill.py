@@ -160,33 +160,60 @@ def test_double_buffer_equals_serialized():
         assert_bf16_close(y[:16], ref, "layer %d" % l)
 
 
-@pytest.mark.parametrize("S", [32, 40, 24])
-def test_prefill_runner_buffers_become_decode_cache(S):
-    """Prefill over the decode slot pool ([jjl357] "4.3"): with S >= 2E the two layer
-    buffers are pool slots (double buffer), with E <= S < 2E one buffer (no overlap).
-    Outputs equal a standalone resident prefill bit for bit; afterwards the experts left
-    in the buffers are the cache's residents (tables equal the oracle's install, slot
-    bytes equal host truth) and a decode call on the last layer hits them all."""
+def _expected_residents(route_ids, E, S):
+    """Where the on-demand runner leaves each layer's routed experts: ascending expert
+    order, groups of G = S // 2 alternating between slots [0, G) and [G, 2G), each
+    layer's last group in the second half (one slot, one buffer, when S = 1)."""
+    G, nb = (S // 2, 2) if S >= 2 else (1, 1)
+    held = [[] for _ in range(nb)]
+    for l, ids in enumerate(route_ids):
+        routed = np.unique(ids[ids >= 0])
+        groups = [routed[i:i + G] for i in range(0, len(routed), G)]
+        h0 = len(groups) % 2 if nb == 2 else 0
+        for g, grp in enumerate(groups):
+            held[(h0 + g) % nb] = [l * E + int(e) for e in grp]
+    flats = []
+    for h in held:
+        flats.extend(h + [-1] * (G - len(h)))
+    while flats and flats[-1] == -1:
+        flats.pop()
+    return flats
+
+
+@pytest.mark.parametrize("S,T", [(32, 512), (40, 512), (24, 512), (8, 512), (5, 512), (1, 64), (6, 3),
+                                 (16, 5), (24, 3)])
+def test_prefill_runner_buffers_become_decode_cache(S, T):
+    """Prefill over the decode slot pool ([jjl357] "4.3", "4.4"): with S >= 2E the two
+    layer buffers are pool slots (double buffer); with S < 2E — also S < E — each layer
+    loads only its routed experts on demand, in groups that ping-pong between two halves
+    of the pool.  Outputs equal a standalone resident prefill bit for bit and the oracle
+    on sampled tokens; afterwards the experts left in the buffers are the cache's
+    residents (tables equal the oracle's install, slot bytes equal host truth), and a
+    decode call on the last layer gives the oracle's lookup and output."""
     from expert_cache_offloaded_amd import _lib as L
     from expert_cache_offloaded_amd.runtime import (BankSet, CacheState, DecodeBuffers, DecodeLayer,
                                                    PrefillRunner, alloc_banks)
-    from oracle import LruOracle, decode_layer
-    cfg = synth.CONFIGS["prefill"].with_(L=3, E=16, k=4, H=512, I=256, T=512)
+    from oracle import LruOracle, decode_layer, route
+    cfg = synth.CONFIGS["prefill"].with_(L=3, E=16, k=4, H=512, I=256, T=T)
     host_np = synth.host_pool(cfg)
     host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
     pool = BankSet(alloc_banks(S, cfg.H, cfg.I, cfg.fmt, device="cuda"), cfg.H, cfg.I, cfg.fmt)
     cache = CacheState(cfg.L, cfg.E, S)
-    x = t_of(synth.activations(cfg, 0)).cuda()
-    logits = [torch.from_numpy(synth.uniform_logits(cfg, layer=l)).cuda() for l in range(cfg.L)]
+    x_np = synth.activations(cfg, 0)
+    x = t_of(x_np).cuda()
+    logits_np = [synth.uniform_logits(cfg, layer=l) for l in range(cfg.L)]
+    logits = [torch.from_numpy(a).cuda() for a in logits_np]
     ys = [torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda") for _ in range(cfg.L)]
     runner = PrefillRunner(cache, host, pool, cfg.T, cfg.k)
     assert runner.double == (S >= 2 * cfg.E)
     flats = runner.run(logits, x, ys)
     torch.cuda.synchronize()
+    print("S=%d T=%d groups per layer %s" % (S, T, [len(g) for g in runner.groups]), flush=True)
     # outputs: a standalone prefill of each layer from its own resident buffer
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
     w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
     ws = torch.empty(L.prefill_ws_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
+    route_ids = []
     for l in range(cfg.L):
         buf = L.make_banks(cfg.fmt, cfg.H, cfg.I,
                            device_banks({k: v[l * cfg.E:(l + 1) * cfg.E] for k, v in host_np.items()}))
@@ -195,12 +222,24 @@ def test_prefill_runner_buffers_become_decode_cache(S):
         L.moe_experts_prefill(x, ids, w, None, cfg.E, buf, ws, y)
         torch.cuda.synchronize()
         assert torch.equal(y, ys[l]), l
-    # the cache after prefill: the last one or two layers, installed where they sit
-    last = [cfg.L - 1] if S < 2 * cfg.E else [cfg.L - 2, cfg.L - 1]
-    want = []
-    for b in range(len(last)):
-        layer = [l for l in last if l % 2 == b][0] if len(last) == 2 else last[0]
-        want.extend(range(layer * cfg.E, (layer + 1) * cfg.E))
+        rid, rw = route(logits_np[l], cfg.k)
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        route_ids.append(rid)
+        layer_np = {k: v[l * cfg.E:(l + 1) * cfg.E] for k, v in host_np.items()}
+        tok = range(min(cfg.T, 16))
+        ref = prefill_per_token(x_np, rid, rw, layer_np, cfg.E, cfg.fmt, cfg.H, cfg.I, tokens=tok)
+        assert_bf16_close(ys[l][:len(tok)], ref, "layer %d" % l)
+    # the cache after prefill
+    if S >= 2 * cfg.E:
+        want = []
+        for b in range(2):
+            layer = [l for l in (cfg.L - 2, cfg.L - 1) if l % 2 == b][0]
+            want.extend(range(layer * cfg.E, (layer + 1) * cfg.E))
+    else:
+        want = _expected_residents(route_ids, cfg.E, S)
+        assert len(runner.groups) == cfg.L
+        for l, groups in enumerate(runner.groups):      # only routed experts were loaded
+            assert np.array_equal(np.concatenate(groups) if groups else np.zeros(0), np.unique(route_ids[l]))
     assert flats == want
     o = LruOracle(cfg.L, cfg.E, S)
     o.install(want)
@@ -208,26 +247,84 @@ def test_prefill_runner_buffers_become_decode_cache(S):
     assert np.array_equal(st["slot_of"], o.slot_of) and np.array_equal(st["id_of"], o.id_of)
     assert np.array_equal(st["stats"], o.stats)
     for sl, f in enumerate(want):
+        if f < 0:
+            continue
         for name, arr in pool.t.items():
             assert torch.equal(arr[sl].cpu(), t_of(host_np[name][f])), (sl, name)
-    # decode on the last layer: every route hits the adopted experts
+    if S < cfg.k:
+        return                      # offload decode needs k slots
+    # decode on the last layer: lookup and output as the oracle's
     dl = DecodeLayer(cache, host, pool, None, DecodeBuffers(1, cfg.k, cfg.H, cfg.I))
-    lg = torch.from_numpy(synth.uniform_logits(cfg.with_(T=1), layer=cfg.L - 1)).cuda()
-    xd = t_of(synth.activations(cfg, 1, T=1)).cuda()
-    yd = dl(cfg.L - 1, lg, xd)
+    lg_np = synth.uniform_logits(cfg.with_(T=1), layer=cfg.L - 1)
+    xd_np = synth.activations(cfg, 1, T=1)
+    yd = dl(cfg.L - 1, torch.from_numpy(lg_np).cuda(), t_of(xd_np).cuda())
     torch.cuda.synchronize()
+    rid, rw = route(lg_np, cfg.k)
+    o.lookup(cfg.L - 1, rid, 1 << 16)
     st = cache.state()
-    assert int(st["stats"][1]) == 0 and int(st["stats"][0]) == cfg.k      # hits only
-    from oracle import route
-    rid, rw = route(lg.cpu().numpy(), cfg.k)
-    ref = decode_layer(synth.activations(cfg, 1, T=1), rid, rw, host_np, cfg.L - 1, cfg.E, cfg.fmt, cfg.H, cfg.I)
+    assert np.array_equal(st["slot_of"], o.slot_of) and np.array_equal(st["stats"], o.stats)
+    if S >= 2 * cfg.E:
+        assert int(st["stats"][1]) == 0 and int(st["stats"][0]) == cfg.k      # hits only
+    ref = decode_layer(xd_np, rid, rw, host_np, cfg.L - 1, cfg.E, cfg.fmt, cfg.H, cfg.I)
     assert_bf16_close(yd, ref, "decode after prefill")
 
 
-def test_prefill_runner_needs_one_layer_of_slots():
-    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, PrefillRunner, alloc_banks
-    cfg = synth.CONFIGS["prefill"].with_(L=2, E=16, k=4, H=512, I=256, T=64)
-    host = BankSet(pinned_banks(cfg, synth.host_pool(cfg)), cfg.H, cfg.I, cfg.fmt)
-    pool = BankSet(alloc_banks(8, cfg.H, cfg.I, cfg.fmt, device="cuda"), cfg.H, cfg.I, cfg.fmt)
-    with pytest.raises(ValueError):
-        PrefillRunner(CacheState(cfg.L, cfg.E, 8), host, pool, cfg.T, cfg.k)
+def test_prefill_part_steps_match_whole_layer():
+    """moe_experts_prefill_part: the sort's route counts equal the oracle's; the experts
+    step run over any partition of the routed experts — here three parts of a shuffled
+    order, each in a buffer of its own in arbitrary entry order — then one combine gives
+    the whole-layer call's output bit for bit."""
+    from expert_cache_offloaded_amd import _lib as L
+    from oracle import route
+    cfg = synth.CONFIGS["prefill"].with_(L=1, E=16, k=4, H=512, I=256, T=300)
+    host_np = synth.host_pool(cfg)
+    x = t_of(synth.activations(cfg, 0)).cuda()
+    lg = synth.uniform_logits(cfg, layer=0)
+    rid, rw = route(lg, cfg.k)
+    ids = torch.from_numpy(rid).cuda()
+    w = torch.from_numpy(rw.astype(np.float32)).cuda()
+    ws = torch.empty(L.prefill_ws_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
+    whole = L.make_banks(cfg.fmt, cfg.H, cfg.I, device_banks(host_np))
+    y0 = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda")
+    L.moe_experts_prefill(x, ids, w, None, cfg.E, whole, ws, y0)
+    counts = torch.full((cfg.E,), -7, dtype=torch.int32, device="cuda")
+    L.moe_experts_prefill_part(x, ids, w, None, cfg.E, whole, None, L.PF_SORT, ws, counts=counts)
+    want_counts = np.bincount(rid.ravel(), minlength=cfg.E)
+    assert np.array_equal(counts.cpu().numpy(), want_counts)
+    rng = np.random.default_rng(5)
+    order = rng.permutation(cfg.E)
+    parts = [order[:5], order[5:6], order[6:]]
+    keep = []
+    for p in parts:
+        perm = rng.permutation(len(p))           # entry j of the part buffer holds expert p[perm[j]]
+        ex = p[perm]
+        buf_np = {k: np.ascontiguousarray(v[ex]) for k, v in host_np.items()}
+        t = device_banks(buf_np)
+        keep.append(t)
+        eo = np.full(cfg.E, -1, dtype=np.int32)
+        eo[ex] = np.arange(len(ex), dtype=np.int32)
+        eo_t = torch.from_numpy(eo).cuda()
+        keep.append(eo_t)
+        L.moe_experts_prefill_part(x, ids, w, None, cfg.E, L.make_banks(cfg.fmt, cfg.H, cfg.I, t), eo_t,
+                                   L.PF_EXPERTS, ws)
+    y1 = torch.empty_like(y0)
+    L.moe_experts_prefill_part(x, ids, w, None, cfg.E, whole, None, L.PF_COMBINE, ws, y=y1)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
+def test_prefill_part_rejects_bad_steps():
+    from expert_cache_offloaded_amd import _lib as L
+    cfg = synth.CONFIGS["prefill"].with_(L=1, E=16, k=4, H=512, I=256, T=8)
+    host_np = synth.host_pool(cfg)
+    whole = L.make_banks(cfg.fmt, cfg.H, cfg.I, device_banks(host_np))
+    ids = torch.zeros((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    x = torch.zeros((cfg.T, cfg.H), dtype=torch.int16, device="cuda")
+    ws = torch.empty(L.prefill_ws_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
+    with pytest.raises(L.McError):
+        L.moe_experts_prefill_part(x, ids, w, None, cfg.E, whole, None, 0, ws)
+    with pytest.raises(L.McError):
+        L.moe_experts_prefill_part(x, ids, w, None, cfg.E, whole, None, 8, ws)
+    with pytest.raises(L.McError):             # experts without entry_of
+        L.moe_experts_prefill_part(x, ids, w, None, cfg.E, whole, None, L.PF_EXPERTS, ws)

@@ -8,7 +8,7 @@ import pytest
 import synth
 from oracle import (LruOracle, best_q_bruteforce, fetch_fraction_q16, lru_bruteforce, miss_latency,
                     split_count)
-from oracle.cache import STAT_EVICT, STAT_FILLS, STAT_HITS, STAT_HOST, STAT_MISSES, fetch_fraction
+from oracle.cache import STAT_ERR, STAT_EVICT, STAT_FILLS, STAT_HITS, STAT_HOST, STAT_MISSES, fetch_fraction
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -138,6 +138,32 @@ def test_lru_rewrite_and_stats():
     # masked rows beyond n_tok
     r = lru.lookup(0, np.array([[1, 6], [5, 4]], np.int32), 1 << 16, n_tok=1)
     assert r["m"] == 0 and r["slots"][1].tolist() == [-1, -1]
+
+
+def test_install_then_lookup_hand_worked():
+    """A fixed placement (installed before any lookup): id -1 leaves its slot empty and
+    is no error; a duplicate, an id out of range and an occupied slot are errors and
+    skipped.  The install is a clock tick of its own: its experts are more recent than
+    the empty slots, which a miss takes first, and older than anything a lookup
+    touches."""
+    lru = LruOracle(2, 4, 5)           # flat ids 0..7
+    lru.install([5, -1, 2, 5, 99])
+    assert lru.id_of.tolist() == [5, -1, 2, -1, -1]
+    assert lru.slot_of.tolist() == [-1, -1, 2, -1, -1, 0, -1, -1]
+    assert lru.stats[STAT_ERR] == 2     # the second 5 and 99
+    lru.install([7])                    # slot 0 is occupied
+    assert lru.stats[STAT_ERR] == 3 and lru.slot_of[7] == -1
+    # layer 1 call: expert 1 (flat 5) hits; 0, 2, 3 (flats 4, 6, 7) fill the empty slots
+    r = lru.lookup(1, np.array([[1, 0], [2, 3]], np.int32), 1 << 16)
+    assert r["hits"] == [5]
+    assert r["fills"] == [(4, 1), (6, 3), (7, 4)]
+    assert r["slots"].tolist() == [[0, 1], [3, 4]]
+    # layer 0 call: expert 2 (flat 2, installed) hits; expert 0 (flat 0) must evict the
+    # least recent resident: flat 2 was just refreshed, the other four carry the first
+    # call's stamp, and the tie goes to the lowest slot (0, flat 5)
+    r = lru.lookup(0, np.array([[2, 0]], np.int32), 1 << 16)
+    assert r["hits"] == [2] and r["fills"] == [(0, 0)]
+    assert lru.stats[STAT_EVICT] == 1 and lru.slot_of[5] == -1
 
 
 def test_lru_reuse_distance_invariants():
