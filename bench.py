@@ -175,7 +175,7 @@ def pmc_workload():
     r = np.random.default_rng(0)
     x = torch.from_numpy(synth.activations(cfg, 0).view(np.int16)).cuda()
     w = torch.full((1, cfg.k), 0.125, dtype=torch.float32, device="cuda")
-    ws = torch.empty(L.decode_ws_bytes(1, cfg.k, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(L.decode_ws_bytes(1, cfg.k, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
     y = torch.zeros((1, cfg.H), dtype=torch.float32, device="cuda")
     for _ in range(20):
         slots = torch.from_numpy(r.choice(n, cfg.k, replace=False).astype(np.int32)[None]).cuda()

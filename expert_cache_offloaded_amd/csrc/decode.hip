@@ -7,10 +7,21 @@
 //
 // Decode streams ~0.53 B of MXFP4 weight per multiply-add, so it is bound by HBM
 // bandwidth, and every weight must be dequantised exactly once whatever the batch.
-// Both passes therefore run on the matrix cores: the expert's weight rows are the
-// MFMA's N side (16 rows per tile, MXFP4 -> bf16 dequantised exactly), the tokens its
-// M side, and K runs in steps of 128 in which each lane owns one whole 32-element MX
-// block (16 B of codes + 1 scale byte) of its row; the activation operand is read in
+// One token (the common decode call):
+//   gate_up: workgroup = (route, 8 intermediate rows); each wave owns 2 gate rows and
+//      the 2 matching up rows and reads each row whole with 16-B loads (bf16 dot2
+//      against the bf16 activation), so a wave's loads are contiguous row runs; the
+//      fp32 h = silu(g) * u goes to the workspace.
+//   down: workgroup = a block of hidden rows over every route of the token, the
+//      token's h vectors copied into LDS by DMA.  Rows of 64 lanes (I >= 2048 MXFP4):
+//      each wave owns its own rows over all routes (even work whatever the route
+//      count) and its row loads go out right behind the h copies, so it computes the
+//      first routes while the later routes' rows still stream in.  Shorter rows: the
+//      waves split the routes and meet in LDS.  Each output row is one fixed-order sum.
+// Several tokens: both passes run on the matrix cores.  The expert's weight rows are
+// the MFMA's N side (16 rows per tile, MXFP4 -> bf16 dequantised exactly), the tokens
+// its M side, and K runs in steps of 128 in which each lane owns one whole 32-element
+// MX block (16 B of codes + 1 scale byte) of its row; the activation operand is read in
 // the same permuted K order.  A unit is one distinct slot of the call (run by the grid
 // column of the first route that holds it) or the shared expert.
 //   gate_up: workgroup = (unit, 16 intermediate rows); the four waves split H, each
@@ -18,17 +29,13 @@
 //      products meet in LDS in a fixed order.  The unit's tokens, 16 at a time, are the
 //      MFMA rows.  h = silu(g) * u is stored as two bf16 halves (hi = bf16(h), lo =
 //      bf16(h - hi): 16 significant bits, the fp32 value to within 2^-17).
-//   down, one token: workgroup = 16 hidden rows over every route of the token (no
-//      cross-workgroup sum); the waves split I.  The hi and lo halves of a route's h are
-//      two MFMA rows of one product, added after it.  The token's h vectors are staged in
-//      LDS by DMA while the weight loads are in flight.
-//   down, several tokens: workgroup = (unit, 64 hidden rows); each wave owns a 16-row
-//      tile over all of I, loaded once; the unit's routes (hi and lo rows, 8 routes per
-//      product) are staged in LDS a batch at a time.  Each route's gated partial is
-//      stored, and the last workgroup of a row block to arrive (one arrival counter per
-//      row block) adds the partials of every token in route order (j = 0 .. k-1, then
-//      the shared expert), so each output element is one fixed-order sum (no float
-//      atomics, run-to-run identical).
+//   down: workgroup = (unit, 64 hidden rows); each wave owns a 16-row tile over all
+//      of I, loaded once; the unit's routes (hi and lo rows, 8 routes per product) are
+//      staged in LDS a batch at a time.  Each route's gated partial is stored, and the
+//      last workgroup of a row block to arrive (one arrival counter per row block) adds
+//      the partials of every token in route order (j = 0 .. k-1, then the shared
+//      expert), so each output element is one fixed-order sum (no float atomics,
+//      run-to-run identical).
 // Fill-through: when the call carries the lookup's fill list, a unit whose slot is
 // being filled reads its fragments from the pinned host entry instead (over the host
 // link) and stores them into the slot from the registers that hold them, so the fill
@@ -97,6 +104,16 @@ struct DecodeArgs {
 };
 
 // ---------------------------------------------------------------- units
+
+// Store visible to the other XCDs once this wave's stores have completed (coherent
+// write, no L2 write-back needed); read of such a value.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 
 // Host entry that fills `slot` in this call, or -1 (wave-uniform; lanes search the
 // list 64 entries at a time).
@@ -462,7 +479,7 @@ __device__ __forceinline__ float dot_chunk_bf_f32(const u32x4_t& w, const float*
 template <int FMT, int CPL>
 __global__ void __launch_bounds__(kThreads)
 gate_up_tok1_kernel(DecodeArgs a) {
-  const int u = blockIdx.x, k = a.k;
+  const int u = blockIdx.x, ib = blockIdx.y, k = a.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool shared_unit = a.has_shared && u == k;
   const int slot_raw = shared_unit ? -1 : a.slots[u];
@@ -492,9 +509,9 @@ gate_up_tok1_kernel(DecodeArgs a) {
       gu = a.f_gu + (size_t)src * per_gu;
       if (FMT == MC_MXFP4) gus = a.f_gus + (size_t)src * per_gus;
     }
-    if (blockIdx.y == 0 && threadIdx.x == 0) a.rsrc[u] = (int32_t)src;
+    if (ib == 0 && threadIdx.x == 0) a.rsrc[u] = (int32_t)src;
   }
-  const int i0 = blockIdx.y * 8 + wave * 2;
+  const int i0 = ib * 8 + wave * 2;
   int cq[CPL];
   bool okq[CPL];
 #pragma unroll
@@ -747,16 +764,227 @@ down_tok1_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- down, one token, wide rows
+//
+// For rows of 64 lanes (I / 32 >= 64 MXFP4 blocks): workgroup = ROWS hidden rows over
+// every route of the token, each wave its own rows (all routes), so the work is even
+// whatever the route count.  The rows go out right behind the copies of h into LDS and
+// the waves start computing as soon as h has landed, the later routes' rows still
+// streaming in.  A row's sum is formed in one wave in a fixed order (routes 0..k-1, then
+// the shared expert, lanes by a fixed butterfly).
+
+template <int FMT, int LPR, int CPLB, int NV>
+__device__ __forceinline__ void tok1_down_role(const DecodeArgs& a, int d, float* s_h) {
+  const int H = a.H, I = a.I, k = a.k;
+  constexpr int ELEMS = FMT == MC_MXFP4 ? 32 : 8;
+  constexpr int E4 = ELEMS / 4;                              // float4 of h per chunk
+  constexpr int RPP = 64 / LPR;                              // rows per pass of a wave
+  constexpr int NPASS = LPR == 64 ? 2 : 1;
+  constexpr int ROWS = 4 * NPASS * RPP;                      // rows of the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row_sub = lane / LPR, c_lane = lane % LPR;
+  const int n_chunks = I / ELEMS;
+  const size_t row_bytes = FMT == MC_MXFP4 ? (size_t)I / 2 : (size_t)I * 2;
+  const size_t per = (size_t)H * row_bytes;
+  const size_t per_s = (size_t)H * I / 32;
+  const int nvec = k + a.has_shared;
+  const int nt = valid_tokens(a);
+  const int rw0 = d * ROWS + wave * NPASS * RPP;             // first row of the wave
+
+  int rowc[NPASS];
+  bool rowok[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int row = rw0 + RPP * p + row_sub;
+    rowok[p] = row < H;
+    rowc[p] = min(row, H - 1);
+  }
+  int cq[CPLB];
+  bool okq[CPLB];
+#pragma unroll
+  for (int q = 0; q < CPLB; ++q) {
+    const int c = c_lane + LPR * q;
+    okq[q] = c < n_chunks;
+    cq[q] = okq[q] ? c : n_chunks - 1;
+  }
+
+  u32x4_t wv[NV][NPASS][CPLB];
+  uint32_t sb[NV][NPASS][CPLB];
+  float gate[NV];
+  int wsl[NV];                                 // fill-through: slot the rows go to, or -1
+  // units v0 .. v0 + NV - 1: slot, gate and host source
+  const uint8_t* dnp[NV];
+  const uint8_t* dnsp[NV];
+  auto meta_group = [&](int v0) {
+    // the slots, gates and host sources of all NV units in one round trip (indices
+    // clamped into the token's routes), then the pointers that depend on them
+    int s_raw[NV], src_raw[NV];
+    float g_raw[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int r = min(v0 + j, k - 1);
+      s_raw[j] = a.slots[r];
+      g_raw[j] = a.w[r];
+      src_raw[j] = a.f_dn ? a.rsrc[r] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = v0 + j;
+      dnp[j] = nullptr;
+      dnsp[j] = nullptr;
+      gate[j] = 0.0f;
+      wsl[j] = -1;
+      if (v < nvec && nt > 0) {
+        if (v < k) {
+          const int sl = (s_raw[j] >= 0 && s_raw[j] < a.n_pool) ? s_raw[j] : -1;
+          if (sl >= 0) {
+            dnp[j] = a.dn + (size_t)sl * per;
+            if (FMT == MC_MXFP4) dnsp[j] = a.dns + (size_t)sl * per_s;
+            gate[j] = g_raw[j];
+            const int64_t src = src_raw[j];              // the host source gate_up found
+            if (src >= 0 && src < a.n_host) {
+              wsl[j] = sl;
+              dnp[j] = a.f_dn + (size_t)src * per;
+              if (FMT == MC_MXFP4) dnsp[j] = a.f_dns + (size_t)src * per_s;
+            }
+          }
+        } else {
+          dnp[j] = a.sh_dn;
+          dnsp[j] = a.sh_dns;
+          gate[j] = 1.0f;
+        }
+      }
+    }
+  };
+  // every row the group's units need (a unit with nothing to read loads one row of
+  // slot 0, the same for every lane group, and is then skipped)
+  auto rows_group = [&]() {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const bool any = dnp[j] != nullptr;
+      const uint8_t* dn = any ? dnp[j] : a.dn;
+      const uint8_t* dns = any ? dnsp[j] : a.dns;
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+        for (int q = 0; q < CPLB; ++q) {
+          const size_t r = any ? (size_t)rowc[p] : 0;
+          wv[j][p][q] = stream_load16(dn + r * row_bytes + (size_t)cq[q] * 16);
+          if (FMT == MC_MXFP4) sb[j][p][q] = dns[r * (I / 32) + cq[q]];
+        }
+    }
+  };
+  auto load_group = [&](int v0) {
+    meta_group(v0);
+    rows_group();
+  };
+  auto compute_group = [&](int v0, float* acc) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int v = v0 + j;
+      if (v >= nvec || gate[j] == 0.0f) continue;
+#pragma unroll
+      for (int q = 0; q < CPLB; ++q) {
+        float hv[ELEMS];
+        const float4* hs = reinterpret_cast<const float4*>(s_h + (size_t)v * I) + cq[q] * E4;
+        const int sw = cq[q] & (E4 - 1);
+#pragma unroll
+        for (int e = 0; e < E4; ++e) {
+          const float4 f = hs[e ^ sw];
+          hv[4 * e + 0] = f.x;
+          hv[4 * e + 1] = f.y;
+          hv[4 * e + 2] = f.z;
+          hv[4 * e + 3] = f.w;
+        }
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+          const u32x4_t wq = okq[q] ? wv[j][p][q] : u32x4_t{0, 0, 0, 0};
+          const float part = FMT == MC_MXFP4 ? dot_chunk_mx_f32(wq, e8m0_to_f32(sb[j][p][q]), hv, 0.0f)
+                                             : dot_chunk_bf_f32(wq, hv, 0.0f);
+          acc[p] = fmaf(gate[j], part, acc[p]);
+        }
+      }
+    }
+    // fill-through: the rows read from the host go into their slot
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (wsl[j] < 0) continue;
+      uint8_t* wb = const_cast<uint8_t*>(a.dn) + (size_t)wsl[j] * per;
+      uint8_t* wbs = FMT == MC_MXFP4 ? const_cast<uint8_t*>(a.dns) + (size_t)wsl[j] * per_s : nullptr;
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        if (!rowok[p]) continue;
+#pragma unroll
+        for (int q = 0; q < CPLB; ++q) {
+          if (!okq[q]) continue;
+          *reinterpret_cast<u32x4_t*>(wb + (size_t)rowc[p] * row_bytes + (size_t)cq[q] * 16) = wv[j][p][q];
+          if (FMT == MC_MXFP4) wbs[(size_t)rowc[p] * (I / 32) + cq[q]] = (uint8_t)sb[j][p][q];
+        }
+      }
+    }
+  };
+
+  meta_group(0);
+  // the token's h vectors into LDS; float4 e of chunk c at float4 c * E4 + (e ^ (c & (E4 - 1)))
+  const int n4 = nvec * I / 4, r4 = I / 4;
+  for (int ch = wave; ch * 64 < n4; ch += 4) {
+    int i4 = ch * 64 + lane;
+    if (i4 >= n4) i4 = n4 - 1;                       // tail lanes re-read a valid vector
+    const int v = i4 / r4, sl = i4 % r4, c = sl / E4;
+    const int e = (c * E4 + ((sl % E4) ^ (c & (E4 - 1)))) * 4;
+    __builtin_amdgcn_global_load_lds(a.h32 + (size_t)v * I + e,
+                                     (__attribute__((address_space(3))) void*)(s_h + ch * 256), 16, 0, 0);
+  }
+  // The rows go out behind the h copies (the empty asm keeps the compiler from moving
+  // any load across), exactly kRowLoads vector loads per wave, all issued whatever the
+  // units (a unit with nothing to read loads one row of slot 0).  Vector memory
+  // operations complete in order, so waiting until at most kRowLoads are outstanding
+  // waits for this wave's h copies only; the rows of later units keep streaming in
+  // while the first ones are computed (the compiler waits for each register as it is
+  // used).  The barrier is issued bare, so that it carries no wait for every load.
+  asm volatile("" ::: "memory");
+  rows_group();
+  constexpr int kRowLoads = NV * NPASS * CPLB * (FMT == MC_MXFP4 ? 2 : 1);
+  static_assert(kRowLoads <= 63, "vmcnt holds at most 63");
+  __builtin_amdgcn_s_waitcnt((((kRowLoads >> 4) & 3) << 14) | (0xF << 8) | (0x7 << 4) | (kRowLoads & 0xF));
+  asm volatile("s_barrier" ::: "memory");
+
+  float acc[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) acc[p] = 0.0f;
+  compute_group(0, acc);
+  for (int v0 = NV; v0 < nvec; v0 += NV) {
+    load_group(v0);
+    compute_group(v0, acc);
+  }
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const float sum = group_sum(acc[p], LPR);
+    if (c_lane == 0 && rowok[p]) {
+      const int row = rowc[p];
+      if (nt == 0) {
+        if (!a.accumulate) a.y[row] = 0.0f;
+        if (a.y_bf16) a.y_bf16[row] = 0;
+      } else {
+        const float v = a.accumulate ? a.y[row] + sum : sum;
+        a.y[row] = v;
+        if (a.y_bf16) a.y_bf16[row] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+// down for one token after gate_up_tok1_kernel: workgroup = ROWS hidden rows over every
+// route, each wave its own rows (balanced whatever the route count)
+template <int FMT, int LPR, int CPLB, int NV>
+__global__ void __launch_bounds__(kThreads)
+down_tok1b_kernel(DecodeArgs a) {
+  extern __shared__ float s_h2[];                 // [k + 1][I] (swizzled)
+  tok1_down_role<FMT, LPR, CPLB, NV>(a, (int)blockIdx.x, s_h2);
+}
+
 // ---------------------------------------------------------------- down, several tokens
 
-// Store visible to the other XCDs once this wave's stores have completed (coherent
-// write, no L2 write-back needed); read of such a value.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <int FMT, int NSTEP>   // NSTEP: K steps covering all of I
 __global__ void __launch_bounds__(kThreads)
@@ -931,6 +1159,30 @@ static bool launch_down_tok1(const DecodeArgs& a, int lpr, int cplb, dim3 grid, 
   }
 }
 
+template <int FMT, int CPLB>
+static bool launch_down_tok1b_nv(const DecodeArgs& a, int nv, uint32_t n_dn, size_t lds, hipStream_t s) {
+  switch (nv) {
+    case 3: hipLaunchKernelGGL((down_tok1b_kernel<FMT, 64, CPLB, 3>), dim3(n_dn), dim3(kThreads), lds, s, a);
+            return true;
+    case 6: hipLaunchKernelGGL((down_tok1b_kernel<FMT, 64, CPLB, 6>), dim3(n_dn), dim3(kThreads), lds, s, a);
+            return true;
+    case 9: hipLaunchKernelGGL((down_tok1b_kernel<FMT, 64, CPLB, 9>), dim3(n_dn), dim3(kThreads), lds, s, a);
+            return true;
+  }
+  return false;
+}
+
+// one-token down for rows of 64 lanes (two 16-B chunks per lane: three routes at once)
+template <int FMT>
+static bool launch_down_tok1b(const DecodeArgs& a, int cplb, int nv, uint32_t n_dn, size_t lds, hipStream_t s) {
+  if (cplb == 1) return launch_down_tok1b_nv<FMT, 1>(a, nv, n_dn, lds, s);
+  if (cplb == 2 && nv == 3) {
+    hipLaunchKernelGGL((down_tok1b_kernel<FMT, 64, 2, 3>), dim3(n_dn), dim3(kThreads), lds, s, a);
+    return true;
+  }
+  return false;
+}
+
 template <int FMT>
 static bool launch_down_unit(const DecodeArgs& a, int nstep, dim3 grid, size_t lds, hipStream_t s) {
   switch (nstep) {
@@ -1073,6 +1325,10 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
   }
 
   bool ok_a, ok_b;
+  // one-token down: rows of 64 lanes take the wide-row kernel (8 rows per workgroup,
+  // nv1 routes held at once), shorter rows the route-split one
+  const int nvec1 = k + has_shared;
+  const int nv1 = (nvec1 <= 3 || cplb1 > 1) ? 3 : (nvec1 <= 6 ? 6 : 9);
   if (T == 1) {
     const dim3 grid_a(k + has_shared, I / 8);
     ok_a = fmt == MC_MXFP4 ? launch_gate_up_tok1<MC_MXFP4>(a, cpl1, grid_a, s)
@@ -1088,7 +1344,11 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
   }
   MC_LAUNCH_CHECK();
   if (fill && fill->down_after) MC_HIP(hipStreamWaitEvent(s, fill->down_after, 0));
-  if (T == 1) {
+  if (T == 1 && lpr1 == 64) {
+    const uint32_t n_dn = (uint32_t)((H + 7) / 8);
+    ok_b = fmt == MC_MXFP4 ? launch_down_tok1b<MC_MXFP4>(a, cplb1, nv1, n_dn, lds1, s)
+                           : launch_down_tok1b<MC_BF16>(a, cplb1, nv1, n_dn, lds1, s);
+  } else if (T == 1) {
     const dim3 grid_b((H + 7) / 8);
     ok_b = fmt == MC_MXFP4 ? launch_down_tok1<MC_MXFP4>(a, lpr1, cplb1, grid_b, lds1, s)
                            : launch_down_tok1<MC_BF16>(a, lpr1, cplb1, grid_b, lds1, s);

@@ -100,7 +100,7 @@ class DecodeBuffers:
         self.y_acc = torch.empty((T, self.H), dtype=torch.float32, device=d)
         self.y_host = torch.empty((T, self.H), dtype=torch.float32, device=d)
         self.y = torch.empty((T, self.H), dtype=torch.int16, device=d)
-        self.ws = torch.empty(L.decode_ws_bytes(T, k, self.H, self.I) // 4 + 4, dtype=torch.float32, device=d)
+        self.ws = torch.zeros(L.decode_ws_bytes(T, k, self.H, self.I) // 4 + 4, dtype=torch.float32, device=d)
 
 
 class DecodeLayer:

@@ -297,11 +297,14 @@ size_t moe_experts_decode_ws_bytes(int32_t T, int32_t k, int32_t H, int32_t I);
  *   fill       NULL (every routed slot is resident), or the fill list of this call's
  *              lookup (mc_fill_list): those slots are read from the host and written
  *              in the same pass, so no separate mc_fill_slots is needed.
- * Two kernel launches, both unit-major (a unit = one distinct slot, or the shared
- * expert): gate_up + SwiGLU, then down, where each unit's rows produce every route's
- * gated partial for a block of rows and the last unit to finish a block adds the
- * partials of each token in route order (a fixed order: results are run-to-run
- * identical).  Needs H % 64 == 0, I % 64 == 0, T <= 64, T*k <= 1024.
+ * Two kernel launches: gate_up + SwiGLU, then down.  One token (T = 1): dot-product
+ * kernels over whole row slices, the down rows of every route of the token summed in
+ * one workgroup per block of rows.  Several tokens: both passes unit-major on the
+ * matrix cores (a unit = one distinct slot, or the shared expert); each unit's down rows
+ * produce every route's gated partial for a block of rows and the last unit to finish a
+ * block adds the partials of each token in route order.  Every order is fixed, so
+ * results are run-to-run identical.  Needs H % 64 == 0, I % 64 == 0, T <= 64,
+ * T*k <= 1024.
  */
 int moe_experts_decode(const void* x_bf16, const int32_t* slots, const float* w, int32_t T,
                        int32_t k, const int32_t* n_tok, const mc_banks* pool,
