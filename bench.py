@@ -32,7 +32,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_pmc.txt")
 # kernels of each measured entry point and the source file they are built from
 TRAFFIC_KERNELS = {
-    "moe_experts_decode": ("decode.hip", ("gate_up_kernel", "down_kernel")),
+    # one token (the headline pass): the dot-product kernels
+    "moe_experts_decode": ("decode.hip", ("gate_up_tok1_kernel", "down_tok1_kernel", "down_tok1b_kernel")),
+    # several tokens (the pmc workload's batched pass): the matrix-core kernels
+    "moe_experts_decode_batched": ("decode.hip", ("gate_up_kernel", "down_unit_kernel")),
     "moe_experts_prefill": ("prefill.hip", ("sort_count_kernel", "sort_plan_kernel", "sort_scatter_kernel",
                                             "prefill_gemm_kernel", "prefill_combine_kernel")),
 }
@@ -44,7 +47,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--cpu-tokens", type=int, default=1, help="decode tokens in the CPU-oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=2, help="decode tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
@@ -55,6 +58,10 @@ def _parse():
                     help="prefill: time only the resident layer (no serialized / double-buffered passes)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="run only the workload the HBM traffic counters are taken on, then exit")
+    ap.add_argument("--pmc-batch", type=int, default=16, help="tokens of the counter workload's batched pass")
+    ap.add_argument("--pmc-table", metavar="CSV",
+                    help="print the per-dispatch average of every counter in a rocprofv3 counter CSV, per "
+                         "kernel of the library, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic table from two rocprofv3 --pmc counter CSVs, then exit")
     ap.add_argument("--c5-sweep", action="store_true",
@@ -105,7 +112,7 @@ def traffic_bytes(entry):
     return None
 
 
-def pmc_summary(fetch_csv, write_csv):
+def pmc_summary(fetch_csv, write_csv, batch=16):
     """Traffic table from FETCH_SIZE / WRITE_SIZE runs of --pmc-workload.  Each counter
     is scaled by what it reads for the workload's 256 MiB device copy (rocclr copy
     kernel dispatches of known size)."""
@@ -145,16 +152,67 @@ def pmc_summary(fetch_csv, write_csv):
         rb, wb = fetch[k] * 1024 * f_fac, write.get(k, 0.0) * 1024 * w_fac
         rows[k] = (rb, wb)
         print("# %-44s %12.1f %12.1f %14.0f %14.0f" % (k[:44], fetch[k], write.get(k, 0.0), rb, wb))
+    algo = pmc_algorithmic(batch)
+    print("# batched pass: %d tokens; algorithmic bytes per call (distinct experts + shared, each read once):"
+          % batch)
     for entry, (src, kernels) in TRAFFIC_KERNELS.items():
-        rb = sum(v[0] for k, v in rows.items() if any(k.startswith("mc::" + n) for n in kernels))
-        wb = sum(v[1] for k, v in rows.items() if any(k.startswith("mc::" + n) for n in kernels))
+        mine = [k for k in rows if any(k == "mc::" + n or k.startswith("mc::" + n + "<") for n in kernels)]
+        rb, wb = sum(rows[k][0] for k in mine), sum(rows[k][1] for k in mine)
+        if entry in algo:
+            print("#   %-28s algorithmic %12.0f  read %12.0f  read / algorithmic %.3f"
+                  % (entry, algo[entry], rb, rb / algo[entry]))
         print("traffic %s %s %s fetch_bytes=%d write_bytes=%d" % (entry, src, _src_sha(src), rb, wb))
 
 
-def pmc_workload():
+def pmc_table(path):
+    """Per-dispatch averages of every counter of a rocprofv3 counter CSV, per library
+    kernel (and the derived MFMA-busy and wave-occupancy ratios where their counters are
+    present)."""
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+            if not name.startswith("mc::"):
+                continue
+            acc[name][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[name].add(r["Dispatch_Id"])
+    for name in sorted(acc):
+        n = len(disp[name])
+        c = {k: v / n for k, v in acc[name].items()}
+        print("%s  (%d dispatches)" % (name, n))
+        for k in sorted(c):
+            print("    %-30s %16.1f" % (k, c[k]))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "SQ_BUSY_CU_CYCLES" in c and c["SQ_BUSY_CU_CYCLES"] > 0:
+            print("    %-30s %16.4f" % ("MFMA busy / CU busy", c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_BUSY_CU_CYCLES"]))
+
+
+def pmc_calls(n, k, T, count=20, seed=0):
+    """Slot lists of the counter workload's expert passes: T tokens x k distinct slots of
+    n resident experts each (seeded, so the summary recomputes the same lists)."""
+    r = np.random.default_rng(seed + T)
+    return [np.stack([r.choice(n, k, replace=False) for _ in range(T)]).astype(np.int32) for _ in range(count)]
+
+
+def pmc_algorithmic(batch):
+    """Algorithmic bytes per call of the workload's passes: the distinct experts' weights
+    (plus the shared expert), each read once."""
+    import synth
+    cfg = synth.CONFIGS["qwen_decode"]
+    eb = synth.expert_bytes(cfg.H, cfg.I, cfg.fmt)
+    out = {}
+    for name, T in (("moe_experts_decode", 1), ("moe_experts_decode_batched", batch)):
+        calls = pmc_calls(64, cfg.k, T)
+        out[name] = float(np.mean([len(np.unique(c)) + 1 for c in calls])) * eb
+    return out
+
+
+def pmc_workload(batch=16):
     """What the traffic counters are taken on: a 256 MiB device copy (calibration), 20
-    Qwen-shaped expert passes over resident experts (8 routed + shared, bs 1) and one
-    8192-token prefill layer (E 256, top-6, H 4096, I 2048)."""
+    Qwen-shaped expert passes over resident experts (8 routed + shared) at bs 1 and 20 at
+    bs `batch`, and one 8192-token prefill layer (E 256, top-6, H 4096, I 2048)."""
     import torch
 
     import synth
@@ -172,15 +230,14 @@ def pmc_workload():
     pool = {k: torch.from_numpy(v).cuda() for k, v in pool_np.items()}
     sh = {k: torch.from_numpy(v).cuda() for k, v in synth.shared_pool(cfg.with_(L=1)).items()}
     pb, sb = L.make_banks(cfg.fmt, cfg.H, cfg.I, pool), L.make_banks(cfg.fmt, cfg.H, cfg.I, sh)
-    r = np.random.default_rng(0)
-    x = torch.from_numpy(synth.activations(cfg, 0).view(np.int16)).cuda()
-    w = torch.full((1, cfg.k), 0.125, dtype=torch.float32, device="cuda")
-    ws = torch.zeros(L.decode_ws_bytes(1, cfg.k, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
-    y = torch.zeros((1, cfg.H), dtype=torch.float32, device="cuda")
-    for _ in range(20):
-        slots = torch.from_numpy(r.choice(n, cfg.k, replace=False).astype(np.int32)[None]).cuda()
-        L.moe_experts_decode(x, slots, w, None, pb, sb, ws, y, accumulate=1)
-    torch.cuda.synchronize()
+    for T in (1, batch):
+        x = torch.from_numpy(synth.activations(cfg.with_(T=T), 0).view(np.int16)).cuda()
+        w = torch.full((T, cfg.k), 0.125, dtype=torch.float32, device="cuda")
+        ws = torch.zeros(L.decode_ws_bytes(T, cfg.k, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
+        y = torch.zeros((T, cfg.H), dtype=torch.float32, device="cuda")
+        for c in pmc_calls(n, cfg.k, T):
+            L.moe_experts_decode(x, torch.from_numpy(c).cuda(), w, None, pb, sb, ws, y, accumulate=1)
+        torch.cuda.synchronize()
     del pool
     cfg = synth.CONFIGS["prefill"]
     T, E, k, H, I = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I
@@ -201,8 +258,162 @@ def pmc_workload():
     print("pmc workload done", flush=True)
 
 
+def random_pool(n, H, I, torch, seed=1):
+    """n MXFP4 experts of random codes with block scales 2^-9 .. 2^-4 (device), for
+    timing passes whose outputs are not checked."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    t = {"gate_up": torch.randint(0, 256, (n, 2 * I, H // 2), dtype=torch.uint8, device="cuda", generator=g),
+         "gate_up_scale": torch.randint(118, 124, (n, 2 * I, H // 32), dtype=torch.uint8, device="cuda", generator=g),
+         "down": torch.randint(0, 256, (n, H, I // 2), dtype=torch.uint8, device="cuda", generator=g),
+         "down_scale": torch.randint(118, 124, (n, H, I // 32), dtype=torch.uint8, device="cuda", generator=g)}
+    return t
+
+
+def time_pass(torch, L, H, I, k, T, calls, pool, shared, reps=5):
+    """Median µs per moe_experts_decode call over graph replays of `calls` (slot arrays
+    [T, k]) back to back, HIP events on the replay stream."""
+    x = torch.randint(-3000, 3000, (T, H), dtype=torch.int16, device="cuda")
+    w = torch.full((T, k), 0.125, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(L.decode_ws_bytes(T, k, H, I), dtype=torch.uint8, device="cuda")
+    slots = [torch.from_numpy(c).cuda() for c in calls]
+    ys = [torch.zeros((T, H), dtype=torch.float32, device="cuda") for _ in calls]
+    for c in range(len(calls)):
+        L.moe_experts_decode(x, slots[c], w, None, pool, shared, ws, ys[c], accumulate=0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            for c in range(len(calls)):
+                L.moe_experts_decode(x, slots[c], w, None, pool, shared, ws, ys[c], accumulate=0)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    st = torch.cuda.current_stream()
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return 1000.0 * float(np.median(ts)) / (reps * len(calls))
+
+
+def expert_pass_rooflines(torch, L, synth):
+    """The expert pass (moe_experts_decode) at the other decode shapes, against 8 TB/s:
+    DeepSeek-V4-Flash-shaped bs 1 (6 routed experts of H 4096 x I 2048, no shared) and
+    Qwen-shaped bs 4 and bs 16 under Zipf(1.1) routing (8 routed + shared, H 2048 x
+    I 512).  Bytes are the distinct experts' weights (each read once)."""
+    out = {}
+    r = np.random.default_rng(0)
+    H, I, k = 4096, 2048, 6
+    pt = random_pool(24, H, I, torch)
+    pool = L.make_banks("mxfp4", H, I, pt)
+    calls = [r.choice(24, k, replace=False).astype(np.int32)[None] for _ in range(40)]
+    us = time_pass(torch, L, H, I, k, 1, calls, pool, None)
+    b = k * synth.expert_bytes(H, I, "mxfp4")
+    out["dsv4_bs1"] = {"us_per_call": round(us, 2), "bytes_per_call": int(b), "gbs": round(b / us * 1e-3, 1),
+                       "frac": round(b / us * 1e-3 / HBM_PEAK_GBS, 4), "units": k}
+    del pt, pool
+    torch.cuda.empty_cache()
+    H, I, k = 2048, 512, 8
+    pt = random_pool(512, H, I, torch)
+    pool = L.make_banks("mxfp4", H, I, pt)
+    st = random_pool(1, H, I, torch, seed=2)
+    sh = L.make_banks("mxfp4", H, I, st)
+    for T in (4, 16):
+        calls = []
+        for c in range(40):
+            ids = synth.zipf_stream(256, k, T, 1.1, r.permutation(256), r)
+            calls.append((ids + 256 * (c % 2)).astype(np.int32))
+        units = float(np.mean([len(np.unique(c)) + 1 for c in calls]))
+        us = time_pass(torch, L, H, I, k, T, calls, pool, sh)
+        b = units * synth.expert_bytes(H, I, "mxfp4")
+        out["qwen_bs%d" % T] = {"us_per_call": round(us, 2), "bytes_per_call": int(b),
+                                "gbs": round(b / us * 1e-3, 1), "frac": round(b / us * 1e-3 / HBM_PEAK_GBS, 4),
+                                "units": round(units, 2)}
+    del pt, pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def tiny_layer(torch, L, synth, steps=64):
+    """The tiny MoE layer (E 8 top-2, H 64, I 128, bf16 experts, 4 tokens, LRU pool of 4
+    slots, locality 0.7): µs per layer call of the whole path (route + lookup + fill +
+    expert pass + bf16 output) over a trace of `steps` calls in one graph."""
+    from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer, alloc_banks
+    cfg = synth.CONFIGS["tiny"]
+    host_t = alloc_banks(cfg.n_flat, cfg.H, cfg.I, cfg.fmt, pin=True)
+    fill_host_pool(cfg, host_t)
+    host = BankSet(host_t, cfg.H, cfg.I, cfg.fmt)
+    pool = BankSet(alloc_banks(cfg.S, cfg.H, cfg.I, cfg.fmt, device="cuda"), cfg.H, cfg.I, cfg.fmt)
+    cache = CacheState(cfg.L, cfg.E, cfg.S)
+    cache.reset()
+    tr = synth.trace(cfg, steps=steps)
+    lg = torch.from_numpy(np.stack([synth.step_logits(cfg, tr[s], s)[0] for s in range(steps)])).cuda()
+    xs = torch.from_numpy(np.stack([synth.activations(cfg, s, 0) for s in range(steps)]).view(np.int16)).cuda()
+    # 4 slots for up to 8 distinct experts per call: overflow misses run on the host branch
+    workers = L.HostPool(2)
+    dl = DecodeLayer(cache, host, pool, None, DecodeBuffers(cfg.T, cfg.k, cfg.H, cfg.I), renorm=cfg.renorm,
+                     hybrid=True, host_pool=workers)
+    for s_ in range(steps):
+        dl(0, lg[s_], xs[s_])
+    torch.cuda.synchronize()
+    cache.reset()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s_ in range(steps):
+            dl(0, lg[s_], xs[s_])
+    cache.reset()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    st = cache.t["stats"].cpu().numpy()
+    del g, dl
+    workers.close()
+    return {"us_per_call": round(1000.0 * e0.elapsed_time(e1) / steps, 2), "calls": steps,
+            "hits": int(st[0]), "misses": int(st[1]), "fills": int(st[2]), "host_routes": int(st[3])}
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def cpu_env():
+    """Host facts for a CPU baseline: the cores this process may run on, the threads
+    the oracle's array library actually uses, and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cores": min(cores, threads), "affinity_cores": cores, "cpu_model": model}
+
+
+def one_core(fn):
+    """fn() with the oracle's array library held to one thread; (result, seconds)."""
+    t0 = time.perf_counter()
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            r = fn()
+    except ImportError:
+        r = fn()
+    return r, time.perf_counter() - t0
 
 
 def build_host_pool(cfg, torch):
@@ -233,11 +444,14 @@ def fill_host_pool(cfg, banks):
 
 def main():
     args = _parse()
+    if args.pmc_table:
+        pmc_table(args.pmc_table)
+        return
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, batch=args.pmc_batch)
         return
     if args.pmc_workload:
-        pmc_workload()
+        pmc_workload(args.pmc_batch)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures a single GPU: the method runs on one GPU (its expert pool, slot "
@@ -390,6 +604,14 @@ def main():
                    "expert_gemv_us_per_token": round(us_per_call * cfg.L, 2),
                    "wall_s": round(wall, 3)},
     }
+
+    # ------------------------------------------------------------------ other decode shapes
+    log("expert pass at the other decode shapes")
+    out["expert_pass"] = expert_pass_rooflines(torch, L, synth)
+    for name, v in out["expert_pass"].items():
+        log("expert pass %s: %.2f us/call, %.0f GB/s (%.3f of 8 TB/s)" % (name, v["us_per_call"], v["gbs"], v["frac"]))
+    out["tiny_layer"] = tiny_layer(torch, L, synth)
+    log("tiny layer: %.2f us per layer call" % out["tiny_layer"]["us_per_call"])
 
     # ------------------------------------------------------------------ bandwidth profile
     # the start-up profile of the two miss paths on this machine (link gather vs host
@@ -611,26 +833,27 @@ def cpu_baseline_c3(cfg, n_layers_model, views, n_layers=4):
     lookup, unsplit per-token expert sum in float64); per-token time scaled to the model."""
     from oracle import LruOracle, decode_layer, route
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    env = cpu_env()
     tr = synth.trace(cfg, steps=1)
     lg = synth.step_logits(cfg, tr[0], 0)
-    o = LruOracle(cfg.L, cfg.E, cfg.S)
+
+    def run(n):
+        o = LruOracle(cfg.L, cfg.E, cfg.S)
+        for l in range(n):
+            ids, w = route(lg[l], cfg.k, cfg.renorm)
+            o.lookup(l, ids, 1 << 16)
+            decode_layer(synth.activations(cfg, 0, l), ids, w, views, l, cfg.E, cfg.fmt, cfg.H, cfg.I)
+
     log("cpu baseline: decode oracle, 1 token x %d layers of the C3 pool" % n_layers)
     t0 = time.perf_counter()
-    for l in range(n_layers):
-        ids, w = route(lg[l], cfg.k, cfg.renorm)
-        o.lookup(l, ids, 1 << 16)
-        decode_layer(synth.activations(cfg, 0, l), ids, w, views, l, cfg.E, cfg.fmt, cfg.H, cfg.I)
+    run(n_layers)
     dt = time.perf_counter() - t0
-    per_token = dt / n_layers * n_layers_model
-    return {"value": round(1.0 / per_token, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": "1 decode token through %d layers (route, LRU lookup, unsplit float64 expert sum); "
-                      "per-token time scaled to %d layers" % (n_layers, n_layers_model),
-            "seconds": round(dt, 2)}
+    _, dt1 = one_core(lambda: run(1))
+    return dict({"value": round(1.0 / (dt / n_layers * n_layers_model), 4), "unit": "tok/s", "kind": "oracle",
+                 "sample": "1 decode token through %d layers (route, LRU lookup, unsplit float64 expert sum); "
+                           "per-token time scaled to %d layers (one core: 1 layer)" % (n_layers, n_layers_model),
+                 "seconds": round(dt, 2),
+                 "one_core": {"value": round(1.0 / (dt1 * n_layers_model), 4), "seconds": round(dt1, 2)}}, **env)
 
 
 def alloc_pinned_exact(n, H, I, fmt, torch):
@@ -782,52 +1005,58 @@ def bench_prefill(args, torch, L, synth):
     return pre, roof
 
 
-def cpu_baseline_prefill(cfg, host_t, n_experts=8):
+def cpu_baseline_prefill(cfg, host_t, n_experts=64):
     """The oracle's grouped prefill (route, stable sort, per-expert float64 FFN, scatter-add)
     on `n_experts` of the 256 experts of layer 0; tok/s scaled to the whole layer."""
     from oracle import prefill_grouped, route
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    env = cpu_env()
     banks = {k: v[:cfg.E].numpy() for k, v in host_t.items()}
     x = synth.activations(cfg, 0)
+
+    def run(n):
+        ids, w = route(synth.uniform_logits(cfg, layer=0), cfg.k, 1)
+        prefill_grouped(x, ids, w, banks, cfg.E, cfg.fmt, cfg.H, cfg.I, experts=range(n))
+
     log("cpu baseline: prefill oracle on %d of %d experts (layer 0)" % (n_experts, cfg.E))
     t0 = time.perf_counter()
-    ids, w = route(synth.uniform_logits(cfg, layer=0), cfg.k, 1)
-    prefill_grouped(x, ids, w, banks, cfg.E, cfg.fmt, cfg.H, cfg.I, experts=range(n_experts))
+    run(n_experts)
     dt = time.perf_counter() - t0
-    layer_s = dt * cfg.E / n_experts
-    return {"value": round(cfg.T / layer_s, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of the %d experts of one 8192-token layer (their routed tokens), grouped per-expert "
-                      "float64 FFN; tok/s scaled to the whole layer" % (n_experts, cfg.E),
-            "seconds": round(dt, 2)}
+    n1 = max(1, n_experts // 4)
+    _, dt1 = one_core(lambda: run(n1))
+    return dict({"value": round(cfg.T / (dt * cfg.E / n_experts), 2), "unit": "tok/s", "kind": "oracle",
+                 "sample": "%d of the %d experts of one 8192-token layer (their routed tokens), grouped "
+                           "per-expert float64 FFN; tok/s scaled to the whole layer (one core: %d experts)"
+                           % (n_experts, cfg.E, n1),
+                 "seconds": round(dt, 2),
+                 "one_core": {"value": round(cfg.T / (dt1 * cfg.E / n1), 2), "seconds": round(dt1, 2)}}, **env)
 
 
 def cpu_baseline(cfg, tr, logits, xs, host_np, sh_np, n_tokens):
-    """The oracle (as it stands) on the host cores: route + LRU + split + per-token expert sum."""
+    """The oracle (as it stands) on the host cores: route + LRU + split + per-token expert
+    sum; then the same sample held to one core."""
     from oracle import LruOracle, decode_layer, route
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    env = cpu_env()
     host = {k: (v.view(np.uint16) if v.dtype == np.int16 else v) for k, v in host_np.items()}
-    o = LruOracle(cfg.L, cfg.E, cfg.S)
-    log("cpu baseline: oracle on %d token(s) x %d layers" % (n_tokens, cfg.L))
+
+    def run():
+        o = LruOracle(cfg.L, cfg.E, cfg.S)
+        for s_ in range(n_tokens):
+            for l in range(cfg.L):
+                ids, w = route(logits[s_, l], cfg.k, cfg.renorm)
+                o.lookup(l, ids, 1 << 16)
+                decode_layer(xs[s_, l], ids, w, host, l, cfg.E, cfg.fmt, cfg.H, cfg.I, shared=sh_np)
+
+    log("cpu baseline: oracle on %d token(s) x %d layers (%d threads, then 1)" % (n_tokens, cfg.L, env["cores"]))
     t0 = time.perf_counter()
-    for s in range(n_tokens):
-        for l in range(cfg.L):
-            ids, w = route(logits[s, l], cfg.k, cfg.renorm)
-            o.lookup(l, ids, 1 << 16)
-            decode_layer(xs[s, l], ids, w, host, l, cfg.E, cfg.fmt, cfg.H, cfg.I, shared=sh_np)
+    run()
     dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": "%d decode token(s) x %d layers of the same workload (route, LRU lookup, split, "
-                      "unsplit per-token expert sum in float64)" % (n_tokens, cfg.L),
-            "seconds": round(dt, 2)}
+    _, dt1 = one_core(run)
+    return dict({"value": round(n_tokens / dt, 4), "unit": "tok/s", "kind": "oracle",
+                 "sample": "%d decode token(s) x %d layers of the same workload (route, LRU lookup, split, "
+                           "unsplit per-token expert sum in float64)" % (n_tokens, cfg.L),
+                 "seconds": round(dt, 2), "one_core": {"value": round(n_tokens / dt1, 4), "seconds": round(dt1, 2)}},
+                **env)
 
 
 if __name__ == "__main__":
