@@ -157,6 +157,9 @@ extern "C" int mc_hybrid_stage_free(void* stage) {
   MC_HIP(hipDeviceSynchronize());            // no kernel may still read or write it
   host_pool_drop_stage(static_cast<StageHeader*>(stage));
   host_forget(stage, 1);
+  // the header is cleared first: the pages may come back from a later pinned allocation,
+  // which must not look like a stage already set up
+  static_cast<StageHeader*>(stage)->magic = 0;
   MC_HIP(hipHostFree(stage));
   return MC_OK;
 }

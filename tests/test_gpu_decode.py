@@ -327,7 +327,7 @@ def test_hybrid_stage_must_be_coherent():
     ids, slots = torch.zeros((T, k), **i32), torch.full((T, k), -1, **i32)
     w = torch.full((T, k), 0.5, dtype=torch.float32, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
-    stage = torch.empty(L.hybrid_stage_bytes(T, k, cfg.H), dtype=torch.uint8, pin_memory=True)
+    stage = torch.zeros(L.hybrid_stage_bytes(T, k, cfg.H), dtype=torch.uint8, pin_memory=True)
     hp = HostPool(2)
     hy = L.make_hybrid(x, ids, slots, w, 0, cfg.E, None, host, hp, stage, torch.empty((T, k), **f32),
                        torch.empty((T, k), **i32), torch.zeros((T, cfg.H), **f32), torch.zeros((T, cfg.H), **f32),
