@@ -271,28 +271,24 @@ __host__ __device__ constexpr int scale_row_bytes(int nsteps_fixed) {
   return nsteps_fixed > 0 ? nsteps_fixed * 4 : kP_MaxK / 32;
 }
 
-template <int MODE, int NSTEPS>   // MODE 0: gate_up (bf16, SwiGLU), 1: down (fp16, gated rows)
-__global__ void __launch_bounds__(kP_Threads, 2)   // two blocks per CU: <= 256 registers per lane
-prefill_gemm_kernel(PrefillArgs a) {
+// One tile of MT 16-row slices (MT = 4 for a full 64-row tile; a tile of fewer rows takes
+// the smallest MT that covers them, so no product runs on 16 rows of padding).
+template <int MODE, int NSTEPS, int MT>   // MODE 0: gate_up (bf16, SwiGLU), 1: down (fp16, gated rows)
+__device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int e, int eb, int row0, int nrows, int nb,
+                                          uint8_t (*sA)[kP_StageBytes], uint8_t* sS, int* s_shift) {
   constexpr int SROW = scale_row_bytes(NSTEPS);
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kP_StageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sS[kP_Threads * SROW];
-  __shared__ int s_shift[kP_Threads];            // down: power-of-two shift of each weight row
-  int e, row0, nrows, nb;
-  if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
-  const int eb = a.entry_of ? a.entry_of[e] : e;   // the expert's entry of the layer buffer
-  if (eb < 0) return;                              // computed by another part of the layer
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, I = a.I;
   const int K = MODE == 0 ? H : I;
   const int nsteps = NSTEPS > 0 ? NSTEPS : K / kP_KS;
 
-  // the 4 activation chunks this thread moves per step: slot i of the tile holds
-  // row i / 16, logical chunk (i % 16) ^ (row % 16)
-  const uint16_t* aptr[4];
-  int aslot[4];
+  // the activation chunks this thread moves per step: slot i of the tile holds row
+  // i / 16, logical chunk (i % 16) ^ (row % 16); chunk q covers rows 16 q .. 16 q + 15,
+  // so the MT slices need chunks q < MT
+  const uint16_t* aptr[MT];
+  int aslot[MT];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < MT; ++q) {
     const int i = tid + kP_Threads * q;
     const int r = i >> 4;
     const int c = (i & 15) ^ (r & 15);
@@ -330,9 +326,9 @@ prefill_gemm_kernel(PrefillArgs a) {
   }
   const int kq = lane >> 4;                             // MX block of the step this lane owns
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[MT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -340,12 +336,12 @@ prefill_gemm_kernel(PrefillArgs a) {
   // tiles (loaded three steps ahead); named, so that every index is static and nothing
   // is placed in scratch memory
   GemmStage st0, st1, st2;
-  u32x4_t ar0[4], ar1[4], ar2[4];
+  u32x4_t ar0[MT], ar1[MT], ar2[MT];
   int shf[4] = {0, 0, 0, 0};                     // down: the shift of the lane's 4 weight rows
   auto issue_a = [&](int s, u32x4_t* ar) {
     const int k0 = s * kP_KS;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ar[q] = *reinterpret_cast<const u32x4_t*>(aptr[q] + k0);
+    for (int q = 0; q < MT; ++q) ar[q] = *reinterpret_cast<const u32x4_t*>(aptr[q] + k0);
   };
   auto issue_w = [&](int s, GemmStage& g) {
     const int kb = ((s * kP_KS) >> 5) + kq;
@@ -361,7 +357,7 @@ prefill_gemm_kernel(PrefillArgs a) {
   };
   auto store_a = [&](const u32x4_t* ar, int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(&sA[buf][aslot[q]]) = ar[q];
+    for (int q = 0; q < MT; ++q) *reinterpret_cast<u32x4_t*>(&sA[buf][aslot[q]]) = ar[q];
   };
   auto compute = [&](const GemmStage& g, int buf) {
     float sc[4];
@@ -381,7 +377,7 @@ prefill_gemm_kernel(PrefillArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_bf16(g.b[nt][ks], sc[nt]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
           const bf16x8_t aop = *reinterpret_cast<const bf16x8_t*>(
               &sA[buf][(mt * 16 + (lane & 15)) * 256 + phys * 16]);
 #pragma unroll
@@ -393,7 +389,7 @@ prefill_gemm_kernel(PrefillArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) bop[nt] = fp4x8_f16(g.b[nt][ks], sc[nt]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
           const f16x8_t aop = *reinterpret_cast<const f16x8_t*>(
               &sA[buf][(mt * 16 + (lane & 15)) * 256 + phys * 16]);
 #pragma unroll
@@ -491,7 +487,7 @@ prefill_gemm_kernel(PrefillArgs a) {
     // h = silu(g) * u -> fp16, rows of this tile; a value beyond fp16's range is flagged
     bool h_over = false;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = mt * 16 + (lane >> 4) * 4 + j;
@@ -509,7 +505,7 @@ prefill_gemm_kernel(PrefillArgs a) {
   } else {
     // the route's own output row, scaled by its gate
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = mt * 16 + (lane >> 4) * 4 + j;
@@ -520,6 +516,25 @@ prefill_gemm_kernel(PrefillArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) yrow[c0 + nt * 16 + (lane & 15)] = ldexpf(g * acc[mt][nt][j], shf[nt]);
       }
+  }
+}
+
+template <int MODE, int NSTEPS>
+__global__ void __launch_bounds__(kP_Threads, 2)   // two blocks per CU: <= 256 registers per lane
+prefill_gemm_kernel(PrefillArgs a) {
+  constexpr int SROW = scale_row_bytes(NSTEPS);
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kP_StageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sS[kP_Threads * SROW];
+  __shared__ int s_shift[kP_Threads];            // down: power-of-two shift of each weight row
+  int e, row0, nrows, nb;
+  if (!find_tile(a, xcd_remap(blockIdx.x, gridDim.x), &e, &row0, &nrows, &nb)) return;
+  const int eb = a.entry_of ? a.entry_of[e] : e;   // the expert's entry of the layer buffer
+  if (eb < 0) return;                              // computed by another part of the layer
+  switch ((nrows + 15) >> 4) {                     // workgroup-uniform
+    case 1: gemm_tile<MODE, NSTEPS, 1>(a, e, eb, row0, nrows, nb, sA, sS, s_shift); break;
+    case 2: gemm_tile<MODE, NSTEPS, 2>(a, e, eb, row0, nrows, nb, sA, sS, s_shift); break;
+    case 3: gemm_tile<MODE, NSTEPS, 3>(a, e, eb, row0, nrows, nb, sA, sS, s_shift); break;
+    default: gemm_tile<MODE, NSTEPS, 4>(a, e, eb, row0, nrows, nb, sA, sS, s_shift); break;
   }
 }
 
