@@ -263,13 +263,16 @@ extern "C" mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* c
     return nullptr;
   }
   // thread i of the pool (0 = the dispatcher, which also computes; 1.. = workers) runs
-  // on p->cpus[i]: the caller's list, or distinct physical cores of the allowed set
+  // on p->cpus[i]: the caller's list, or distinct physical cores of the allowed set.  The
+  // first core of that order is left to the rest of the process (the thread that drives
+  // the GPU must never share a CPU with a spinning worker); threads beyond the remaining
+  // CPUs stay unpinned
   p->cpus.assign(n_threads, -1);
   if (cpu_ids) {
     for (int i = 0; i < n_threads; ++i) p->cpus[i] = cpu_ids[i];
   } else {
     const std::vector<int> order = mc::physical_core_order();
-    for (int i = 0; i < n_threads && !order.empty(); ++i) p->cpus[i] = order[i % order.size()];
+    for (int i = 0; i < n_threads && (size_t)i + 1 < order.size(); ++i) p->cpus[i] = order[i + 1];
   }
   // the calling thread takes part in parallel_for, so n_threads - 1 workers
   for (int i = 0; i + 1 < n_threads; ++i) {

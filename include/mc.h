@@ -435,8 +435,10 @@ typedef struct mc_host_pool mc_host_pool;
  * and computes, plus n_threads - 1 workers.  cpu_ids: NULL pins thread i to a distinct
  * physical core of the CPUs this process may use (one hardware thread per core, in
  * (package, core) order, further hardware threads only when there are more threads than
- * cores); else n_threads CPU ids, thread 0 being the dispatcher, -1 leaving a thread
- * unpinned.  NULL on failure. */
+ * cores), leaving the first core of that order to the rest of the process (the thread
+ * that launches GPU work); threads beyond the remaining CPUs stay unpinned.  Else
+ * n_threads CPU ids, thread 0 being the dispatcher, -1 leaving a thread unpinned.  NULL
+ * on failure. */
 mc_host_pool* mc_host_pool_create(int32_t n_threads, const int32_t* cpu_ids);
 /* The CPU of each pool thread (-1 = not pinned): writes min(n, n_threads) entries and
  * returns n_threads (MC_EINVAL for a NULL pool). */

@@ -170,7 +170,8 @@ def test_noalloc_rejects_oversized_calls_without_a_gpu():
 def test_host_pool_pins_physical_cores_by_default():
     """[jjl357] "8.3": the workers are pinned to physical cores.  With no CPU list the pool's
     threads take distinct CPUs of this process's affinity set, one per physical core before
-    any second hardware thread; an explicit list is taken as given, -1 leaving a thread free."""
+    any second hardware thread, leaving one CPU to the rest of the process (threads beyond
+    the others stay unpinned); an explicit list is taken as given, -1 leaving a thread free."""
     import os
     from expert_cache_offloaded_amd import HostPool
     allowed = sorted(os.sched_getaffinity(0))
@@ -189,9 +190,17 @@ def test_host_pool_pins_physical_cores_by_default():
     p = HostPool(n)
     cpus = p.cpus()
     p.close()
-    assert len(cpus) == n and all(c in allowed for c in cpus) and len(set(cpus)) == n
-    if n <= n_cores:
-        assert len({core_of(c) for c in cpus}) == n          # distinct physical cores
+    pinned = [c for c in cpus if c >= 0]
+    assert len(cpus) == n and len(pinned) == min(n, len(allowed) - 1)
+    assert all(c in allowed for c in pinned) and len(set(pinned)) == len(pinned)
+    assert len(set(allowed) - set(pinned)) >= 1               # one CPU left to the process
+    if len(pinned) < n_cores:
+        assert len({core_of(c) for c in pinned}) == len(pinned)   # distinct physical cores
+    # as many threads as allowed CPUs: every CPU but one pinned, the last thread free
+    p = HostPool(len(allowed))
+    cpus = p.cpus()
+    p.close()
+    assert cpus[-1] == -1 and len({c for c in cpus if c >= 0}) == len(allowed) - 1
     p = HostPool(2, [allowed[0], -1])
     assert p.cpus() == [allowed[0], -1]
     p.close()
