@@ -55,12 +55,16 @@ struct PrefillWs {
   int32_t* counts4;     // [E][4] per-wave counts
   int32_t* offsets;     // [E+1]
   int32_t* mtile_off;   // [E+1]
+  int32_t* tile_e;      // [T*k/BM + E]: expert of each M tile
   int32_t* perm;        // [T*k]
   _Float16* h;          // [T*k][I]
   float* yr;            // [T*k][H]
 };
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// bound on the M tiles of a call: sum over experts of ceil(n_e / BM) <= T*k / BM + E
+__host__ __device__ inline int max_mtiles(int T, int k, int E) { return (T * k) / kP_BM + E; }
 
 static size_t ws_layout(int T, int k, int E, int H, int I, PrefillWs* w, uint8_t* base) {
   size_t o = 0;
@@ -81,6 +85,8 @@ static size_t ws_layout(int T, int k, int E, int H, int I, PrefillWs* w, uint8_t
   if (w) w->offsets = (int32_t*)p;
   p = take((size_t)(E + 1) * 4);
   if (w) w->mtile_off = (int32_t*)p;
+  p = take((size_t)max_mtiles(T, k, E) * 4);
+  if (w) w->tile_e = (int32_t*)p;
   p = take(nr * 4);
   if (w) w->perm = (int32_t*)p;
   p = take(nr * (size_t)I * 2);
@@ -133,7 +139,7 @@ sort_count_kernel(const int32_t* __restrict__ ids, int T, int k, const int32_t* 
 // 2. offsets and the M-tile table (one workgroup, E <= 1024)
 __global__ void __launch_bounds__(1024)
 sort_plan_kernel(int E, const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                 int32_t* __restrict__ mtile_off) {
+                 int32_t* __restrict__ mtile_off, int32_t* __restrict__ tile_e) {
   __shared__ int s_a[kP_MaxE], s_b[kP_MaxE];
   const int tid = threadIdx.x;
   const int c = tid < E ? counts[tid] : 0;
@@ -156,6 +162,20 @@ sort_plan_kernel(int E, const int32_t* __restrict__ counts, int32_t* __restrict_
   if (tid == 0) {
     offsets[0] = 0;
     mtile_off[0] = 0;
+  }
+  // expert of every M tile (the first e whose inclusive tile count exceeds j), so a GEMM
+  // workgroup finds its tile with one table read instead of a search over mtile_off
+  if (tile_e) {
+    const int n_mt = s_b[E - 1];
+    for (int j = tid; j < n_mt; j += blockDim.x) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_b[mid] > j) hi = mid;
+        else lo = mid + 1;
+      }
+      tile_e[j] = lo;
+    }
   }
 }
 
@@ -206,15 +226,13 @@ struct PrefillArgs {
 __device__ __forceinline__ bool find_tile(const PrefillArgs& a, int L, int* e_out, int* row0,
                                           int* nrows, int* nb) {
   const int32_t* mo = a.ws.mtile_off;
+  // tiles run expert-major, so tile L belongs to M tile L / n_nb's expert (mo[e] * n_nb <= L
+  // < mo[e + 1] * n_nb exactly when mo[e] <= L / n_nb < mo[e + 1]); both reads are issued
+  // together, the table index clamped into the table
+  const int j = min(L / a.n_nb, max_mtiles(a.T, a.k, a.E) - 1);
   const int total = mo[a.E] * a.n_nb;
+  const int e = a.ws.tile_e[j];
   if (L >= total) return false;
-  int lo = 0, hi = a.E;                         // largest e with mo[e] * n_nb <= L
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (mo[mid] * a.n_nb <= L) lo = mid;
-    else hi = mid;
-  }
-  const int e = lo;
   const int m_e = mo[e + 1] - mo[e];
   const int Lp = L - mo[e] * a.n_nb;
   *nb = Lp / m_e;
@@ -285,19 +303,16 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int e, int eb, i
   // the activation chunks this thread moves per step: slot i of the tile holds row
   // i / 16, logical chunk (i % 16) ^ (row % 16); chunk q covers rows 16 q .. 16 q + 15,
   // so the MT slices need chunks q < MT
+  // gate_up's activation rows come from perm: its reads go out first, and the row
+  // addresses are formed after the first weight loads are issued (a wait for an earlier
+  // load waits for everything issued before it)
   const uint16_t* aptr[MT];
   int aslot[MT];
+  int prow[MT];
 #pragma unroll
   for (int q = 0; q < MT; ++q) {
-    const int i = tid + kP_Threads * q;
-    const int r = i >> 4;
-    const int c = (i & 15) ^ (r & 15);
-    const int rr = min(r, nrows - 1);
-    const uint16_t* rowp;
-    if (MODE == 0) rowp = a.x + (size_t)(a.ws.perm[row0 + rr] / a.k) * H;
-    else rowp = reinterpret_cast<const uint16_t*>(a.ws.h) + (size_t)(row0 + rr) * I;
-    aptr[q] = rowp + c * 8;
-    aslot[q] = i * 16;
+    const int rr = min((tid + kP_Threads * q) >> 4, nrows - 1);
+    prow[q] = MODE == 0 ? a.ws.perm[row0 + rr] : 0;
   }
   // weight rows of the lane's 4 column tiles; srow_g = scales of table row tid
   const uint8_t* brow[4];
@@ -422,7 +437,35 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int e, int eb, i
     step(s0 + 2, st2, st1, ar2, ar0);
   };
 
-  // prologue: this thread's row of the scale table, then the first two steps
+  // prologue, in issue order: the weights of the first two steps (they depend on the
+  // tile only), this thread's row of the scale table (whole, when the step count is fixed),
+  // then the activation tiles of three steps (gate_up's rows wait for perm, read first);
+  // the scale table's LDS stores come last, since a wait for a load also waits for every
+  // load issued before it
+  issue_w(0, st0);
+  if (nsteps > 1) issue_w(1, st1);
+  constexpr int kSC = NSTEPS > 0 && NSTEPS % 4 == 0 ? NSTEPS / 4 : 1;   // 16-B scale chunks held
+  u32x4_t sv[kSC];
+  if (NSTEPS > 0 && NSTEPS % 4 == 0) {
+#pragma unroll
+    for (int c = 0; c < kSC; ++c) sv[c] = *reinterpret_cast<const u32x4_t*>(srow_g + c * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    const int i = tid + kP_Threads * q;
+    const int r = i >> 4;
+    const int c = (i & 15) ^ (r & 15);
+    const int rr = min(r, nrows - 1);
+    const uint16_t* rowp;
+    if (MODE == 0) rowp = a.x + (size_t)(prow[q] / a.k) * H;
+    else rowp = reinterpret_cast<const uint16_t*>(a.ws.h) + (size_t)(row0 + rr) * I;
+    aptr[q] = rowp + c * 8;
+    aslot[q] = i * 16;
+  }
+  issue_a(0, ar0);
+  if (nsteps > 1) issue_a(1, ar1);
+  if (nsteps > 2) issue_a(2, ar2);
   {
     uint8_t* dst = sS + tid * SROW;
     const int swt = ((tid & 15) * SROW) >> 8;
@@ -435,17 +478,20 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int e, int eb, i
         xmax = max(xmax, x);
       }
     };
-    if ((nsteps & 3) == 0) {
-      for (int c = 0; c < (nsteps >> 2); ++c) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(srow_g + c * 16);
-        *reinterpret_cast<u32x4_t*>(dst + ((c ^ swt) << 4)) = v;
-        if (MODE == 1) {
-          minmax4(v[0]);
-          minmax4(v[1]);
-          minmax4(v[2]);
-          minmax4(v[3]);
-        }
+    auto put16 = [&](int c, const u32x4_t& v) {
+      *reinterpret_cast<u32x4_t*>(dst + ((c ^ swt) << 4)) = v;
+      if (MODE == 1) {
+        minmax4(v[0]);
+        minmax4(v[1]);
+        minmax4(v[2]);
+        minmax4(v[3]);
       }
+    };
+    if (NSTEPS > 0 && NSTEPS % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < kSC; ++c) put16(c, sv[c]);
+    } else if ((nsteps & 3) == 0) {
+      for (int c = 0; c < (nsteps >> 2); ++c) put16(c, *reinterpret_cast<const u32x4_t*>(srow_g + c * 16));
     } else {
       for (int d = 0; d < nsteps; ++d) {
         const uint32_t v = *reinterpret_cast<const uint32_t*>(srow_g + d * 4);
@@ -461,13 +507,6 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int e, int eb, i
     if (MODE == 1)
       s_shift[tid] = ((int)xmin - 127 >= -23 && (int)xmax - 127 <= 13) ? 0 : (int)xmax - 140;
   }
-  issue_a(0, ar0);
-  issue_w(0, st0);
-  if (nsteps > 1) {
-    issue_a(1, ar1);
-    issue_w(1, st1);
-  }
-  if (nsteps > 2) issue_a(2, ar2);
   store_a(ar0, 0);
   __syncthreads();
   if (MODE == 1) {
@@ -593,7 +632,7 @@ static int sort_launch(const int32_t* ids, int T, int k, const int32_t* n_tok, i
   hipLaunchKernelGGL(sort_count_kernel, dim3(E), dim3(256), 0, s, ids, T, k, n_tok, E, w.counts,
                      w.counts4, w.status);
   hipLaunchKernelGGL(sort_plan_kernel, dim3(1), dim3(1024), 0, s, E, w.counts, w.offsets,
-                     w.mtile_off);
+                     w.mtile_off, w.tile_e);
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(E), dim3(256), 0, s, ids, T, k, n_tok, E, w.counts4,
                      w.offsets, w.perm);
   MC_LAUNCH_CHECK();
@@ -673,8 +712,7 @@ static int prefill_steps(const void* x_bf16, const int32_t* ids, const float* w,
     a.dns = static_cast<const uint8_t*>(buf->down_scale);
     a.ws = pw;
     a.entry_of = entry_of;
-    // tile count bound: sum_e ceil(n_e / BM) <= T*k / BM + E
-    const int max_mt = (T * k) / kP_BM + E;
+    const int max_mt = max_mtiles(T, k, E);
     a.n_nb = I / kP_GU_Cols;
     int g = max_mt * a.n_nb;
     g = (g + 7) & ~7;
