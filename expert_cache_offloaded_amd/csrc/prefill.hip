@@ -9,8 +9,8 @@
 //
 // Steps (all on the compute stream, fixed grids, no host synchronisation):
 //   1. count:   one workgroup per expert counts its routes (ballots; 4 wave quarters).
-//   2. plan:    one workgroup: row offsets per expert (exclusive scan) and the M-tile
-//               table (64-row tiles per expert).
+//   2. plan:    one workgroup: row offsets per expert (exclusive scan), the M-tile
+//               offsets (64-row tiles per expert) and the expert of every M tile.
 //   3. scatter: one workgroup per expert writes its routes' indices r = t*k + j in
 //               (t, j) order — a stable counting sort — into perm.
 //   4. gate_up: grouped GEMM, tile = (expert, 64 sorted rows, 128 intermediate
