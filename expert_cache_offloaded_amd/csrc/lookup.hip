@@ -109,6 +109,14 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   __shared__ int32_t s_ids[ROUTE ? kLkMaxRoutes : 1];
 
   const int tid = threadIdx.x, wid = tid >> 6;
+  // the scalars the call reads and later updates, read before anything else so their
+  // round trips overlap the routing (nothing in the call writes them before the end)
+  const int64_t clock0 = *clock_p;
+  const int n_tok_in = n_tok ? *n_tok : T;
+  int64_t stats0[MC_STAT_ERR + 1];
+  if (tid == 0)
+#pragma unroll
+    for (int i = 0; i <= MC_STAT_ERR; ++i) stats0[i] = stats[i];
   // each thread owns a contiguous run of the layer's experts (so ranks follow e order)
   // and of the slots
   const int per = (E + kLkThreads - 1) / kLkThreads;
@@ -156,9 +164,9 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
     ids = s_ids;
   }
   if (route_waves == kWaves) load_tables(0);     // every wave routed
-  const int nt = n_tok ? min(max(*n_tok, 0), T) : T;
+  const int nt = min(max(n_tok_in, 0), T);
   const int nroutes = nt * k;
-  const int64_t clock = *clock_p + 1;
+  const int64_t clock = clock0 + 1;
   __syncthreads();
 
   // 1. presence of the valid routes
@@ -310,13 +318,13 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
     *clock_p = clock;
     *n_fill = q;
     *n_host = m - q;
-    stats[MC_STAT_HITS] += n_hits;
-    stats[MC_STAT_MISSES] += m;
-    stats[MC_STAT_FILLS] += q;
-    stats[MC_STAT_HOST] += m - q;
-    stats[MC_STAT_EVICT] += n_evict;
-    stats[MC_STAT_CALLS] += 1;
-    stats[MC_STAT_ERR] += s_err;
+    stats[MC_STAT_HITS] = stats0[MC_STAT_HITS] + n_hits;
+    stats[MC_STAT_MISSES] = stats0[MC_STAT_MISSES] + m;
+    stats[MC_STAT_FILLS] = stats0[MC_STAT_FILLS] + q;
+    stats[MC_STAT_HOST] = stats0[MC_STAT_HOST] + m - q;
+    stats[MC_STAT_EVICT] = stats0[MC_STAT_EVICT] + n_evict;
+    stats[MC_STAT_CALLS] = stats0[MC_STAT_CALLS] + 1;
+    stats[MC_STAT_ERR] = stats0[MC_STAT_ERR] + s_err;
   }
 }
 

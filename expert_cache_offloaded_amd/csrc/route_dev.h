@@ -70,10 +70,15 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   uint64_t key[NPER];
   float val[NPER];                   // logits, NaN as -inf (padding -inf)
   float rmax = -INFINITY;
+  // every logit read is issued before the first is used (a read under e < E would be a
+  // branch holding its own wait, one round trip per read); padding lanes read logit E - 1
+  float raw[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) raw[i] = row[min(lane + 64 * i, E - 1)];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
-    float x = e < E ? row[e] : -INFINITY;
+    float x = e < E ? raw[i] : -INFINITY;
     if (x != x) x = -INFINITY;
     val[i] = x;
     key[i] = e < E ? route_key(x, e) : 0ull;
