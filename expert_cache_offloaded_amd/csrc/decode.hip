@@ -1264,7 +1264,7 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
   const bool tile_ok = T == 1 ? (cpl1 <= 4 && cplb1 <= 2 && lds1 <= (size_t)kTok1LdsBytes)
                               : (spw_gu <= 8 && tb >= 1 && pow2_at_least(nstep_dn) <= 16);
   if (!tile_ok) {
-    set_error("moe_experts_decode: H=%d I=%d k=%d T=%d is beyond this build's tiles", H, I, k, T);
+    set_error("moe_experts_decode: H=%d I=%d k=%d T=%d is beyond the library's tiles", H, I, k, T);
     return MC_EUNSUPPORTED;
   }
 

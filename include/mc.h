@@ -52,7 +52,7 @@ typedef enum {
   MC_EINVAL = -1,        /* invalid argument (nothing was enqueued)           */
   MC_ENOMEM = -2,        /* a caller-provided workspace/staging is too small  */
   MC_EHIP = -3,          /* a HIP runtime call failed                         */
-  MC_EUNSUPPORTED = -4,  /* shape or format this build does not handle        */
+  MC_EUNSUPPORTED = -4,  /* shape or format the library does not handle      */
   MC_EDEVICE = -5        /* device-side error counter was found non-zero      */
 } mc_status;
 
