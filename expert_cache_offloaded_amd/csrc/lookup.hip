@@ -53,7 +53,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 
 // Exclusive prefix sum of one int per thread over the workgroup; returns the
 // thread's offset and writes the total to *total (all threads).  Each wave scans its
-// lanes, publishes its total, and then scans the 16 wave totals itself.
+// lanes, publishes its total, and then scans the 16 wave totals itself.  With TRAIL the
+// scan ends with a barrier, so sh_wave may be written again at once; without it, the
+// caller passes another barrier before the next write.
+template <bool TRAIL = true>
 __device__ int block_excl_scan(int v, int* sh_wave, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int x = wave_incl_scan(v);
@@ -63,7 +66,7 @@ __device__ int block_excl_scan(int v, int* sh_wave, int* total) {
   const int wi = wave_incl_scan(w);
   const int before = __builtin_amdgcn_readlane(wi - w, wid);   // waves ahead of this one
   *total = __builtin_amdgcn_readlane(wi, kLkThreads / 64 - 1);
-  __syncthreads();                         // sh_wave is written again by the next scan
+  if (TRAIL) __syncthreads();              // sh_wave is written again by the next scan
   return before + x - v;
 }
 
@@ -73,6 +76,17 @@ __device__ int block_excl_scan(int v, int* sh_wave, int* total) {
 // again only after the caller's next barrier.
 __device__ __forceinline__ int64_t wave_min_nonneg(int64_t v) {
   return (int64_t)~wave_max_u64(~(uint64_t)v);
+}
+
+// Maximum over the workgroup of an unsigned 32-bit value: a DPP wave maximum, one LDS
+// slot per wave, and every wave reduces the 16 slots itself.  The slots are written
+// again only after the caller's next barrier.
+__device__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_max_u32(v);
+  if (lane == 0) sh[wid] = v;
+  __syncthreads();
+  return wave_max_u32(lane < kLkThreads / 64 ? sh[lane] : 0u);
 }
 
 __device__ int64_t block_min_nonneg(int64_t v, int64_t* sh) {
@@ -105,6 +119,7 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   __shared__ int32_t s_id[FAST ? kLkFastS : 1];         // id_of of every slot (FAST)
   __shared__ int s_scan[kLkThreads / 64 + 1];
   __shared__ int64_t s_min[kLkThreads / 64];
+  __shared__ uint32_t s_max32[kLkThreads / 64];
   __shared__ int s_err, s_evict;
   __shared__ int32_t s_ids[ROUTE ? kLkMaxRoutes : 1];
 
@@ -235,12 +250,49 @@ lookup_kernel(const float* __restrict__ logits, int32_t renorm, int32_t* __restr
   int taken = 0;
   int64_t floor_stamp = -1;   // stamps <= floor_stamp were exhausted by earlier rounds
   int64_t st_e[kLkPerS];
+  bool exact64 = !FAST;       // the 64-bit rounds: large pools, or a stamp 2^32 calls old
   if (FAST) {
 #pragma unroll
     for (int j = 0; j < kLkPerS; ++j)
       st_e[j] = s0 + j < s1 ? (s_hit_slot[s0 + j] ? clock : s_st[s0 + j]) : INT64_MAX;
+    // FAST rounds on ages clock - stamp of the evictable slots (0 for the rest), saturated
+    // to 32 bits: a round takes the largest age not yet taken (the smallest stamp) with one
+    // 32-bit block maximum and one scan, two barriers
+    uint32_t age[kLkPerS];
+#pragma unroll
+    for (int j = 0; j < kLkPerS; ++j)
+      age[j] = (s0 + j < s1 && st_e[j] < clock) ? (uint32_t)min(clock - st_e[j], (int64_t)0xFFFFFFFF) : 0u;
+    uint32_t lim = 0xFFFFFFFFu;   // ages above lim were taken by earlier rounds
+    while (taken < q) {
+      uint32_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < kLkPerS; ++j)
+        if (age[j] <= lim && age[j] > mine) mine = age[j];
+      const uint32_t amax = block_max_u32(mine, s_max32);
+      if (amax == 0u) break;                  // no evictable slot left (inconsistent tables)
+      if (amax == 0xFFFFFFFFu) {              // saturated (first round only): exact rounds
+        exact64 = true;
+        break;
+      }
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kLkPerS; ++j) cnt += age[j] == amax;
+      int tot;
+      int off = block_excl_scan<false>(cnt, s_scan, &tot);
+      const int need = q - taken;
+#pragma unroll
+      for (int j = 0; j < kLkPerS; ++j)
+        if (age[j] == amax && off < need) {
+          s_victim[taken + off] = s0 + j;
+          s_vold[taken + off] = s_id[s0 + j];
+          ++off;
+        }
+      taken += min(tot, need);
+      lim = amax - 1u;
+    }
+    __syncthreads();                          // the victims are read by other threads
   }
-  while (taken < q) {
+  while (exact64 && taken < q) {
     int64_t mine = INT64_MAX;
     if (FAST) {
 #pragma unroll

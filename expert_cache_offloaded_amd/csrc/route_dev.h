@@ -5,12 +5,11 @@
 // largest logits; the layer output is their gate-weighted sum.  Order: logit
 // descending, equal logits to the lower expert id; NaN ranks with -inf.
 //
-// Each (logit, id) pair becomes one 64-bit key whose unsigned order is that
-// selection order: high word = the logit's bits mapped to an order-preserving
-// unsigned integer, low word = 0xFFFF - id.  A lane holds NPER keys (ids lane,
-// lane + 64, ...); each of the k rounds takes the lane-local best untaken key and a
-// wavefront max built from DPP lane moves (no LDS traffic), then the owner marks it
-// taken.  Padding lanes (id >= E) hold key 0, below every real key.
+// Each logit becomes a 32-bit value whose unsigned order is the logit order (NaN as -inf,
+// -0 as +0).  A lane holds NPER of them (ids lane, lane + 64, ...); each of the k rounds
+// takes the lane-local best untaken entry and a wavefront max built from DPP lane moves
+// (no LDS traffic); equal logits in several lanes go to the lowest id, found with ballots.
+// The 64-bit wavefront max below serves the lookup's stamp minimum.
 #pragma once
 
 #include <math.h>
@@ -21,23 +20,7 @@ namespace mc {
 
 constexpr int kRouteMaxE = 1024;
 
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-  if (v != v) v = -INFINITY;
-  if (v == 0.0f) v = 0.0f;           // -0 and +0 compare equal: the lower id wins
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
-  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-  return __uint_as_float(u);
-}
-
-__device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFu - (uint32_t)(key & 0xFFFFu)); }
-
-// max(v, DPP-moved v) on a 64-bit key; lanes outside row_mask keep v
+// max(v, DPP-moved v) on a 64-bit value; lanes outside row_mask keep v
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
   const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
@@ -60,14 +43,50 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Order-preserving 32-bit image of a logit (NaN as -inf, -0 as +0).  Every logit maps above
+// 0, so 0 marks a taken or padding entry.
+__device__ __forceinline__ uint32_t logit_order(float v) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_value(uint32_t ord) {
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  return __uint_as_float(u);
+}
+
+// max(v, DPP-moved v); lanes outside ROW_MASK keep v
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+  return m > v ? m : v;
+}
+
+// Maximum over the 64 lanes, returned to every lane (wave-uniform).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<0xB1, 0xF>(v);
+  v = dpp_max_u32<0x4E, 0xF>(v);
+  v = dpp_max_u32<0x141, 0xF>(v);
+  v = dpp_max_u32<0x140, 0xF>(v);
+  v = dpp_max_u32<0x142, 0xA>(v);
+  v = dpp_max_u32<0x143, 0xC>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Top-k of one logits row on the calling wavefront.  Lane j < k returns the j-th
 // pick in *id and its gate in *gate (softmax over the k picks when renorm, else the
 // full-softmax probability); other lanes return id -1.  Needs E <= 64 * NPER, k <= 64.
+// A lane holds the ordered logits of ids lane, lane + 64, ...; each of the k rounds takes
+// every lane's best untaken entry (the lowest id of its equal ones), a 32-bit DPP wave
+// maximum of those, and, when several lanes hold that value, the lowest id among them
+// (the lowest entry index first, then the lowest lane); the winner marks its entry taken.
 template <int NPER>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int renorm,
                                             int* id, float* gate) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[NPER];
+  uint32_t key[NPER];
   float val[NPER];                   // logits, NaN as -inf (padding -inf)
   float rmax = -INFINITY;
   // every logit read is issued before the first is used (a read under e < E would be a
@@ -81,21 +100,42 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     float x = e < E ? raw[i] : -INFINITY;
     if (x != x) x = -INFINITY;
     val[i] = x;
-    key[i] = e < E ? route_key(x, e) : 0ull;
+    key[i] = e < E ? logit_order(x) : 0u;
     rmax = fmaxf(rmax, x);
   }
-  uint64_t mine = 0;                 // lane j keeps pick j
+  uint32_t mine = 0;                 // lane j keeps pick j
+  int mine_id = -1;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) best = key[i] > best ? key[i] : best;
-    const uint64_t w = wave_max_u64(best);
+    uint32_t best = 0;
+    int bi = 0;
 #pragma unroll
     for (int i = 0; i < NPER; ++i)
-      if (key[i] == w) key[i] = 0;   // taken (keys are unique)
-    if (lane == j) mine = w;
+      if (key[i] > best) {           // strict: the lowest index wins among equal entries
+        best = key[i];
+        bi = i;
+      }
+    const uint32_t m = wave_max_u32(best);
+    const uint64_t cand = __ballot(best == m);
+    uint64_t c = cand;
+    if (__popcll(cand) > 1) {        // equal logits in several lanes: the lowest entry index
+      c = 0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (c == 0) c = __ballot(best == m && bi == i);
+    }
+    const int w = (int)__builtin_ctzll(c);
+    const int wi = __builtin_amdgcn_readlane(bi, w);
+    if (lane == w) {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (i == wi) key[i] = 0u;
+    }
+    if (lane == j) {
+      mine = m;
+      mine_id = w + 64 * wi;
+    }
   }
-  const float v = key_value(mine);
+  const float v = order_value(mine);
   const float top = __shfl(v, 0, 64);                     // the largest pick
   float z, denom;
   if (renorm) {
@@ -112,7 +152,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     denom = wave_sum(part);
     z = lane < k ? __expf(v - wmax) : 0.0f;
   }
-  *id = lane < k ? key_id(mine) : -1;
+  *id = lane < k ? mine_id : -1;
   *gate = z / denom;
 }
 
