@@ -222,3 +222,53 @@ def test_route_lookup_fused_equals_separate(cname, T, S, steps):
             sa, sb = a["cs"].state(), b["cs"].state()
             for key in sa:
                 assert np.array_equal(sa[key], sb[key]), (s, l, key)
+
+
+def _set_state(g, o, id_of, stamp, clock):
+    """The same cache state on the device tables and the oracle."""
+    L_, E, S = o.L, o.E, o.S
+    slot_of = np.full(L_ * E, -1, dtype=np.int64)
+    for sl, f in enumerate(id_of):
+        if f >= 0:
+            slot_of[f] = sl
+    o.slot_of, o.id_of = slot_of.copy(), np.asarray(id_of, dtype=np.int64).copy()
+    o.stamp, o.clock = np.asarray(stamp, dtype=np.int64).copy(), int(clock)
+    o.stats = np.zeros(8, dtype=np.int64)
+    t = g.cs.t
+    t["slot_of"].copy_(torch.from_numpy(slot_of.astype(np.int32)))
+    t["id_of"].copy_(torch.from_numpy(np.asarray(id_of, dtype=np.int32)))
+    t["stamp"].copy_(torch.from_numpy(np.asarray(stamp, dtype=np.int64)))
+    t["clock"].fill_(int(clock))
+    t["stats"].zero_()
+
+
+@pytest.mark.parametrize("clock,edge", [(1 << 32, 2), (1 << 32, 1), ((1 << 33) + 10, 1), ((1 << 40) + 3, 5)])
+@pytest.mark.parametrize("S", [8, 4097])
+def test_lookup_victims_at_large_clock(clock, edge, S):
+    """Victim order when stamps lie up to 2^32 and more calls behind the clock: with every
+    slot occupied and the oldest stamp clock - 2^32 + 2, the ages just fit 32 bits (a tie at
+    the oldest included); at clock - 2^32 + 1 and beyond they do not (the exact rounds).
+    A small pool and one above the fast path's size; tables bit-exact after every call."""
+    L_, E, k = 2, 16, 2
+    g = GpuLookup(L_, E, S, 1, k)
+    o = LruOracle(L_, E, S)
+    rng = np.random.default_rng(clock % 9973 + S + edge)
+    id_of = np.full(S, -1, dtype=np.int64)
+    stamp = np.zeros(S, dtype=np.int64)
+    id_of[:8] = [0, 1, 2, 3, 16, 17, 18, 19]
+    base = clock - (1 << 32)
+    stamp[:8] = [base + edge, base + edge + 2, base + edge, clock - 5, clock - 7, clock - 7, clock - 3,
+                 base + edge + 1]
+    if S > 8:                                    # more resident experts, recent stamps
+        extra = rng.permutation(np.arange(20, L_ * E))
+        id_of[8:8 + len(extra)] = extra
+        stamp[8:8 + len(extra)] = clock - rng.integers(1, 50, len(extra))
+    _set_state(g, o, id_of, stamp, clock)
+    for step in range(12):
+        layer = step % L_
+        ids = rng.choice(E, k, replace=False).astype(np.int32)[None, :]
+        a = g(layer, ids, 1 << 16)
+        b = o.lookup(layer, ids, 1 << 16)
+        assert np.array_equal(a["slots"], b["slots"]), step
+        assert a["fills"] == b["fills"] and a["host"] == b["host"], step
+        _compare_state(g, o)
