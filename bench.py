@@ -76,10 +76,11 @@ def _parse():
     ap.add_argument("--c3-layers", type=int, default=16,
                     help="layers of the C3 pool actually built (the box pins at most 64 GiB; the slot "
                          "pool is scaled to the same share of the experts)")
-    ap.add_argument("--fill-mode", choices=("copy", "through", "split"), default="copy",
+    ap.add_argument("--fill-mode", choices=("copy", "through", "split", "fused"), default="fused",
                     help="how misses reach their slots: copy (mc_fill_slots first), through (the expert "
                          "pass reads the host and writes the slots), split (gate_up through, down banks "
-                         "copied on a side stream)")
+                         "copied on a side stream), fused (gate_up through, down banks copied by "
+                         "workgroups of the same launch)")
     return ap.parse_args()
 
 

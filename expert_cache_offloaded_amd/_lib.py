@@ -52,11 +52,12 @@ class BwProfile(C.Structure):
 
 class FillList(C.Structure):
     _fields_ = [("host", C.POINTER(Banks)), ("fill_flat", C.c_void_p), ("fill_slot", C.c_void_p),
-                ("n_fill", C.c_void_p), ("kcap", C.c_int32), ("gate_up_only", C.c_int32),
+                ("n_fill", C.c_void_p), ("kcap", C.c_int32), ("mode", C.c_int32),
                 ("down_after", C.c_void_p)]
 
 
 MC_BANK_GATE_UP, MC_BANK_GATE_UP_SCALE, MC_BANK_DOWN, MC_BANK_DOWN_SCALE, MC_BANK_ALL = 1, 2, 4, 8, 15
+MC_FILL_THROUGH, MC_FILL_GATE_UP, MC_FILL_WITH_GATE_UP = 0, 1, 2
 
 
 class Hybrid(C.Structure):
@@ -251,17 +252,18 @@ def decode_ws_bytes(T: int, k: int, H: int, I: int) -> int:
     return int(lib().moe_experts_decode_ws_bytes(T, k, H, I))
 
 
-def make_fill_list(host: Banks, fill_flat, fill_slot, n_fill, gate_up_only: bool = False,
+def make_fill_list(host: Banks, fill_flat, fill_slot, n_fill, mode: int = MC_FILL_THROUGH,
                    down_after=None) -> FillList:
-    """Fill list of a lookup call for fill-through decode (device tensors).  down_after:
-    a recorded torch.cuda.Event the down pass waits for (or None)."""
+    """Fill list of a lookup call for fill-through decode (device tensors).  mode: one of
+    MC_FILL_THROUGH, MC_FILL_GATE_UP, MC_FILL_WITH_GATE_UP.  down_after: a recorded
+    torch.cuda.Event the down pass waits for (or None)."""
     f = FillList()
     f.host = C.pointer(host)
     f.fill_flat = _ptr(fill_flat)
     f.fill_slot = _ptr(fill_slot)
     f.n_fill = _ptr(n_fill)
     f.kcap = fill_flat.numel()
-    f.gate_up_only = 1 if gate_up_only else 0
+    f.mode = mode
     f.down_after = down_after.cuda_event if down_after is not None else None
     f._keep = (host, fill_flat, fill_slot, n_fill, down_after)
     return f

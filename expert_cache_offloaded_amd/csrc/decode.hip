@@ -43,11 +43,12 @@
 #include <algorithm>
 #include <mutex>
 
-#include "mc_common.h"
+#include "fill_dev.h"
 
 namespace mc {
 
 constexpr int kThreads = 256;
+static_assert(kThreads == kFillThreads, "the fused copy workgroups run the fill's chunk loop");
 constexpr int kMaxRoutes = 1024;
 constexpr int kMaxTok = 64;
 constexpr int kKS = 128;                     // K elements per step (4 MFMAs of 32)
@@ -116,16 +117,26 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 
 
 // Host entry that fills `slot` in this call, or -1 (wave-uniform; lanes search the
-// list 64 entries at a time).
+// list 64 entries at a time).  The count and the first 64 entries are read in one round
+// trip (entries below kcap are always readable).
 __device__ int64_t fill_source(const DecodeArgs& a, int slot) {
   const int lane = threadIdx.x & 63;
-  const int nf = min(max(*a.n_fill, 0), a.kcap);
+  const int nf_raw = *a.n_fill;
+  int fs = -1, ff = -1;
+  if (lane < a.kcap) {
+    fs = a.fill_slot[lane];
+    ff = a.fill_flat[lane];
+  }
+  const int nf = min(max(nf_raw, 0), a.kcap);
   for (int base = 0; base < nf; base += 64) {
     const int i = base + lane;
-    const bool hit = i < nf && a.fill_slot[i] == slot;
-    const uint64_t m = __ballot(hit);
+    if (base > 0 && i < nf) {
+      fs = a.fill_slot[i];
+      ff = a.fill_flat[i];
+    }
+    const uint64_t m = __ballot(i < nf && fs == slot);
     if (m) {
-      const int64_t f = a.fill_flat[base + __builtin_ctzll(m)];
+      const int64_t f = __builtin_amdgcn_readlane(ff, __builtin_ctzll(m));
       return (f >= 0 && f < a.n_host) ? f : -1;
     }
   }
@@ -477,9 +488,8 @@ __device__ __forceinline__ float dot_chunk_bf_f32(const u32x4_t& w, const float*
 // expert).  Every route with a valid slot runs (a slot named twice by the token is read
 // twice, which only a malformed id list can cause).
 template <int FMT, int CPL>
-__global__ void __launch_bounds__(kThreads)
-gate_up_tok1_kernel(DecodeArgs a) {
-  const int u = blockIdx.x, ib = blockIdx.y, k = a.k;
+__device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, int ib) {
+  const int k = a.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool shared_unit = a.has_shared && u == k;
   const int slot_raw = shared_unit ? -1 : a.slots[u];
@@ -571,6 +581,32 @@ gate_up_tok1_kernel(DecodeArgs a) {
       }
     }
   }
+}
+
+template <int FMT, int CPL>
+__global__ void __launch_bounds__(kThreads)
+gate_up_tok1_kernel(DecodeArgs a) {
+  gate_up_tok1_role<FMT, CPL>(a, blockIdx.x, blockIdx.y);
+}
+
+// The same pass with the fill's down-bank copy in the launch: the first n_copy
+// workgroups copy chunk (j mod chunks) of fill entry (j / chunks) into its slot (the
+// fill kernel's loop, entries beyond *n_fill skipped), the rest run the gate_up
+// workgroups (route fastest), which fill through the gate_up banks.  The copies and the
+// filled routes' gate_up rows share the host link while the hits' rows stream from HBM.
+template <int FMT, int CPL>
+__global__ void __launch_bounds__(kThreads)
+gate_up_fill_tok1_kernel(DecodeArgs a, FillSegs g, int n_copy) {
+  const int b = blockIdx.x;
+  if (b < n_copy) {
+    const int chunks = g.chunk0[4];
+    const int i = b / chunks;
+    if (i >= min(*a.n_fill, a.kcap)) return;
+    fill_chunk(g, a.fill_flat[i], a.fill_slot[i], b - i * chunks);
+    return;
+  }
+  const int nu = a.k + a.has_shared, j = b - n_copy;
+  gate_up_tok1_role<FMT, CPL>(a, j % nu, j / nu);
 }
 
 // down for one token: workgroup = ROWS hidden rows over every route of the token.  The
@@ -1142,6 +1178,21 @@ static bool launch_gate_up_tok1(const DecodeArgs& a, int cpl, dim3 grid, hipStre
   }
 }
 
+template <int FMT>
+static bool launch_gate_up_fill_tok1(const DecodeArgs& a, int cpl, const FillSegs& g, int n_copy, int n_gu,
+                                     hipStream_t s) {
+  const dim3 grid(n_copy + n_gu);
+  switch (cpl) {
+    case 1: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a, g, n_copy);
+            return true;
+    case 2: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a, g, n_copy);
+            return true;
+    case 4: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a, g, n_copy);
+            return true;
+    default: return false;
+  }
+}
+
 template <int FMT, int LPR>
 static bool launch_down_tok1_l(const DecodeArgs& a, int cplb, dim3 grid, size_t lds, hipStream_t s) {
   if (cplb == 1) hipLaunchKernelGGL((down_tok1_kernel<FMT, LPR, 1, 8>), grid, dim3(kThreads), lds, s, a);
@@ -1318,10 +1369,23 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
     a.fill_slot = fill->fill_slot;
     a.n_fill = fill->n_fill;
     a.kcap = fill->kcap;
-    MC_REQUIRE(fill->gate_up_only == 0 || fill->gate_up_only == 1,
-               "moe_experts_decode: fill gate_up_only=%d", fill->gate_up_only);
-    if (fill->gate_up_only) a.f_dn = a.f_dns = nullptr;   // down reads the slots
+    MC_REQUIRE(fill->mode == MC_FILL_THROUGH || fill->mode == MC_FILL_GATE_UP ||
+                   fill->mode == MC_FILL_WITH_GATE_UP,
+               "moe_experts_decode: fill mode=%d", fill->mode);
+    if (fill->mode != MC_FILL_THROUGH) a.f_dn = a.f_dns = nullptr;   // down reads the slots
     if (a.kcap == 0) a.f_gu = a.f_dn = nullptr;
+  }
+  // the fill's down-bank copy carried by this call (MC_FILL_WITH_GATE_UP)
+  const bool copy_down = fill && fill->mode == MC_FILL_WITH_GATE_UP && a.kcap > 0;
+  FillSegs gd{};
+  int chunks_dn = 0;
+  if (copy_down) {
+    MC_REQUIRE(fill->down_after == nullptr,
+               "moe_experts_decode: fill mode MC_FILL_WITH_GATE_UP copies the down banks itself (down_after must be NULL)");
+    MC_REQUIRE(a.kcap <= 65535, "moe_experts_decode: fill kcap=%d (0..65535)", a.kcap);
+    if ((rc = fill_segs(fill->host, pool, MC_BANK_DOWN | (fmt == MC_MXFP4 ? MC_BANK_DOWN_SCALE : 0),
+                        "moe_experts_decode fill", s, &gd, &chunks_dn)) != MC_OK)
+      return rc;
   }
 
   bool ok_a, ok_b;
@@ -1329,7 +1393,11 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
   // nv1 routes held at once), shorter rows the route-split one
   const int nvec1 = k + has_shared;
   const int nv1 = (nvec1 <= 3 || cplb1 > 1) ? 3 : (nvec1 <= 6 ? 6 : 9);
-  if (T == 1) {
+  if (T == 1 && copy_down) {
+    const int n_copy = chunks_dn * a.kcap, n_gu = (k + has_shared) * (I / 8);
+    ok_a = fmt == MC_MXFP4 ? launch_gate_up_fill_tok1<MC_MXFP4>(a, cpl1, gd, n_copy, n_gu, s)
+                           : launch_gate_up_fill_tok1<MC_BF16>(a, cpl1, gd, n_copy, n_gu, s);
+  } else if (T == 1) {
     const dim3 grid_a(k + has_shared, I / 8);
     ok_a = fmt == MC_MXFP4 ? launch_gate_up_tok1<MC_MXFP4>(a, cpl1, grid_a, s)
                            : launch_gate_up_tok1<MC_BF16>(a, cpl1, grid_a, s);
@@ -1344,6 +1412,9 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
   }
   MC_LAUNCH_CHECK();
   if (fill && fill->down_after) MC_HIP(hipStreamWaitEvent(s, fill->down_after, 0));
+  if (T > 1 && copy_down) {          // several tokens: the down-bank copy between the passes
+    if ((rc = launch_fill(gd, a.fill_flat, a.fill_slot, a.n_fill, a.kcap, s)) != MC_OK) return rc;
+  }
   if (T == 1 && lpr1 == 64) {
     const uint32_t n_dn = (uint32_t)((H + 7) / 8);
     ok_b = fmt == MC_MXFP4 ? launch_down_tok1b<MC_MXFP4>(a, cplb1, nv1, n_dn, lds1, s)

@@ -13,55 +13,62 @@
 // the XCDs in turn, so with the chunk as the fast grid index even a single fill
 // is spread over every XCD (with the entry first, one XCD carried it alone: 46
 // against 51 GB/s for one 1.67 MB expert).
+#include <cstdio>
 #include <mutex>
 
-#include "mc_common.h"
+#include "fill_dev.h"
 
 namespace mc {
-
-constexpr int kFillThreads = 256;
-constexpr int kFillUnroll = 8;                                   // 16-byte loads in flight
-constexpr int kFillChunk = kFillThreads * kFillUnroll * 16;      // 32 KiB per workgroup
-
-struct FillSegs {
-  const uint8_t* src[4];     // host (device-visible) bank bases
-  uint8_t* dst[4];           // slot bank bases
-  int64_t bytes[4];          // bytes per expert entry of each bank
-  int32_t chunk0[5];         // first chunk index of each bank
-  int64_t n_src, n_dst;
-};
 
 __global__ void __launch_bounds__(kFillThreads)
 fill_kernel(FillSegs g, const int32_t* __restrict__ fill_flat, const int32_t* __restrict__ fill_slot,
             const int32_t* __restrict__ n_fill) {
   const int i = blockIdx.y;
   if (i >= *n_fill) return;
-  const int64_t f = fill_flat[i];
-  const int64_t s = fill_slot[i];
-  if (f < 0 || f >= g.n_src || s < 0 || s >= g.n_dst) return;
-  const int c = blockIdx.x;
-  int seg = 0;
-#pragma unroll
-  for (int b = 1; b < 4; ++b)
-    if (c >= g.chunk0[b]) seg = b;
-  if (c >= g.chunk0[4] || g.bytes[seg] == 0) return;
-  const int64_t nb = g.bytes[seg];
-  const int64_t off0 = (int64_t)(c - g.chunk0[seg]) * kFillChunk;
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4* src = reinterpret_cast<const u32x4*>(g.src[seg] + f * nb + off0);
-  u32x4* dst = reinterpret_cast<u32x4*>(g.dst[seg] + s * nb + off0);
-  const int64_t n16 = min((int64_t)kFillChunk, nb - off0) / 16;
-  u32x4 v[kFillUnroll];
-#pragma unroll
-  for (int u = 0; u < kFillUnroll; ++u) {
-    int64_t j = threadIdx.x + (int64_t)u * kFillThreads;
-    if (j < n16) v[u] = __builtin_nontemporal_load(src + j);
+  fill_chunk(g, fill_flat[i], fill_slot[i], blockIdx.x);
+}
+
+int launch_fill(const FillSegs& g, const int32_t* fill_flat, const int32_t* fill_slot, const int32_t* n_fill,
+                int32_t kcap, hipStream_t s) {
+  if (kcap == 0 || g.chunk0[4] == 0) return MC_OK;
+  hipLaunchKernelGGL(fill_kernel, dim3(g.chunk0[4], kcap), dim3(kFillThreads), 0, s, g, fill_flat, fill_slot,
+                     n_fill);
+  MC_LAUNCH_CHECK();
+  return MC_OK;
+}
+
+int fill_segs(const mc_banks* host, const mc_banks* pool, uint32_t banks, const char* fn, hipStream_t s,
+              FillSegs* g, int* chunks) {
+  MC_REQUIRE(banks != 0 && (banks & ~(uint32_t)MC_BANK_ALL) == 0, "%s: bank mask 0x%x", fn, banks);
+  char what_host[96], what_pool[96];
+  snprintf(what_host, sizeof what_host, "%s host", fn);
+  snprintf(what_pool, sizeof what_pool, "%s pool", fn);
+  int rc;
+  if ((rc = check_banks(host, what_host)) != MC_OK) return rc;
+  if ((rc = check_banks(pool, what_pool)) != MC_OK) return rc;
+  MC_REQUIRE(host->fmt == pool->fmt && host->H == pool->H && host->I == pool->I,
+             "%s: host and pool banks differ in format or shape", fn);
+  BankBytes bb = bank_bytes(host->fmt, host->H, host->I);
+  *g = FillSegs{};
+  const void* hs[4] = {host->gate_up, host->gate_up_scale, host->down, host->down_scale};
+  void* ds[4] = {pool->gate_up, pool->gate_up_scale, pool->down, pool->down_scale};
+  int64_t nbytes[4] = {(int64_t)bb.gate_up, (int64_t)bb.gate_up_scale, (int64_t)bb.down,
+                       (int64_t)bb.down_scale};
+  int n = 0;
+  for (int b = 0; b < 4; ++b) {
+    g->chunk0[b] = n;
+    g->bytes[b] = (banks >> b) & 1u ? nbytes[b] : 0;    // banks left out get no chunks
+    if (g->bytes[b] == 0) continue;
+    MC_REQUIRE(nbytes[b] % 16 == 0, "%s: bank %d entry is not a multiple of 16 bytes", fn, b);
+    if ((rc = host_device_view(hs[b], &g->src[b], what_host, s)) != MC_OK) return rc;
+    g->dst[b] = static_cast<uint8_t*>(ds[b]);
+    n += (int)((nbytes[b] + kFillChunk - 1) / kFillChunk);
   }
-#pragma unroll
-  for (int u = 0; u < kFillUnroll; ++u) {
-    int64_t j = threadIdx.x + (int64_t)u * kFillThreads;
-    if (j < n16) dst[j] = v[u];
-  }
+  g->chunk0[4] = n;
+  g->n_src = host->n;
+  g->n_dst = pool->n;
+  *chunks = n;
+  return MC_OK;
 }
 
 // Device-visible address of pinned host memory.  Outside stream capture every call
@@ -147,38 +154,12 @@ extern "C" int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, c
                                    const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap,
                                    uint32_t banks, hipStream_t s) {
   clear_error();
-  MC_REQUIRE(banks != 0 && (banks & ~(uint32_t)MC_BANK_ALL) == 0, "mc_fill_slots: bank mask 0x%x", banks);
-  int rc;
-  if ((rc = check_banks(host, "mc_fill_slots host")) != MC_OK) return rc;
-  if ((rc = check_banks(pool, "mc_fill_slots pool")) != MC_OK) return rc;
-  MC_REQUIRE(host->fmt == pool->fmt && host->H == pool->H && host->I == pool->I,
-             "mc_fill_slots: host and pool banks differ in format or shape");
   MC_REQUIRE(kcap >= 0 && kcap <= 65535, "mc_fill_slots: kcap=%d (0..65535)", kcap);
   MC_REQUIRE(fill_flat && fill_slot && n_fill, "mc_fill_slots: NULL list pointer");
-  if (kcap == 0) return MC_OK;
-  BankBytes bb = bank_bytes(host->fmt, host->H, host->I);
-  FillSegs g{};
-  const void* hs[4] = {host->gate_up, host->gate_up_scale, host->down, host->down_scale};
-  void* ds[4] = {pool->gate_up, pool->gate_up_scale, pool->down, pool->down_scale};
-  int64_t nbytes[4] = {(int64_t)bb.gate_up, (int64_t)bb.gate_up_scale, (int64_t)bb.down,
-                       (int64_t)bb.down_scale};
-  int chunks = 0;
-  for (int b = 0; b < 4; ++b) {
-    g.chunk0[b] = chunks;
-    g.bytes[b] = (banks >> b) & 1u ? nbytes[b] : 0;    // banks left out get no chunks
-    if (g.bytes[b] == 0) continue;
-    MC_REQUIRE(nbytes[b] % 16 == 0, "mc_fill_slots: bank %d entry is not a multiple of 16 bytes", b);
-    if ((rc = host_device_view(hs[b], &g.src[b], "mc_fill_slots: host bank", s)) != MC_OK) return rc;
-    g.dst[b] = static_cast<uint8_t*>(ds[b]);
-    chunks += (int)((nbytes[b] + kFillChunk - 1) / kFillChunk);
-  }
-  g.chunk0[4] = chunks;
-  g.n_src = host->n;
-  g.n_dst = pool->n;
-  hipLaunchKernelGGL(fill_kernel, dim3(chunks, kcap), dim3(kFillThreads), 0, s, g, fill_flat,
-                     fill_slot, n_fill);
-  MC_LAUNCH_CHECK();
-  return MC_OK;
+  FillSegs g;
+  int chunks = 0, rc;
+  if ((rc = fill_segs(host, pool, banks, "mc_fill_slots", s, &g, &chunks)) != MC_OK) return rc;
+  return launch_fill(g, fill_flat, fill_slot, n_fill, kcap, s);
 }
 
 extern "C" int mc_host_forget(const void* p, size_t bytes) {

@@ -4,7 +4,8 @@ torch allocates every buffer (device tensors, pinned host tensors) and provides 
 stream; each step of the path is one call into ``libmc.so``:
 
   moe_route_lookup (= moe_route + slot_cache_lookup_evict) -> [hybrid_split_merge(SPLIT)]
-            -> mc_fill_slots -> moe_experts_decode -> [hybrid_split_merge(MERGE)]
+            -> moe_experts_decode (its gate_up launch also carries the fill of the chosen
+               misses, mc_fill_slots) -> [hybrid_split_merge(MERGE)]
 
 which follows [jjl357] "6.8 CPU 与 GPU 并发执行的顺序" and [wanger] "代码全链路":
 the host branch is started before the fills and the GPU experts, and the two
@@ -109,7 +110,7 @@ class DecodeLayer:
     def __init__(self, cache: CacheState, host: BankSet, pool: BankSet, shared: Optional[BankSet],
                  bufs: DecodeBuffers, frac_q16: int = 1 << 16, fixed_cap: int = 1, min_fill: int = 1,
                  renorm: int = 1, hybrid: bool = False, host_pool: Optional[L.HostPool] = None,
-                 fill_mode: str = "copy"):
+                 fill_mode: str = "fused"):
         self.cache, self.host, self.pool, self.shared, self.b = cache, host, pool, shared, bufs
         self.frac_q16, self.fixed_cap, self.min_fill, self.renorm = frac_q16, fixed_cap, min_fill, renorm
         self.hybrid = hybrid
@@ -124,8 +125,10 @@ class DecodeLayer:
         #   through the expert pass reads the filled experts from the host and writes the slots
         #   split   the gate_up pass fills through its banks while mc_fill_slots_banks copies
         #           the down banks on a side stream; the down pass waits for that copy
-        if fill_mode not in ("copy", "through", "split"):
-            raise ValueError("fill_mode must be copy, through or split")
+        #   fused   the gate_up pass fills through its banks and its launch also copies the
+        #           down banks (one launch, one stream); the down pass reads the slots
+        if fill_mode not in ("copy", "through", "split", "fused"):
+            raise ValueError("fill_mode must be copy, through, split or fused")
         self.fill_mode = fill_mode
         self.fill = None
         if fill_mode == "split":
@@ -134,9 +137,12 @@ class DecodeLayer:
             self.ev_fill = torch.cuda.Event()
             self.ev_fill.record()            # creates the event, so its handle can go in the list
             self.fill = L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill,
-                                         gate_up_only=True, down_after=self.ev_fill)
+                                         mode=L.MC_FILL_GATE_UP, down_after=self.ev_fill)
         elif fill_mode == "through":
             self.fill = L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill)
+        elif fill_mode == "fused":
+            self.fill = L.make_fill_list(host.desc, bufs.fill_flat, bufs.fill_slot, bufs.n_fill,
+                                         mode=L.MC_FILL_WITH_GATE_UP)
         if hybrid:
             self.stage = L.HybridStage(bufs.T, bufs.k, bufs.H)
         self._hy = {}

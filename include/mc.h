@@ -235,8 +235,8 @@ enum { MC_BANK_GATE_UP = 1, MC_BANK_GATE_UP_SCALE = 2, MC_BANK_DOWN = 4, MC_BANK
 /*
  * mc_fill_slots restricted to the banks in `banks` (a nonzero mask of MC_BANK_*): the
  * other banks of the slots are left as they are.  Used with a gate_up-only
- * fill-through pass (mc_fill_list.gate_up_only), which writes the gate_up banks while
- * this copies the down banks on another stream.
+ * fill-through pass (mc_fill_list.mode = MC_FILL_GATE_UP), which writes the gate_up
+ * banks while this copies the down banks on another stream.
  */
 int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, const int32_t* fill_flat,
                         const int32_t* fill_slot, const int32_t* n_fill, int32_t kcap,
@@ -254,17 +254,25 @@ int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, const int32_
  * pool).  Entries with a flat id outside [0, host->n) are ignored (the route then
  * reads its slot as usual).
  */
+enum { MC_FILL_THROUGH = 0, MC_FILL_GATE_UP = 1, MC_FILL_WITH_GATE_UP = 2 };
+
 typedef struct {
   const mc_banks* host;
   const int32_t* fill_flat;  /* [kcap] */
   const int32_t* fill_slot;  /* [kcap] */
   const int32_t* n_fill;     /* [1]    */
   int32_t kcap;
-  /* 1: only the gate_up pass reads the host and writes the gate_up banks; the down pass
-   * reads the slots, whose down banks the caller fills (mc_fill_slots_banks with
-   * MC_BANK_DOWN | MC_BANK_DOWN_SCALE, e.g. on another stream, concurrently with the
-   * gate_up pass).  0: both passes fill through. */
-  int32_t gate_up_only;
+  /* MC_FILL_THROUGH: both passes read the host and fill through.
+   * MC_FILL_GATE_UP: only the gate_up pass reads the host and writes the gate_up banks;
+   *   the down pass reads the slots, whose down banks the caller fills
+   *   (mc_fill_slots_banks with MC_BANK_DOWN | MC_BANK_DOWN_SCALE, e.g. on another
+   *   stream, concurrently with the gate_up pass).
+   * MC_FILL_WITH_GATE_UP: the gate_up pass fills through its banks and its launch also
+   *   copies the down banks of every listed entry (workgroups of their own beside the
+   *   gate_up workgroups), so the down pass reads the slots; one token per call gets the
+   *   single launch, several tokens a separate copy between the two passes.  The caller
+   *   runs no mc_fill_slots. */
+  int32_t mode;
   /* NULL, or an event the down pass waits for (the caller's down-bank fill) */
   hipEvent_t down_after;
 } mc_fill_list;

@@ -169,7 +169,8 @@ def _step_oracle(cfg, o, layer, ids, w, x, banks, frac, shared=None):
 
 
 @pytest.mark.parametrize("frac,fill_mode", [(1 << 16, "copy"), (1 << 15, "copy"), (1 << 16, "through"),
-                                            (1 << 15, "through"), (1 << 15, "split")])
+                                            (1 << 15, "through"), (1 << 15, "split"), (1 << 16, "fused"),
+                                            (1 << 15, "fused")])
 def test_tiny_trace_end_to_end(frac, fill_mode):
     """The tiny config through route -> lookup -> split -> fill -> experts -> merge, every step
     (4 slots for up to 8 unique experts: overflow misses run on the host branch)."""
@@ -209,10 +210,12 @@ def test_tiny_trace_end_to_end(frac, fill_mode):
     hp.close()
 
 
-@pytest.mark.parametrize("ratio,p", [(1.5, 0.5), (2.0, 0.5), (1.5, 0.9), (3.0, 0.9)])
-def test_dsv4_shaped_hybrid_steps(ratio, p):
+@pytest.mark.parametrize("ratio,p,fill_mode", [(1.5, 0.5, "copy"), (2.0, 0.5, "copy"), (1.5, 0.9, "copy"),
+                                               (3.0, 0.9, "copy"), (2.0, 0.9, "fused")])
+def test_dsv4_shaped_hybrid_steps(ratio, p, fill_mode):
     """DeepSeek-V4-Flash expert shapes (H 4096, I 2048, MXFP4, top-6) on a reduced pool of
-    E=16 experts x 3 layers, split by q* with B_H/B_P = ratio; y against the unsplit layer."""
+    E=16 experts x 3 layers, split by q* with B_H/B_P = ratio; y against the unsplit layer
+    (fills copied first, or carried by the gate_up launch)."""
     from expert_cache_offloaded_amd import HostPool, fetch_fraction_q16
     from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer
     from oracle import route
@@ -226,7 +229,7 @@ def test_dsv4_shaped_hybrid_steps(ratio, p):
     frac = fetch_fraction_q16(1.0, ratio)
     hp = HostPool(4)
     dl = DecodeLayer(cs, host, pool, None, DecodeBuffers(1, cfg.k, cfg.H, cfg.I), frac_q16=frac,
-                     hybrid=True, host_pool=hp)
+                     hybrid=True, host_pool=hp, fill_mode=fill_mode)
     o = LruOracle(cfg.L, cfg.E, cfg.S)
     x_dev = torch.empty((1, cfg.H), dtype=torch.int16, device="cuda")
     for s in range(cfg.steps):
@@ -337,13 +340,14 @@ def test_hybrid_stage_must_be_coherent():
     hp.close()
 
 
-@pytest.mark.parametrize("cname,T,steps", [("qwen_decode", 1, 4), ("zipf_decode", 4, 3)])
+@pytest.mark.parametrize("cname,T,steps", [("qwen_decode", 1, 4), ("zipf_decode", 4, 3), ("dsv4_hybrid", 1, 2)])
 def test_fill_through_equals_fill_then_decode(cname, T, steps):
     """Fill-through (the expert pass reads filled experts from the host and writes their
-    slots) and the split form (gate_up fills through while the down banks are copied on a
-    side stream) against the separate fill copy followed by the expert pass: outputs,
-    slots and every resident pool byte identical after each layer call; outputs against
-    the oracle."""
+    slots), the split form (gate_up fills through while the down banks are copied on a
+    side stream) and the fused form (gate_up fills through, the down banks copied by
+    workgroups of the same launch) against the separate fill copy followed by the expert
+    pass: outputs, slots and every resident pool byte identical after each layer call;
+    outputs against the oracle."""
     from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer
     from oracle import route
     # S >= T*k keeps every miss fillable (no overflow to the host set)
@@ -355,7 +359,7 @@ def test_fill_through_equals_fill_then_decode(cname, T, steps):
     shared = (BankSet({k: t_of(v).cuda() for k, v in sh_np.items()}, cfg.H, cfg.I, cfg.fmt)
               if sh_np is not None else None)
     runs = []
-    for mode in ("through", "split", "copy"):
+    for mode in ("through", "split", "fused", "copy"):
         pool = BankSet(empty_device_banks(cfg, cfg.S), cfg.H, cfg.I, cfg.fmt)
         cs = CacheState(cfg.L, cfg.E, cfg.S)
         cs.reset()

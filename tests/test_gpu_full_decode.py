@@ -1,7 +1,8 @@
 """GPU parity at full size, in the launch configuration bench.py times: the Qwen3.6-shaped
 decode (40 MoE layers, E=256 top-8 + one shared expert, H 2048, I 512, MXFP4, bs 1, an LRU
 pool of 600 of the 10 240 slots, locality 0.8), one captured hipGraph per 40-layer step,
-replayed with each step's logits and activations copied in.
+replayed with each step's logits and activations copied in; the fills carried by the gate_up
+launch (the default) and copied by their own kernel first.
 
 After every replay: every layer's slot rewrite and the whole cache state (slot_of, id_of,
 stamp, clock, stats) against the oracle LRU, bit for bit, and the bf16 outputs of four
@@ -34,15 +35,24 @@ def _pinned_pool(cfg):
     return banks, views
 
 
-def test_qwen_shaped_decode_graph_full_size():
+@pytest.fixture(scope="module")
+def qwen_host():
+    """The Qwen-shaped host banks (10 240 experts, 17 GB pinned), built once for the module."""
+    cfg = synth.CONFIGS["qwen_decode"]
+    host_t, host_np = _pinned_pool(cfg)
+    yield cfg, host_t, host_np
+    del host_t, host_np
+
+
+@pytest.mark.parametrize("fill_mode", ["fused", "copy"])
+def test_qwen_shaped_decode_graph_full_size(qwen_host, fill_mode):
     from expert_cache_offloaded_amd.runtime import BankSet, CacheState, DecodeBuffers, DecodeLayer, alloc_banks
     from oracle import route
-    cfg = synth.CONFIGS["qwen_decode"]
+    cfg, host_t, host_np = qwen_host
     steps = 8                  # 320 experts at step 0, ~64 new per step: the 600 slots wrap
     tr = synth.trace(cfg, steps=steps)
     logits = np.stack([synth.step_logits(cfg, tr[s], s) for s in range(steps)])          # [S, L, 1, E]
     xs = np.stack([np.stack([synth.activations(cfg, s, l) for l in range(cfg.L)]) for s in range(steps)])
-    host_t, host_np = _pinned_pool(cfg)
     host = BankSet(host_t, cfg.H, cfg.I, cfg.fmt)
     sh_np = synth.shared_pool(cfg)
     shared = BankSet({k: torch.from_numpy(v).cuda() for k, v in sh_np.items()}, cfg.H, cfg.I, cfg.fmt)
@@ -50,7 +60,7 @@ def test_qwen_shaped_decode_graph_full_size():
     cache = CacheState(cfg.L, cfg.E, cfg.S)
     cache.reset()
     layers = [DecodeLayer(cache, host, pool, shared, DecodeBuffers(1, cfg.k, cfg.H, cfg.I),
-                          frac_q16=1 << 16, renorm=cfg.renorm) for _ in range(cfg.L)]
+                          frac_q16=1 << 16, renorm=cfg.renorm, fill_mode=fill_mode) for _ in range(cfg.L)]
     logits_buf = torch.from_numpy(logits[0]).cuda()
     x_buf = torch.from_numpy(xs[0].view(np.int16)).cuda()
 
