@@ -589,24 +589,26 @@ gate_up_tok1_kernel(DecodeArgs a) {
   gate_up_tok1_role<FMT, CPL>(a, blockIdx.x, blockIdx.y);
 }
 
-// The same pass with the fill's down-bank copy in the launch: the first n_copy
-// workgroups copy chunk (j mod chunks) of fill entry (j / chunks) into its slot (the
-// fill kernel's loop, entries beyond *n_fill skipped), the rest run the gate_up
-// workgroups (route fastest), which fill through the gate_up banks.  The copies and the
-// filled routes' gate_up rows share the host link while the hits' rows stream from HBM.
+// The same pass with the fill's down-bank copy in the launch: the first n_gu workgroups
+// run the gate_up workgroups (route fastest), which fill through the gate_up banks, and
+// the last n_copy copy chunk (j mod chunks) of fill entry (j / chunks) into its slot (the
+// fill kernel's loop, entries beyond *n_fill skipped).  The copies and the filled routes'
+// gate_up rows share the host link while the hits' rows stream from HBM.  Workgroups are
+// dispatched in order; with the copies last the Qwen-shaped decode step took 2.66
+// against 2.74 ms (copies first), on one box in one run.
 template <int FMT, int CPL>
 __global__ void __launch_bounds__(kThreads)
-gate_up_fill_tok1_kernel(DecodeArgs a, FillSegs g, int n_copy) {
+gate_up_fill_tok1_kernel(DecodeArgs a, FillSegs g, int n_gu) {
   const int b = blockIdx.x;
-  if (b < n_copy) {
+  if (b >= n_gu) {
     const int chunks = g.chunk0[4];
-    const int i = b / chunks;
+    const int i = (b - n_gu) / chunks;
     if (i >= min(*a.n_fill, a.kcap)) return;
-    fill_chunk(g, a.fill_flat[i], a.fill_slot[i], b - i * chunks);
+    fill_chunk(g, a.fill_flat[i], a.fill_slot[i], b - n_gu - i * chunks);
     return;
   }
-  const int nu = a.k + a.has_shared, j = b - n_copy;
-  gate_up_tok1_role<FMT, CPL>(a, j % nu, j / nu);
+  const int nu = a.k + a.has_shared;
+  gate_up_tok1_role<FMT, CPL>(a, b % nu, b / nu);
 }
 
 // down for one token: workgroup = ROWS hidden rows over every route of the token.  The
@@ -1183,11 +1185,11 @@ static bool launch_gate_up_fill_tok1(const DecodeArgs& a, int cpl, const FillSeg
                                      hipStream_t s) {
   const dim3 grid(n_copy + n_gu);
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a, g, n_copy);
+    case 1: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a, g, n_gu);
             return true;
-    case 2: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a, g, n_copy);
+    case 2: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a, g, n_gu);
             return true;
-    case 4: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a, g, n_copy);
+    case 4: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a, g, n_gu);
             return true;
     default: return false;
   }
