@@ -490,7 +490,7 @@ __device__ __forceinline__ float dot_chunk_bf_f32(const u32x4_t& w, const float*
 template <int FMT, int CPL>
 __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, int ib) {
   const int k = a.k;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;   // wave of its 256-thread group
   const bool shared_unit = a.has_shared && u == k;
   const int slot_raw = shared_unit ? -1 : a.slots[u];
   if (valid_tokens(a) == 0) return;
@@ -519,7 +519,7 @@ __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, in
       gu = a.f_gu + (size_t)src * per_gu;
       if (FMT == MC_MXFP4) gus = a.f_gus + (size_t)src * per_gus;
     }
-    if (ib == 0 && threadIdx.x == 0) a.rsrc[u] = (int32_t)src;
+    if (ib == 0 && (threadIdx.x & (kThreads - 1)) == 0) a.rsrc[u] = (int32_t)src;
   }
   const int i0 = ib * 8 + wave * 2;
   int cq[CPL];
@@ -589,26 +589,29 @@ gate_up_tok1_kernel(DecodeArgs a) {
   gate_up_tok1_role<FMT, CPL>(a, blockIdx.x, blockIdx.y);
 }
 
-// The same pass with the fill's down-bank copy in the launch: the first n_gu workgroups
-// run the gate_up workgroups (route fastest), which fill through the gate_up banks, and
-// the last n_copy copy chunk (j mod chunks) of fill entry (j / chunks) into its slot (the
-// fill kernel's loop, entries beyond *n_fill skipped).  The copies and the filled routes'
-// gate_up rows share the host link while the hits' rows stream from HBM.  Workgroups are
-// dispatched in order; with the copies last the Qwen-shaped decode step took 2.66
-// against 2.74 ms (copies first), on one box in one run.
-template <int FMT, int CPL>
-__global__ void __launch_bounds__(kThreads)
+// The same pass with the fill's down-bank copy in the launch.  A workgroup of
+// kFusedThreads threads runs four 256-thread groups: group v < n_gu is gate_up group
+// (route v mod nu, row block v / nu), which fills through its gate_up banks, and the
+// groups after n_gu copy chunk (j mod chunks) of fill entry (j / chunks) into its slot's
+// down banks (the fill kernel's loop, entries beyond *n_fill skipped).  The copies and
+// the filled routes' gate_up rows share the host link while the hits' rows stream from
+// HBM.  Measured on the Qwen-shaped decode step (one box, A/B in one run each): the
+// copies after the gate_up groups 2.66 against 2.74 ms with them first; 1024-thread
+// workgroups 2.64-2.66 against 2.67-2.68 ms with 256-thread ones.  NT: threads per
+// workgroup (256 for CPL 4, whose registers do not fit four waves per SIMD).
+template <int FMT, int CPL, int NT>
+__global__ void __launch_bounds__(NT)
 gate_up_fill_tok1_kernel(DecodeArgs a, FillSegs g, int n_gu) {
-  const int b = blockIdx.x;
-  if (b >= n_gu) {
+  const int v = (int)blockIdx.x * (NT / kThreads) + (int)(threadIdx.x / kThreads);
+  if (v >= n_gu) {
     const int chunks = g.chunk0[4];
-    const int i = (b - n_gu) / chunks;
+    const int i = (v - n_gu) / chunks;
     if (i >= min(*a.n_fill, a.kcap)) return;
-    fill_chunk(g, a.fill_flat[i], a.fill_slot[i], b - n_gu - i * chunks);
+    fill_chunk(g, a.fill_flat[i], a.fill_slot[i], v - n_gu - i * chunks);
     return;
   }
   const int nu = a.k + a.has_shared;
-  gate_up_tok1_role<FMT, CPL>(a, b % nu, b / nu);
+  gate_up_tok1_role<FMT, CPL>(a, v % nu, v / nu);
 }
 
 // down for one token: workgroup = ROWS hidden rows over every route of the token.  The
@@ -1183,13 +1186,16 @@ static bool launch_gate_up_tok1(const DecodeArgs& a, int cpl, dim3 grid, hipStre
 template <int FMT>
 static bool launch_gate_up_fill_tok1(const DecodeArgs& a, int cpl, const FillSegs& g, int n_copy, int n_gu,
                                      hipStream_t s) {
-  const dim3 grid(n_copy + n_gu);
+  const int n = n_copy + n_gu;
   switch (cpl) {
-    case 1: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 1>), grid, dim3(kThreads), 0, s, a, g, n_gu);
+    case 1: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 1, 1024>), dim3((n + 3) / 4), dim3(1024), 0, s, a, g,
+                               n_gu);
             return true;
-    case 2: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 2>), grid, dim3(kThreads), 0, s, a, g, n_gu);
+    case 2: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 2, 1024>), dim3((n + 3) / 4), dim3(1024), 0, s, a, g,
+                               n_gu);
             return true;
-    case 4: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 4>), grid, dim3(kThreads), 0, s, a, g, n_gu);
+    case 4: hipLaunchKernelGGL((gate_up_fill_tok1_kernel<FMT, 4, kThreads>), dim3(n), dim3(kThreads), 0, s, a, g,
+                               n_gu);
             return true;
     default: return false;
   }
