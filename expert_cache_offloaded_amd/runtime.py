@@ -110,7 +110,7 @@ class DecodeLayer:
     def __init__(self, cache: CacheState, host: BankSet, pool: BankSet, shared: Optional[BankSet],
                  bufs: DecodeBuffers, frac_q16: int = 1 << 16, fixed_cap: int = 1, min_fill: int = 1,
                  renorm: int = 1, hybrid: bool = False, host_pool: Optional[L.HostPool] = None,
-                 fill_mode: str = "fused"):
+                 fill_mode: Optional[str] = None):
         self.cache, self.host, self.pool, self.shared, self.b = cache, host, pool, shared, bufs
         self.frac_q16, self.fixed_cap, self.min_fill, self.renorm = frac_q16, fixed_cap, min_fill, renorm
         self.hybrid = hybrid
@@ -127,6 +127,10 @@ class DecodeLayer:
         #           the down banks on a side stream; the down pass waits for that copy
         #   fused   the gate_up pass fills through its banks and its launch also copies the
         #           down banks (one launch, one stream); the down pass reads the slots
+        # default: fused for one token (the measured fastest), copy for several (their gate_up
+        # pass runs on the matrix cores, which would wait on host reads)
+        if fill_mode is None:
+            fill_mode = "fused" if bufs.T == 1 else "copy"
         if fill_mode not in ("copy", "through", "split", "fused"):
             raise ValueError("fill_mode must be copy, through, split or fused")
         self.fill_mode = fill_mode
