@@ -607,7 +607,7 @@ gate_up_fill_tok1_kernel(DecodeArgs a, FillSegs g, int n_gu) {
     const int chunks = g.chunk0[4];
     const int i = (v - n_gu) / chunks;
     if (i >= min(*a.n_fill, a.kcap)) return;
-    fill_chunk(g, a.fill_flat[i], a.fill_slot[i], v - n_gu - i * chunks);
+    fill_chunk<kFusedCopyUnroll>(g, a.fill_flat[i], a.fill_slot[i], v - n_gu - i * chunks);
     return;
   }
   const int nu = a.k + a.has_shared;
@@ -1391,8 +1391,11 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
     MC_REQUIRE(fill->down_after == nullptr,
                "moe_experts_decode: fill mode MC_FILL_WITH_GATE_UP copies the down banks itself (down_after must be NULL)");
     MC_REQUIRE(a.kcap <= 65535, "moe_experts_decode: fill kcap=%d (0..65535)", a.kcap);
+    // one token: copy groups in the gate_up launch; several: the fill kernel between the passes
+    const int unroll = T == 1 ? kFusedCopyUnroll : kFillUnroll;
     if ((rc = fill_segs(fill->host, pool, MC_BANK_DOWN | (fmt == MC_MXFP4 ? MC_BANK_DOWN_SCALE : 0),
-                        "moe_experts_decode fill", s, &gd, &chunks_dn)) != MC_OK)
+                        (int64_t)kFillThreads * unroll * 16, "moe_experts_decode fill", s, &gd, &chunks_dn)) !=
+        MC_OK)
       return rc;
   }
 

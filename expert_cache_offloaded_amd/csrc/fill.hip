@@ -25,7 +25,7 @@ fill_kernel(FillSegs g, const int32_t* __restrict__ fill_flat, const int32_t* __
             const int32_t* __restrict__ n_fill) {
   const int i = blockIdx.y;
   if (i >= *n_fill) return;
-  fill_chunk(g, fill_flat[i], fill_slot[i], blockIdx.x);
+  fill_chunk<kFillUnroll>(g, fill_flat[i], fill_slot[i], blockIdx.x);
 }
 
 int launch_fill(const FillSegs& g, const int32_t* fill_flat, const int32_t* fill_slot, const int32_t* n_fill,
@@ -37,8 +37,8 @@ int launch_fill(const FillSegs& g, const int32_t* fill_flat, const int32_t* fill
   return MC_OK;
 }
 
-int fill_segs(const mc_banks* host, const mc_banks* pool, uint32_t banks, const char* fn, hipStream_t s,
-              FillSegs* g, int* chunks) {
+int fill_segs(const mc_banks* host, const mc_banks* pool, uint32_t banks, int64_t chunk_bytes, const char* fn,
+              hipStream_t s, FillSegs* g, int* chunks) {
   MC_REQUIRE(banks != 0 && (banks & ~(uint32_t)MC_BANK_ALL) == 0, "%s: bank mask 0x%x", fn, banks);
   char what_host[96], what_pool[96];
   snprintf(what_host, sizeof what_host, "%s host", fn);
@@ -62,7 +62,7 @@ int fill_segs(const mc_banks* host, const mc_banks* pool, uint32_t banks, const 
     MC_REQUIRE(nbytes[b] % 16 == 0, "%s: bank %d entry is not a multiple of 16 bytes", fn, b);
     if ((rc = host_device_view(hs[b], &g->src[b], what_host, s)) != MC_OK) return rc;
     g->dst[b] = static_cast<uint8_t*>(ds[b]);
-    n += (int)((nbytes[b] + kFillChunk - 1) / kFillChunk);
+    n += (int)((nbytes[b] + chunk_bytes - 1) / chunk_bytes);
   }
   g->chunk0[4] = n;
   g->n_src = host->n;
@@ -158,7 +158,9 @@ extern "C" int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, c
   MC_REQUIRE(fill_flat && fill_slot && n_fill, "mc_fill_slots: NULL list pointer");
   FillSegs g;
   int chunks = 0, rc;
-  if ((rc = fill_segs(host, pool, banks, "mc_fill_slots", s, &g, &chunks)) != MC_OK) return rc;
+  if ((rc = fill_segs(host, pool, banks, (int64_t)kFillThreads * kFillUnroll * 16, "mc_fill_slots", s, &g,
+                      &chunks)) != MC_OK)
+    return rc;
   return launch_fill(g, fill_flat, fill_slot, n_fill, kcap, s);
 }
 

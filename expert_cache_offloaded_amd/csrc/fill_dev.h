@@ -9,8 +9,13 @@
 namespace mc {
 
 constexpr int kFillThreads = 256;
-constexpr int kFillUnroll = 8;                                   // 16-byte loads in flight
-constexpr int kFillChunk = kFillThreads * kFillUnroll * 16;      // 32 KiB per workgroup
+// 16-byte loads in flight per thread: the fill kernel's own workgroups copy 64 KiB chunks,
+// the copy groups inside the one-token gate_up launch 32 KiB ones.  Measured with the fill
+// kernel alone in graph replays on a box whose link profiles at 46 GB/s: 1 / 2 / 4 experts
+// per call in 32.0 / 65.2 / 143.4 µs with 64 KiB chunks against 35.7 / 77.6 / 154.5 with
+// 32 KiB ones; the gate_up launch moved the same experts at 54-55 GB/s with 32 KiB copies.
+constexpr int kFillUnroll = 16;
+constexpr int kFusedCopyUnroll = 8;
 
 // The banks one copy covers: chunk c of an entry lies in bank `seg` where
 // chunk0[seg] <= c < chunk0[seg + 1]; a bank left out has bytes 0 and no chunks.
@@ -22,10 +27,12 @@ struct FillSegs {
   int64_t n_src, n_dst;
 };
 
-// Chunk c (of chunk0[4]) of host entry f into slot s, by a workgroup of kFillThreads
-// threads: every load of the chunk is issued before the first store.  Entries outside
-// the banks are skipped.
+// Chunk c (of chunk0[4], chunks of kFillThreads * UNROLL * 16 bytes) of host entry f into
+// slot s, by a group of kFillThreads threads: every load of the chunk is issued before the
+// first store.  Entries outside the banks are skipped.
+template <int UNROLL>
 __device__ __forceinline__ void fill_chunk(const FillSegs& g, int64_t f, int64_t s, int c) {
+  constexpr int kFillChunk = kFillThreads * UNROLL * 16;
   if (f < 0 || f >= g.n_src || s < 0 || s >= g.n_dst) return;
   int seg = 0;
 #pragma unroll
@@ -40,25 +47,25 @@ __device__ __forceinline__ void fill_chunk(const FillSegs& g, int64_t f, int64_t
   const int tid = threadIdx.x % kFillThreads;
   // every load is issued (indexes past the chunk's end re-read its last word), so all
   // of them are in flight together; only the stores are conditional
-  u32x4_t v[kFillUnroll];
+  u32x4_t v[UNROLL];
 #pragma unroll
-  for (int u = 0; u < kFillUnroll; ++u) {
+  for (int u = 0; u < UNROLL; ++u) {
     const int j = tid + u * kFillThreads;
     v[u] = __builtin_nontemporal_load(src + min((int64_t)j, n16 - 1));
   }
 #pragma unroll
-  for (int u = 0; u < kFillUnroll; ++u) {
+  for (int u = 0; u < UNROLL; ++u) {
     const int j = tid + u * kFillThreads;
     if (j < n16) dst[j] = v[u];
   }
 }
 
 // Host side: the segments of a copy of the banks in `banks` (MC_BANK_* mask) from the
-// pinned host banks into the pool banks, and the chunks per entry (0 if no bank has
-// bytes).  Checks both descriptors and the host banks' pinning; MC_OK or an error with
-// its message set.
-int fill_segs(const mc_banks* host, const mc_banks* pool, uint32_t banks, const char* fn, hipStream_t s,
-              FillSegs* g, int* chunks);
+// pinned host banks into the pool banks in chunks of chunk_bytes, and the chunks per entry
+// (0 if no bank has bytes).  Checks both descriptors and the host banks' pinning; MC_OK
+// or an error with its message set.
+int fill_segs(const mc_banks* host, const mc_banks* pool, uint32_t banks, int64_t chunk_bytes, const char* fn,
+              hipStream_t s, FillSegs* g, int* chunks);
 // Host side: the fill kernel over list entries [0, min(*n_fill, kcap)) with segments g
 // (nothing when g has no chunks or kcap is 0).
 int launch_fill(const FillSegs& g, const int32_t* fill_flat, const int32_t* fill_slot, const int32_t* n_fill,
