@@ -340,8 +340,9 @@ def test_hybrid_stage_must_be_coherent():
     hp.close()
 
 
-@pytest.mark.parametrize("cname,T,steps", [("qwen_decode", 1, 4), ("zipf_decode", 4, 3), ("dsv4_hybrid", 1, 2)])
-def test_fill_through_equals_fill_then_decode(cname, T, steps):
+@pytest.mark.parametrize("cname,T,steps,fmt", [("qwen_decode", 1, 4, None), ("zipf_decode", 4, 3, None),
+                                               ("dsv4_hybrid", 1, 2, None), ("qwen_decode", 1, 3, "bf16")])
+def test_fill_through_equals_fill_then_decode(cname, T, steps, fmt):
     """Fill-through (the expert pass reads filled experts from the host and writes their
     slots), the split form (gate_up fills through while the down banks are copied on a
     side stream) and the fused form (gate_up fills through, the down banks copied by
@@ -352,6 +353,8 @@ def test_fill_through_equals_fill_then_decode(cname, T, steps):
     from oracle import route
     # S >= T*k keeps every miss fillable (no overflow to the host set)
     cfg = synth.CONFIGS[cname].with_(L=3, E=32, S=max(14, T * 8 + 6), steps=steps, T=T)
+    if fmt is not None:            # bf16 rows of H = 2048: the widest one-token gate_up rows
+        cfg = cfg.with_(fmt=fmt)
     tr = synth.trace(cfg)
     host_np = synth.host_pool(cfg)
     host = BankSet(pinned_banks(cfg, host_np), cfg.H, cfg.I, cfg.fmt)
