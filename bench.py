@@ -28,6 +28,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 63.0       # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b encoding
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_pmc.txt")
 # kernels of each measured entry point and the source file they are built from
@@ -380,6 +381,61 @@ def tiny_layer(torch, L, synth, steps=64):
             "hits": int(st[0]), "misses": int(st[1]), "fills": int(st[2]), "host_routes": int(st[3])}
 
 
+def link_roofline(torch, L, synth, cfg, host, pool, shared_desc, x, calls=20, n_fill=2):
+    """The decode step's dominant kernel, the one-token gate_up launch that carries the
+    fills, against the host link: graph replays of moe_experts_decode with n_fill experts
+    filled in that launch (the rest of the routes resident) and with none; the time the
+    fills add, per filled expert, gives the link rate the launch reaches.  The slots the
+    fills write are overwritten (pool contents are not used after this point)."""
+    rng = np.random.default_rng(7)
+    k, dev = cfg.k, "cuda"
+    S_e = synth.expert_bytes(cfg.H, cfg.I, cfg.fmt)
+    w = torch.full((1, k), 1.0 / k, dtype=torch.float32, device=dev)
+    y = torch.empty((1, cfg.H), dtype=torch.float32, device=dev)
+    yb = torch.empty((1, cfg.H), dtype=torch.int16, device=dev)
+    ws = torch.zeros(L.decode_ws_bytes(1, k, cfg.H, cfg.I) // 4 + 4, dtype=torch.float32, device=dev)
+    us = {}
+    for n in (0, n_fill):
+        keep = []
+        for c in range(calls):
+            sl = rng.choice(pool.n, k, replace=False).astype(np.int32)
+            fl = np.full(k, -1, np.int32)
+            fl[:n] = rng.choice(host.n, n, replace=False)
+            fs = np.full(k, -1, np.int32)
+            fs[:n] = sl[:n]
+            ff, fsl = torch.tensor(fl, device=dev), torch.tensor(fs, device=dev)
+            nf = torch.tensor([n], dtype=torch.int32, device=dev)
+            keep.append((torch.tensor(sl.reshape(1, k), device=dev),
+                         L.make_fill_list(host.desc, ff, fsl, nf, mode=L.MC_FILL_WITH_GATE_UP), ff, fsl, nf))
+
+        def run():
+            for slots, fill, *_ in keep:
+                L.moe_experts_decode(x, slots, w, None, pool.desc, shared_desc, ws, y, 0, yb, fill=fill)
+        run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / calls)
+        us[n] = float(np.median(times))
+        del g
+    per_expert = (us[n_fill] - us[0]) / n_fill
+    achieved = S_e / (per_expert * 1e-6) / 1e9
+    return {"bound": "host link", "kernel": "gate_up_fill_tok1_kernel (moe_experts_decode, MC_FILL_WITH_GATE_UP)",
+            "achieved": round(achieved, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / PCIE_PEAK_GBS, 4), "us_per_filled_expert": round(per_expert, 2),
+            "bytes_per_filled_expert": S_e, "us_per_call": {str(n): round(v, 2) for n, v in us.items()}}
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -605,6 +661,12 @@ def main():
                    "expert_gemv_us_per_token": round(us_per_call * cfg.L, 2),
                    "wall_s": round(wall, 3)},
     }
+
+    # ------------------------------------------------------------------ dominant kernel vs the host link
+    out["roofline_link"] = link_roofline(torch, L, synth, cfg, host, pool, shared.entry(0).desc, x_buf[0])
+    log("gate_up launch with fills: %.2f us per filled expert -> %.1f GB/s (%.3f of %.0f GB/s)"
+        % (out["roofline_link"]["us_per_filled_expert"], out["roofline_link"]["achieved"],
+           out["roofline_link"]["frac"], PCIE_PEAK_GBS))
 
     # ------------------------------------------------------------------ other decode shapes
     log("expert pass at the other decode shapes")
