@@ -483,11 +483,18 @@ __device__ __forceinline__ float dot_chunk_bf_f32(const u32x4_t& w, const float*
   return acc;
 }
 
-// gate_up for one token: workgroup = (route column, 8 intermediate rows); each wave
-// owns 2 gate rows and the 2 matching up rows of the route's slot (or of the shared
-// expert).  Every route with a valid slot runs (a slot named twice by the token is read
-// twice, which only a malformed id list can cause).
-template <int FMT, int CPL>
+// gate_up for one token: group of 256 threads = (route column, 4 * NP intermediate rows);
+// each wave owns NP gate rows and the NP matching up rows of the route's slot (or of the
+// shared expert).  Every route with a valid slot runs (a slot named twice by the token is
+// read twice, which only a malformed id list can cause).  NP, measured on one box (A/B in
+// one run): the pass alone (HBM) is fastest with NP = 1 (Qwen shape 9.9 against 10.3 µs,
+// DeepSeek-V4-Flash shape 21.7 against 23.3 with NP = 2), the launch that also carries
+// the fills with NP = 4 for rows of one 16-B chunk per lane (58 against 54.5 GB/s over the
+// host link, 2.61 against 2.65-2.68 ms per decode token); wider rows keep NP = 2 there,
+// within the registers of four waves per SIMD.
+constexpr int kTok1NP = 1;                                     // the pass alone
+template <int CPL> constexpr int tok1_fill_np() { return CPL == 1 ? 4 : 2; }   // with the fills (no spills)
+template <int FMT, int CPL, int NP>
 __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, int ib) {
   const int k = a.k;
   const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3;   // wave of its 256-thread group
@@ -521,7 +528,7 @@ __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, in
     }
     if (ib == 0 && (threadIdx.x & (kThreads - 1)) == 0) a.rsrc[u] = (int32_t)src;
   }
-  const int i0 = ib * 8 + wave * 2;
+  const int i0 = ib * (4 * NP) + wave * NP;
   int cq[CPL];
   bool okq[CPL];
 #pragma unroll
@@ -531,11 +538,11 @@ __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, in
     cq[q] = okq[q] ? c : n_chunks - 1;
   }
   // all loads of the wave's 4 rows first, the scale bytes kept raw until every load is issued
-  u32x4_t wv[4][CPL];
-  uint32_t sb[4][CPL];
+  u32x4_t wv[2 * NP][CPL];
+  uint32_t sb[2 * NP][CPL];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = r < 2 ? i0 + r : I + i0 + r - 2;
+  for (int r = 0; r < 2 * NP; ++r) {
+    const int row = r < NP ? i0 + r : I + i0 + r - NP;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
       wv[r][q] = stream_load16(gu + (size_t)row * row_bytes + (size_t)cq[q] * 16);
@@ -543,7 +550,9 @@ __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, in
     }
   }
   const uint16_t* xrow = a.x;                                  // the one token
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[2 * NP];
+#pragma unroll
+  for (int r = 0; r < 2 * NP; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
     uint32_t xp[ELEMS / 2];
@@ -557,22 +566,20 @@ __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, in
       xp[4 * v + 3] = xx[3];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 2 * NP; ++r) {
       const u32x4_t wq = okq[q] ? wv[r][q] : u32x4_t{0, 0, 0, 0};
       acc[r] = FMT == MC_MXFP4 ? dot_chunk_mx(wq, e8m0_to_f32(sb[r][q]), xp, acc[r]) : dot_chunk_bf(wq, xp, acc[r]);
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
-  if (lane < 2) {
-    const float g = lane == 0 ? acc[0] : acc[1];
-    const float up = lane == 0 ? acc[2] : acc[3];
-    a.h32[(size_t)u * I + i0 + lane] = silu(g) * up;
-  }
+  for (int r = 0; r < 2 * NP; ++r) acc[r] = wave_sum(acc[r]);
+#pragma unroll
+  for (int r = 0; r < NP; ++r)
+    if (lane == r) a.h32[(size_t)u * I + i0 + r] = silu(acc[r]) * acc[NP + r];
   if (wb) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = r < 2 ? i0 + r : I + i0 + r - 2;
+    for (int r = 0; r < 2 * NP; ++r) {
+      const int row = r < NP ? i0 + r : I + i0 + r - NP;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
         if (!okq[q]) continue;
@@ -586,12 +593,12 @@ __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, in
 template <int FMT, int CPL>
 __global__ void __launch_bounds__(kThreads)
 gate_up_tok1_kernel(DecodeArgs a) {
-  gate_up_tok1_role<FMT, CPL>(a, blockIdx.x, blockIdx.y);
+  gate_up_tok1_role<FMT, CPL, kTok1NP>(a, blockIdx.x, blockIdx.y);
 }
 
-// The same pass with the fill's down-bank copy in the launch.  A workgroup of
-// kFusedThreads threads runs four 256-thread groups: group v < n_gu is gate_up group
-// (route v mod nu, row block v / nu), which fills through its gate_up banks, and the
+// The same pass with the fill's down-bank copy in the launch.  A workgroup of NT threads
+// runs NT / 256 groups: group v < n_gu is gate_up group (route v mod nu, row block v / nu,
+// 4 * tok1_fill_np rows), which fills through its gate_up banks, and the
 // groups after n_gu copy chunk (j mod chunks) of fill entry (j / chunks) into its slot's
 // down banks (the fill kernel's loop, entries beyond *n_fill skipped).  The copies and
 // the filled routes' gate_up rows share the host link while the hits' rows stream from
@@ -611,7 +618,7 @@ gate_up_fill_tok1_kernel(DecodeArgs a, FillSegs g, int n_gu) {
     return;
   }
   const int nu = a.k + a.has_shared;
-  gate_up_tok1_role<FMT, CPL>(a, v % nu, v / nu);
+  gate_up_tok1_role<FMT, CPL, tok1_fill_np<CPL>()>(a, v % nu, v / nu);
 }
 
 // down for one token: workgroup = ROWS hidden rows over every route of the token.  The
@@ -1405,11 +1412,12 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
   const int nvec1 = k + has_shared;
   const int nv1 = (nvec1 <= 3 || cplb1 > 1) ? 3 : (nvec1 <= 6 ? 6 : 9);
   if (T == 1 && copy_down) {
-    const int n_copy = chunks_dn * a.kcap, n_gu = (k + has_shared) * (I / 8);
+    const int np = cpl1 == 1 ? tok1_fill_np<1>() : tok1_fill_np<2>();
+    const int n_copy = chunks_dn * a.kcap, n_gu = (k + has_shared) * (I / (4 * np));
     ok_a = fmt == MC_MXFP4 ? launch_gate_up_fill_tok1<MC_MXFP4>(a, cpl1, gd, n_copy, n_gu, s)
                            : launch_gate_up_fill_tok1<MC_BF16>(a, cpl1, gd, n_copy, n_gu, s);
   } else if (T == 1) {
-    const dim3 grid_a(k + has_shared, I / 8);
+    const dim3 grid_a(k + has_shared, I / (4 * kTok1NP));
     ok_a = fmt == MC_MXFP4 ? launch_gate_up_tok1<MC_MXFP4>(a, cpl1, grid_a, s)
                            : launch_gate_up_tok1<MC_BF16>(a, cpl1, grid_a, s);
   } else {
