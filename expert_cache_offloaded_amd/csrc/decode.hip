@@ -1399,10 +1399,10 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
                "moe_experts_decode: fill mode MC_FILL_WITH_GATE_UP copies the down banks itself (down_after must be NULL)");
     MC_REQUIRE(a.kcap <= 65535, "moe_experts_decode: fill kcap=%d (0..65535)", a.kcap);
     // one token: copy groups in the gate_up launch; several: the fill kernel between the passes
-    const int unroll = T == 1 ? kFusedCopyUnroll : kFillUnroll;
-    if ((rc = fill_segs(fill->host, pool, MC_BANK_DOWN | (fmt == MC_MXFP4 ? MC_BANK_DOWN_SCALE : 0),
-                        (int64_t)kFillThreads * unroll * 16, "moe_experts_decode fill", s, &gd, &chunks_dn)) !=
-        MC_OK)
+    const int64_t chunk = T == 1 ? (int64_t)kFillThreads * kFusedCopyUnroll * 16
+                                 : (int64_t)kFillBlock * kFillUnroll * 16;
+    if ((rc = fill_segs(fill->host, pool, MC_BANK_DOWN | (fmt == MC_MXFP4 ? MC_BANK_DOWN_SCALE : 0), chunk,
+                        "moe_experts_decode fill", s, &gd, &chunks_dn)) != MC_OK)
       return rc;
   }
 

@@ -20,18 +20,18 @@
 
 namespace mc {
 
-__global__ void __launch_bounds__(kFillThreads)
+__global__ void __launch_bounds__(kFillBlock)
 fill_kernel(FillSegs g, const int32_t* __restrict__ fill_flat, const int32_t* __restrict__ fill_slot,
             const int32_t* __restrict__ n_fill) {
   const int i = blockIdx.y;
   if (i >= *n_fill) return;
-  fill_chunk<kFillUnroll>(g, fill_flat[i], fill_slot[i], blockIdx.x);
+  fill_chunk<kFillUnroll, kFillBlock>(g, fill_flat[i], fill_slot[i], blockIdx.x);
 }
 
 int launch_fill(const FillSegs& g, const int32_t* fill_flat, const int32_t* fill_slot, const int32_t* n_fill,
                 int32_t kcap, hipStream_t s) {
   if (kcap == 0 || g.chunk0[4] == 0) return MC_OK;
-  hipLaunchKernelGGL(fill_kernel, dim3(g.chunk0[4], kcap), dim3(kFillThreads), 0, s, g, fill_flat, fill_slot,
+  hipLaunchKernelGGL(fill_kernel, dim3(g.chunk0[4], kcap), dim3(kFillBlock), 0, s, g, fill_flat, fill_slot,
                      n_fill);
   MC_LAUNCH_CHECK();
   return MC_OK;
@@ -158,7 +158,7 @@ extern "C" int mc_fill_slots_banks(const mc_banks* host, const mc_banks* pool, c
   MC_REQUIRE(fill_flat && fill_slot && n_fill, "mc_fill_slots: NULL list pointer");
   FillSegs g;
   int chunks = 0, rc;
-  if ((rc = fill_segs(host, pool, banks, (int64_t)kFillThreads * kFillUnroll * 16, "mc_fill_slots", s, &g,
+  if ((rc = fill_segs(host, pool, banks, (int64_t)kFillBlock * kFillUnroll * 16, "mc_fill_slots", s, &g,
                       &chunks)) != MC_OK)
     return rc;
   return launch_fill(g, fill_flat, fill_slot, n_fill, kcap, s);

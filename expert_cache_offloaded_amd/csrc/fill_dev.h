@@ -9,12 +9,16 @@
 namespace mc {
 
 constexpr int kFillThreads = 256;
-// 16-byte loads in flight per thread: the fill kernel's own workgroups copy 64 KiB chunks,
-// the copy groups inside the one-token gate_up launch 32 KiB ones.  Measured with the fill
-// kernel alone in graph replays on a box whose link profiles at 46 GB/s: 1 / 2 / 4 experts
-// per call in 32.0 / 65.2 / 143.4 µs with 64 KiB chunks against 35.7 / 77.6 / 154.5 with
-// 32 KiB ones; the gate_up launch moved the same experts at 54-55 GB/s with 32 KiB copies.
+// The fill kernel's own workgroups: kFillBlock threads with kFillUnroll 16-byte loads in
+// flight each, one 256 KiB chunk per workgroup; the copy groups inside the one-token
+// gate_up launch: 256 threads, 32 KiB chunks.  Measured with the fill kernel alone in graph
+// replays on a box whose link profiles at 46 GB/s, time per expert beyond an empty call for
+// 1 / 2 / 4 / 8 / 62 experts per call: 256 KiB chunks of 1024 threads 33.6 / 31.0 / 30.5 /
+// 30.4 / 30.7 µs; 64 KiB chunks of 256 threads 30.9-32.1 / 32.0-32.7 / 35.5-35.9 / 35.7-36.1 /
+// 30.7-30.9; 32 KiB chunks 35.7 / 38.7 / 38.6 / 35.8 / 30.7.  The gate_up launch moved the
+// same experts at 56-59 GB/s with its 32 KiB copies.
 constexpr int kFillUnroll = 16;
+constexpr int kFillBlock = 1024;
 constexpr int kFusedCopyUnroll = 8;
 
 // The banks one copy covers: chunk c of an entry lies in bank `seg` where
@@ -27,12 +31,12 @@ struct FillSegs {
   int64_t n_src, n_dst;
 };
 
-// Chunk c (of chunk0[4], chunks of kFillThreads * UNROLL * 16 bytes) of host entry f into
-// slot s, by a group of kFillThreads threads: every load of the chunk is issued before the
-// first store.  Entries outside the banks are skipped.
-template <int UNROLL>
+// Chunk c (of chunk0[4], chunks of NTH * UNROLL * 16 bytes) of host entry f into slot s, by
+// a group of NTH threads: every load of the chunk is issued before the first store.
+// Entries outside the banks are skipped.
+template <int UNROLL, int NTH = kFillThreads>
 __device__ __forceinline__ void fill_chunk(const FillSegs& g, int64_t f, int64_t s, int c) {
-  constexpr int kFillChunk = kFillThreads * UNROLL * 16;
+  constexpr int kFillChunk = NTH * UNROLL * 16;
   if (f < 0 || f >= g.n_src || s < 0 || s >= g.n_dst) return;
   int seg = 0;
 #pragma unroll
@@ -44,18 +48,18 @@ __device__ __forceinline__ void fill_chunk(const FillSegs& g, int64_t f, int64_t
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(g.src[seg] + f * nb + off0);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(g.dst[seg] + s * nb + off0);
   const int64_t n16 = min((int64_t)kFillChunk, nb - off0) / 16;
-  const int tid = threadIdx.x % kFillThreads;
+  const int tid = threadIdx.x % NTH;
   // every load is issued (indexes past the chunk's end re-read its last word), so all
   // of them are in flight together; only the stores are conditional
   u32x4_t v[UNROLL];
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const int j = tid + u * kFillThreads;
+    const int j = tid + u * NTH;
     v[u] = __builtin_nontemporal_load(src + min((int64_t)j, n16 - 1));
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const int j = tid + u * kFillThreads;
+    const int j = tid + u * NTH;
     if (j < n16) dst[j] = v[u];
   }
 }
