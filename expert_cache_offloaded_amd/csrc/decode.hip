@@ -1374,6 +1374,9 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
                "moe_experts_decode: fill host banks differ from the pool in format or shape");
     MC_REQUIRE(fill->kcap >= 0 && fill->fill_flat && fill->fill_slot && fill->n_fill,
                "moe_experts_decode: bad fill list");
+    MC_REQUIRE(fill->mode == MC_FILL_THROUGH || fill->mode == MC_FILL_GATE_UP ||
+                   fill->mode == MC_FILL_WITH_GATE_UP,
+               "moe_experts_decode: fill mode=%d", fill->mode);
     if ((rc = host_device_view(fill->host->gate_up, &a.f_gu, "moe_experts_decode: fill host bank", s)) ||
         (rc = host_device_view(fill->host->gate_up_scale, &a.f_gus, "moe_experts_decode: fill host bank", s)) ||
         (rc = host_device_view(fill->host->down, &a.f_dn, "moe_experts_decode: fill host bank", s)) ||
@@ -1384,9 +1387,6 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
     a.fill_slot = fill->fill_slot;
     a.n_fill = fill->n_fill;
     a.kcap = fill->kcap;
-    MC_REQUIRE(fill->mode == MC_FILL_THROUGH || fill->mode == MC_FILL_GATE_UP ||
-                   fill->mode == MC_FILL_WITH_GATE_UP,
-               "moe_experts_decode: fill mode=%d", fill->mode);
     if (fill->mode != MC_FILL_THROUGH) a.f_dn = a.f_dns = nullptr;   // down reads the slots
     if (a.kcap == 0) a.f_gu = a.f_dn = nullptr;
   }

@@ -94,6 +94,17 @@ def test_validation_errors_do_not_need_a_gpu():
     assert lib.mc_fill_slots(C.byref(fb), C.byref(fb), ids, ids, ids, 65536, None) == L.MC_EINVAL
     assert "kcap" in L.last_error()
     assert lib.mc_fill_slots(C.byref(fb), C.byref(fb), ids, ids, ids, -1, None) == L.MC_EINVAL
+    # a fill list of an unknown mode is refused before any device work
+    ws_n = lib.moe_experts_decode_ws_bytes(1, 2, 64, 64)
+    ws = (C.c_uint8 * (ws_n + 16))()
+    ws_addr = (C.addressof(ws) + 15) // 16 * 16
+    fl = L.FillList()
+    fl.host = C.pointer(fb)
+    fl.fill_flat = fl.fill_slot = fl.n_fill = C.cast(ids, C.c_void_p)
+    fl.kcap, fl.mode = 2, 7
+    assert lib.moe_experts_decode(addr, ids, w, 1, 2, None, C.byref(fb), None, ws_addr, ws_n, w, 0, None, None,
+                                  C.byref(fl)) == L.MC_EINVAL
+    assert "fill mode" in L.last_error()
     assert lib.mc_host_pool_create(0, None) is None
 
 
