@@ -131,13 +131,14 @@ def pmc_summary(fetch_csv, write_csv, batch=16):
                 acc[name].append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
+    # the commands are printed with the directories the two counter files came from
+    dir_f, dir_w = os.path.dirname(fetch_csv) or ".", os.path.dirname(write_csv) or "."
     print("# HBM traffic per dispatch from rocprofv3 counters on MI355X (ROCm 7.2), made by:")
-    print("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_f -o run -- "
-          "python3 -u bench.py --pmc-workload")
-    print("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_w -o run -- "
-          "python3 -u bench.py --pmc-workload")
-    print("#   python3 bench.py --pmc-summary gpurun_out/pmc_f/run_counter_collection.csv "
-          "gpurun_out/pmc_w/run_counter_collection.csv")
+    print("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o run -- "
+          "python3 -u bench.py --pmc-workload" % dir_f)
+    print("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o run -- "
+          "python3 -u bench.py --pmc-workload" % dir_w)
+    print("#   python3 bench.py --pmc-summary %s %s" % (fetch_csv, write_csv))
     print("# 'traffic' lines: calibrated bytes per call of each entry point, keyed by the sha256 "
           "prefix of the kernel source they were taken on (bench.py reports null once it changes).")
     fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
