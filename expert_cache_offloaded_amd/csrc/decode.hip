@@ -1152,14 +1152,26 @@ down_unit_kernel(DecodeArgs a) {
       if (a.y_bf16) a.y_bf16[o] = 0;
       continue;
     }
+    // the token's partials (routes in order, then the shared expert), eight loads in
+    // flight at a time: indices past the end re-read the last one, unused
+    const int nv = k + (a.has_shared ? 1 : 0);
     float sum = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = t * k + j;
-      const int sl = a.slots[r];
-      const float v = load_coherent(a.part + (size_t)r * H + row);
-      sum += (sl >= 0 && sl < a.n_pool) ? v : 0.0f;
+    for (int j0 = 0; j0 < nv; j0 += 8) {
+      float pv[8];
+      int sl[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = min(j0 + q, nv - 1);
+        sl[q] = a.slots[t * k + min(j, k - 1)];
+        pv[q] = load_coherent(a.part + (size_t)(j < k ? t * k + j : n_all + t) * H + row);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q;
+        if (j < k) sum += (sl[q] >= 0 && sl[q] < a.n_pool) ? pv[q] : 0.0f;
+        else if (j < nv) sum += pv[q];
+      }
     }
-    if (a.has_shared) sum += load_coherent(a.part + (size_t)(n_all + t) * H + row);
     if (a.accumulate) sum = a.y[o] + sum;
     a.y[o] = sum;
     if (a.y_bf16) a.y_bf16[o] = f32_to_bf16_rne(sum);
