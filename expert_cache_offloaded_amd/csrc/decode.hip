@@ -255,6 +255,36 @@ __device__ __forceinline__ void wfrag_store(const WFrag<FMT>& f, uint8_t* row, u
   }
 }
 
+// MXFP4 codes loaded four consecutive lanes per row (lane l: row (l >> 2) & 15 of the tile,
+// 16-byte chunk l & 3 of the row's 64-byte run of four blocks), which the vector memory path
+// serves faster than the operand layout, and moved into the operand layout (lane l: row
+// l & 15, chunk l >> 4) with four cross-lane reads once the data is in.  The scale byte is
+// loaded in the operand layout directly.  bf16 fragments load in the operand layout.
+template <int FMT>
+__device__ __forceinline__ void wfrag_load_rows(WFrag<FMT>& f, const uint8_t* base, size_t row_bytes, int row0,
+                                                int row_last, const uint8_t* srow, int blk0, int n_blk) {
+  const int lane = threadIdx.x & 63;
+  if (FMT == MC_MXFP4) {
+    const int bl = blk0 + (lane & 3), b = blk0 + (lane >> 4);
+    const int r = min(row0 + ((lane >> 2) & 15), row_last);
+    f.v[0] = stream_load16(base + (size_t)r * row_bytes + (size_t)(bl < n_blk ? bl : 0) * 16);
+    f.s = srow[b < n_blk ? b : 0];
+  } else {
+    const int b = blk0 + (lane >> 4);
+    wfrag_load<FMT>(f, base + (size_t)min(row0 + (lane & 15), row_last) * row_bytes, srow, b, b < n_blk);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void wfrag_to_operand(WFrag<FMT>& f) {
+  if (FMT == MC_MXFP4) {
+    const int lane = threadIdx.x & 63;
+    const int src = (4 * (lane & 15) + (lane >> 4)) << 2;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) f.v[0][d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)f.v[0][d]);
+  }
+}
+
 // B operand of MFMA ks (an invalid block contributes zeros)
 template <int FMT>
 __device__ __forceinline__ bf16x8_t wfrag_op(const WFrag<FMT>& f, int ks, bool ok) {
@@ -311,8 +341,6 @@ gate_up_kernel(DecodeArgs a) {
   const int i0 = blockIdx.y * 16;                // first intermediate row of the tile
   const int rl = lane & 15, g4 = lane >> 4;
   const int n_blk = H / 32;
-  const uint8_t* grow = gu + (size_t)(i0 + rl) * row_bytes;
-  const uint8_t* urow = gu + (size_t)(I + i0 + rl) * row_bytes;
   const uint8_t* gsrow = FMT == MC_MXFP4 ? gus + (size_t)(i0 + rl) * (H / 32) : nullptr;
   const uint8_t* usrow = FMT == MC_MXFP4 ? gus + (size_t)(I + i0 + rl) * (H / 32) : nullptr;
 
@@ -324,8 +352,8 @@ gate_up_kernel(DecodeArgs a) {
   for (int q = 0; q < SPW; ++q) {
     blk[q] = 4 * (wave * SPW + q) + g4;
     okb[q] = blk[q] < n_blk;
-    wfrag_load<FMT>(fg[q], grow, gsrow, blk[q], okb[q]);
-    wfrag_load<FMT>(fu[q], urow, usrow, blk[q], okb[q]);
+    wfrag_load_rows<FMT>(fg[q], gu, row_bytes, i0, i0 + 15, gsrow, 4 * (wave * SPW + q), n_blk);
+    wfrag_load_rows<FMT>(fu[q], gu, row_bytes, I + i0, I + i0 + 15, usrow, 4 * (wave * SPW + q), n_blk);
   }
   if (wave == 0) {
     const int n = unit_vectors(a, u, slot, win_slot, nt, nr, s_vec);
@@ -351,6 +379,10 @@ gate_up_kernel(DecodeArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         xa[ks] = ok ? *reinterpret_cast<const u32x4_t*>(xrow + (size_t)blk[q] * 32 + 8 * ks) : u32x4_t{0, 0, 0, 0};
+      if (b0 == 0) {                               // the weights into the operand layout, once
+        wfrag_to_operand<FMT>(fg[q]);
+        wfrag_to_operand<FMT>(fu[q]);
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[ks]);
@@ -1075,14 +1107,12 @@ down_unit_kernel(DecodeArgs a) {
     // the wave's 16-row tile over all of I, loaded once
     const int prow = r0 + wave * 16 + rl;
     const int row = min(prow, H - 1);
-    const uint8_t* wrow = dn + (size_t)row * row_bytes;
+    const int tile0 = r0 + wave * 16;                  // first row of the wave's tile
     const uint8_t* srow = FMT == MC_MXFP4 ? dns + (size_t)row * (I / 32) : nullptr;
     WFrag<FMT> f[NSTEP];
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      const int blk = 4 * s + g4;
-      wfrag_load<FMT>(f[s], wrow, srow, blk, blk < n_blk);
-    }
+    for (int s = 0; s < NSTEP; ++s)
+      wfrag_load_rows<FMT>(f[s], dn, row_bytes, tile0, H - 1, srow, 4 * s, n_blk);
     if (wave == 0) {
       const int n = unit_vectors(a, u, slot, win_slot, nt, nr, s_vec);
       for (int i = lane; i < n; i += 64) s_gate[i] = s_vec[i] < n_all ? a.w[s_vec[i]] : 1.0f;
@@ -1095,6 +1125,10 @@ down_unit_kernel(DecodeArgs a) {
       stage_h(a, s_vec + b0, nb, s_hv, wave, lane);
       __builtin_amdgcn_s_waitcnt(0);                   // the LDS copies (and the rows) have landed
       __syncthreads();
+      if (b0 == 0) {                                   // the rows into the operand layout, once
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) wfrag_to_operand<FMT>(f[s]);
+      }
       for (int t0 = 0; t0 < nb; t0 += kRouteTile) {
         // product row R = 2 i + half for route t0 + i of the batch
         const int R = 2 * t0 + rl;
