@@ -310,7 +310,7 @@ gate_up_kernel(DecodeArgs a) {
   // the several-token down pass's arrival counters start at zero in every call
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i < a.n_cnt; i += kThreads) a.cnt[i * kCntStride] = 0u;
-  const int u = blockIdx.x;
+  const int u = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I, n_all = a.T * a.k;
   const bool shared_unit = a.has_shared && u == n_all;
@@ -338,7 +338,7 @@ gate_up_kernel(DecodeArgs a) {
       if (FMT == MC_MXFP4) gus = a.f_gus + (size_t)src * per_gus;
     }
   }
-  const int i0 = blockIdx.y * 16;                // first intermediate row of the tile
+  const int i0 = blockIdx.x * 16;                // first intermediate row of the tile
   const int rl = lane & 15, g4 = lane >> 4;
   const int n_blk = H / 32;
   const uint8_t* gsrow = FMT == MC_MXFP4 ? gus + (size_t)(i0 + rl) * (H / 32) : nullptr;
@@ -361,7 +361,7 @@ gate_up_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int n_vec = s_n;
-  if (!shared_unit && blockIdx.y == 0)
+  if (!shared_unit && blockIdx.x == 0)
     for (int i = threadIdx.x; i < n_vec; i += kThreads) a.rsrc[s_vec[i]] = (int32_t)src;
 
   for (int b0 = 0; b0 < n_vec; b0 += 16) {
@@ -1074,7 +1074,7 @@ down_unit_kernel(DecodeArgs a) {
   __shared__ float s_gate[kMaxRoutes];
   __shared__ int32_t s_n;
   __shared__ uint32_t s_last;
-  const int u = blockIdx.x, rb = blockIdx.y;
+  const int u = blockIdx.y, rb = blockIdx.x;
   const int H = a.H, I = a.I, k = a.k, n_all = a.T * k;
   const int r0 = rb * kUnitRows;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1172,7 +1172,7 @@ down_unit_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) {
     const uint32_t before =
         __hip_atomic_fetch_add(a.cnt + (size_t)rb * kCntStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = before == gridDim.x - 1;
+    s_last = before == gridDim.y - 1;
   }
   __syncthreads();
   if (!s_last) return;
@@ -1467,7 +1467,8 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
     ok_a = fmt == MC_MXFP4 ? launch_gate_up_tok1<MC_MXFP4>(a, cpl1, grid_a, s)
                            : launch_gate_up_tok1<MC_BF16>(a, cpl1, grid_a, s);
   } else {
-    const dim3 grid_a(T * k + has_shared, I / 16);
+    // a unit's row blocks are launched one after another (x), the units along y
+    const dim3 grid_a(I / 16, T * k + has_shared);
     ok_a = fmt == MC_MXFP4 ? launch_gate_up<MC_MXFP4>(a, spw_gu, grid_a, s)
                            : launch_gate_up<MC_BF16>(a, spw_gu, grid_a, s);
   }
@@ -1489,7 +1490,7 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
     ok_b = fmt == MC_MXFP4 ? launch_down_tok1<MC_MXFP4>(a, lpr1, cplb1, grid_b, lds1, s)
                            : launch_down_tok1<MC_BF16>(a, lpr1, cplb1, grid_b, lds1, s);
   } else {
-    const dim3 grid_b(T * k + has_shared, (H + kUnitRows - 1) / kUnitRows);
+    const dim3 grid_b((H + kUnitRows - 1) / kUnitRows, T * k + has_shared);
     ok_b = fmt == MC_MXFP4 ? launch_down_unit<MC_MXFP4>(a, pow2_at_least(nstep_dn), grid_b, ldsn, s)
                            : launch_down_unit<MC_BF16>(a, pow2_at_least(nstep_dn), grid_b, ldsn, s);
   }
