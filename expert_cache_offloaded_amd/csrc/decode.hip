@@ -52,7 +52,7 @@ static_assert(kThreads == kFillThreads, "the fused copy workgroups run the fill'
 constexpr int kMaxRoutes = 1024;
 constexpr int kMaxTok = 64;
 constexpr int kKS = 128;                     // K elements per step (4 MFMAs of 32)
-constexpr int kHLdsBytes = 32 * 1024;        // down (several tokens): LDS for a batch of h
+constexpr int kHLdsBytes = 16 * 1024;        // down (several tokens): LDS for a batch of h
 constexpr int kRouteTile = 8;                // routes per down product (hi + lo rows)
 constexpr int kUnitRows = 64;                // down (several tokens): rows per workgroup
 constexpr int kCntStride = 16;               // uint32 words between arrival counters (64 B)
@@ -301,8 +301,12 @@ __device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((
 
 // ---------------------------------------------------------------- gate_up kernel
 
+// Four waves per SIMD for MXFP4 rows of up to four K steps per wave (the compiler then keeps
+// the kernel within 128 registers, against 140 on its own); longer rows and bf16 weights keep
+// the registers they need.
 template <int FMT, int SPW>   // SPW: K steps per wave
 __global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(FMT == MC_MXFP4 && SPW <= 4 ? 4 : 1)))
 gate_up_kernel(DecodeArgs a) {
   __shared__ f32x4_t s_red[4][2][64];            // per-wave gate / up products
   __shared__ int32_t s_vec[kMaxRoutes];
