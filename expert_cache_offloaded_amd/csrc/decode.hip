@@ -629,7 +629,7 @@ __device__ __forceinline__ void gate_up_tok1_role(const DecodeArgs& a, int u, in
 template <int FMT, int CPL>
 __global__ void __launch_bounds__(kThreads)
 gate_up_tok1_kernel(DecodeArgs a) {
-  gate_up_tok1_role<FMT, CPL, kTok1NP>(a, blockIdx.x, blockIdx.y);
+  gate_up_tok1_role<FMT, CPL, kTok1NP>(a, blockIdx.y, blockIdx.x);
 }
 
 // The same pass with the fill's down-bank copy in the launch.  A workgroup of NT threads
@@ -1467,7 +1467,8 @@ static int decode_impl(const void* x_bf16, const int32_t* slots, const float* w,
     ok_a = fmt == MC_MXFP4 ? launch_gate_up_fill_tok1<MC_MXFP4>(a, cpl1, gd, n_copy, n_gu, s)
                            : launch_gate_up_fill_tok1<MC_BF16>(a, cpl1, gd, n_copy, n_gu, s);
   } else if (T == 1) {
-    const dim3 grid_a(k + has_shared, I / (4 * kTok1NP));
+    // a unit's row blocks are launched one after another (x), the units along y
+    const dim3 grid_a(I / (4 * kTok1NP), k + has_shared);
     ok_a = fmt == MC_MXFP4 ? launch_gate_up_tok1<MC_MXFP4>(a, cpl1, grid_a, s)
                            : launch_gate_up_tok1<MC_BF16>(a, cpl1, grid_a, s);
   } else {
