@@ -542,18 +542,32 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int e, int eb, i
       }
     if (__ballot(h_over) && lane == 0) atomicOr(a.ws.status, kStatusHOverflow);
   } else {
-    // the route's own output row, scaled by its gate
+    // the route's own output row, scaled by its gate.  Every route and gate of the lane's
+    // rows is read before the first store: a gate read after a store to the (float) output
+    // rows could not be moved ahead of it, one dependent round trip per row.
+    int route[MT][4];
+    float g[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = mt * 16 + (lane >> 4) * 4 + j;
+        route[mt][j] = a.ws.perm[row0 + min(r, nrows - 1)];
+      }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[mt][j] = a.w[route[mt][j]];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = mt * 16 + (lane >> 4) * 4 + j;
         if (r >= nrows) continue;
-        const int route = a.ws.perm[row0 + r];
-        const float g = a.w[route];
-        float* yrow = a.ws.yr + (size_t)route * H;
+        float* yrow = a.ws.yr + (size_t)route[mt][j] * H;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) yrow[c0 + nt * 16 + (lane & 15)] = ldexpf(g * acc[mt][nt][j], shf[nt]);
+        for (int nt = 0; nt < 4; ++nt)
+          yrow[c0 + nt * 16 + (lane & 15)] = ldexpf(g[mt][j] * acc[mt][nt][j], shf[nt]);
       }
   }
 }
